@@ -1,0 +1,281 @@
+"""Python binding of libhelmkv.so, the gfx950 cross-model KV-cache transfer.
+
+Argument marshalling only: every step of the transfer runs in the HIP
+kernels behind include/helm_kv.h.  The names mirror the C ABI
+(``helm_kv_transfer``, ``helm_kv_transfer_paged``, ...).  torch supplies
+device memory and the current stream; tensors are passed by ``data_ptr()``.
+
+The library is loaded from this directory; if it is missing the import of
+any entry point raises — there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhelmkv.so")
+
+HELM_BF16 = 0
+HELM_F32 = 1
+
+STATUS = {0: "HELM_OK", 1: "HELM_E_INVALID_ARG", 2: "HELM_E_PAIR_SHAPE", 3: "HELM_E_LAYER_SEL",
+          4: "HELM_E_NO_DEVICE", 5: "HELM_E_DTYPE", 6: "HELM_E_ARCH", 7: "HELM_E_WORKSPACE",
+          8: "HELM_E_ALIAS", 9: "HELM_E_PAGED_TABLE", 10: "HELM_E_LAUNCH"}
+
+EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_paged", "helm_kv_workspace_bytes",
+            "helm_kv_paged_workspace_bytes", "helm_mapper_check", "helm_paged_check",
+            "helm_device_check", "helm_arch_supported", "helm_last_error", "helm_status_string",
+            "helm_abi_version")
+
+
+class HelmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class HelmShape(ctypes.Structure):
+    _fields_ = [
+        ("n_src_layers", ctypes.c_int32), ("n_tgt_layers", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("n_tokens", ctypes.c_int64),
+        ("rope_theta_src", ctypes.c_double), ("rope_theta_tgt", ctypes.c_double),
+        ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class HelmPagedShape(ctypes.Structure):
+    _fields_ = [
+        ("n_src_layers", ctypes.c_int32), ("n_tgt_layers", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("n_requests", ctypes.c_int32),
+        ("max_blocks_src", ctypes.c_int32), ("max_blocks_tgt", ctypes.c_int32),
+        ("n_src_blocks", ctypes.c_int32), ("n_tgt_blocks", ctypes.c_int32),
+        ("n_tokens_total", ctypes.c_int64),
+        ("rope_theta_src", ctypes.c_double), ("rope_theta_tgt", ctypes.c_double),
+        ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libhelmkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(the transfer has no other implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32p = ctypes.c_void_p, ctypes.c_void_p
+        L.helm_kv_transfer.restype = ctypes.c_int
+        L.helm_kv_transfer.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
+        L.helm_kv_transfer_paged.restype = ctypes.c_int
+        L.helm_kv_transfer_paged.argtypes = [vp] * 14 + [ctypes.POINTER(HelmPagedShape)]
+        L.helm_kv_workspace_bytes.restype = ctypes.c_size_t
+        L.helm_kv_workspace_bytes.argtypes = [ctypes.POINTER(HelmShape)]
+        L.helm_kv_paged_workspace_bytes.restype = ctypes.c_size_t
+        L.helm_kv_paged_workspace_bytes.argtypes = [ctypes.POINTER(HelmPagedShape)]
+        L.helm_mapper_check.restype = ctypes.c_int
+        L.helm_mapper_check.argtypes = [ctypes.POINTER(HelmShape), i32p]
+        L.helm_paged_check.restype = ctypes.c_int
+        L.helm_paged_check.argtypes = [ctypes.POINTER(HelmPagedShape), i32p, i32p, i32p]
+        L.helm_device_check.restype = ctypes.c_int
+        L.helm_device_check.argtypes = [ctypes.c_int]
+        L.helm_arch_supported.restype = ctypes.c_int
+        L.helm_arch_supported.argtypes = [ctypes.c_char_p]
+        L.helm_last_error.restype = ctypes.c_char_p
+        L.helm_last_error.argtypes = []
+        L.helm_status_string.restype = ctypes.c_char_p
+        L.helm_status_string.argtypes = [ctypes.c_int]
+        L.helm_abi_version.restype = ctypes.c_int
+        L.helm_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def helm_last_error() -> str:
+    return lib().helm_last_error().decode()
+
+
+def helm_status_string(status: int) -> str:
+    return lib().helm_status_string(status).decode()
+
+
+def helm_abi_version() -> int:
+    return int(lib().helm_abi_version())
+
+
+def helm_arch_supported(name: str) -> bool:
+    return bool(lib().helm_arch_supported(name.encode()))
+
+
+def helm_device_check(device: int = -1) -> int:
+    return int(lib().helm_device_check(device))
+
+
+def _raise(status: int):
+    if status != 0:
+        raise HelmError(status, helm_last_error())
+
+
+def helm_kv_workspace_bytes(shape: HelmShape) -> int:
+    n = int(lib().helm_kv_workspace_bytes(ctypes.byref(shape)))
+    if n == 0:
+        raise HelmError(1, helm_last_error())
+    return n
+
+
+def helm_kv_paged_workspace_bytes(shape: HelmPagedShape) -> int:
+    n = int(lib().helm_kv_paged_workspace_bytes(ctypes.byref(shape)))
+    if n == 0:
+        raise HelmError(1, helm_last_error())
+    return n
+
+
+def _host_i32(a):
+    """(pointer, keepalive) of a host int32 buffer from a torch tensor or numpy array."""
+    import numpy as np
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return ctypes.c_void_p(a.ctypes.data), a
+
+
+def helm_mapper_check(shape: HelmShape, layer_sel_host) -> int:
+    p, keep = _host_i32(layer_sel_host)
+    return int(lib().helm_mapper_check(ctypes.byref(shape), p))
+
+
+def helm_paged_check(shape: HelmPagedShape, src_block_table_host, tgt_block_table_host,
+                     cu_seqlens_host) -> int:
+    (a, ka), (b, kb), (c, kc) = (_host_i32(x) for x in
+                                 (src_block_table_host, tgt_block_table_host, cu_seqlens_host))
+    return int(lib().helm_paged_check(ctypes.byref(shape), a, b, c))
+
+
+# ---------------------------------------------------------------- torch glue
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return HELM_BF16
+    if t.dtype == torch.float32:
+        return HELM_F32
+    raise TypeError(f"unsupported storage dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev_ptr(t, name, dtype=None, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def current_stream_ptr(device=None) -> int:
+    import torch
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_shape(src_k, W_k, layer_sel, theta_src: float, theta_tgt: float) -> HelmShape:
+    """helm_shape_t from tensor shapes: src_k [L_s,H,T,D], W_k [L_t,H,k*D,D], layer_sel [L_t,k]."""
+    L_s, H, T, D = src_k.shape
+    L_t, k = layer_sel.shape
+    s = HelmShape()
+    s.n_src_layers, s.n_tgt_layers, s.n_kv_heads, s.head_dim, s.k = L_s, L_t, H, D, k
+    s.dtype = _dtype_code(src_k)
+    s.n_tokens = T
+    s.rope_theta_src, s.rope_theta_tgt = theta_src, theta_tgt
+    return s
+
+
+def helm_kv_transfer(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v,
+                     shape: HelmShape, workspace=None) -> None:
+    """Enqueues the contiguous transfer on ``shape.stream`` (torch's current
+    stream when unset).  ``workspace``: a uint8 device tensor of at least
+    helm_kv_workspace_bytes(shape) bytes; allocated here when omitted.
+    Raises HelmError on a refused call (nothing is written then)."""
+    import torch
+    L_s, L_t, H, D, k, T = (shape.n_src_layers, shape.n_tgt_layers, shape.n_kv_heads,
+                            shape.head_dim, shape.k, shape.n_tokens)
+    dt = torch.bfloat16 if shape.dtype == HELM_BF16 else torch.float32
+    ptrs = [
+        _dev_ptr(src_k, "src_k", dt, (L_s, H, T, D)), _dev_ptr(src_v, "src_v", dt, (L_s, H, T, D)),
+        _dev_ptr(src_pos, "src_pos", torch.int32, (T,)), _dev_ptr(tgt_pos, "tgt_pos", torch.int32, (T,)),
+        _dev_ptr(layer_sel, "layer_sel", torch.int32, (L_t, k)),
+        _dev_ptr(W_k, "W_k", dt, (L_t, H, k * D, D)), _dev_ptr(b_k, "b_k", torch.float32, (L_t, H, D)),
+        _dev_ptr(W_v, "W_v", dt, (L_t, H, k * D, D)), _dev_ptr(b_v, "b_v", torch.float32, (L_t, H, D)),
+        _dev_ptr(out_k, "out_k", dt, (L_t, H, T, D)), _dev_ptr(out_v, "out_v", dt, (L_t, H, T, D)),
+    ]
+    if not shape.stream:
+        shape.stream = current_stream_ptr(src_k.device)
+    if workspace is None:
+        workspace = torch.empty(helm_kv_workspace_bytes(shape), dtype=torch.uint8, device=src_k.device)
+    shape.workspace = workspace.data_ptr()
+    shape.workspace_bytes = workspace.numel()
+    _raise(lib().helm_kv_transfer(*ptrs, ctypes.byref(shape)))
+
+
+def make_paged_shape(src_k_pool, tgt_k_pool, W_k, layer_sel, src_block_table, tgt_block_table,
+                     n_tokens_total: int, theta_src: float, theta_tgt: float) -> HelmPagedShape:
+    """helm_paged_shape_t from tensor shapes (pools [L, n_blocks, B, H, D])."""
+    L_s, nsb, B, H, D = src_k_pool.shape
+    L_t, ntb = tgt_k_pool.shape[:2]
+    k = layer_sel.shape[1]
+    s = HelmPagedShape()
+    s.n_src_layers, s.n_tgt_layers, s.n_kv_heads, s.head_dim, s.k = L_s, L_t, H, D, k
+    s.dtype = _dtype_code(src_k_pool)
+    s.block_size, s.n_requests = B, src_block_table.shape[0]
+    s.max_blocks_src, s.max_blocks_tgt = src_block_table.shape[1], tgt_block_table.shape[1]
+    s.n_src_blocks, s.n_tgt_blocks = nsb, ntb
+    s.n_tokens_total = n_tokens_total
+    s.rope_theta_src, s.rope_theta_tgt = theta_src, theta_tgt
+    return s
+
+
+def helm_kv_transfer_paged(src_k_pool, src_v_pool, src_block_table, tgt_block_table, cu_seqlens,
+                           src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, tgt_k_pool, tgt_v_pool,
+                           shape: HelmPagedShape, workspace=None) -> None:
+    """Enqueues the paged transfer; same conventions as helm_kv_transfer."""
+    import torch
+    s = shape
+    dt = torch.bfloat16 if s.dtype == HELM_BF16 else torch.float32
+    L_s, L_t, H, D, k, B = s.n_src_layers, s.n_tgt_layers, s.n_kv_heads, s.head_dim, s.k, s.block_size
+    N, R = s.n_tokens_total, s.n_requests
+    ptrs = [
+        _dev_ptr(src_k_pool, "src_k_pool", dt, (L_s, s.n_src_blocks, B, H, D)),
+        _dev_ptr(src_v_pool, "src_v_pool", dt, (L_s, s.n_src_blocks, B, H, D)),
+        _dev_ptr(src_block_table, "src_block_table", torch.int32, (R, s.max_blocks_src)),
+        _dev_ptr(tgt_block_table, "tgt_block_table", torch.int32, (R, s.max_blocks_tgt)),
+        _dev_ptr(cu_seqlens, "cu_seqlens", torch.int32, (R + 1,)),
+        _dev_ptr(src_pos, "src_pos", torch.int32, (N,)), _dev_ptr(tgt_pos, "tgt_pos", torch.int32, (N,)),
+        _dev_ptr(layer_sel, "layer_sel", torch.int32, (L_t, k)),
+        _dev_ptr(W_k, "W_k", dt, (L_t, H, k * D, D)), _dev_ptr(b_k, "b_k", torch.float32, (L_t, H, D)),
+        _dev_ptr(W_v, "W_v", dt, (L_t, H, k * D, D)), _dev_ptr(b_v, "b_v", torch.float32, (L_t, H, D)),
+        _dev_ptr(tgt_k_pool, "tgt_k_pool", dt, (L_t, s.n_tgt_blocks, B, H, D)),
+        _dev_ptr(tgt_v_pool, "tgt_v_pool", dt, (L_t, s.n_tgt_blocks, B, H, D)),
+    ]
+    if not s.stream:
+        s.stream = current_stream_ptr(src_k_pool.device)
+    if workspace is None:
+        workspace = torch.empty(helm_kv_paged_workspace_bytes(s), dtype=torch.uint8, device=src_k_pool.device)
+    s.workspace = workspace.data_ptr()
+    s.workspace_bytes = workspace.numel()
+    _raise(lib().helm_kv_transfer_paged(*ptrs, ctypes.byref(s)))

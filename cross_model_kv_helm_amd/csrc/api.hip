@@ -1,0 +1,422 @@
+// api.hip — the C ABI (include/helm_kv.h): host-side validation, workspace
+// layout, the device/arch gate, and kernel dispatch.  Every check runs
+// before anything is enqueued, so a refused call writes nothing and the
+// caller can fall back to a normal prefill ("Helm Intelligent Routing",
+// section "What happens when a transfer cannot be used").
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../include/helm_kv.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  std::va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Multiplies non-negative factors; returns false on int64 overflow.
+bool mul_ok(int64_t& acc, int64_t f) {
+  if (f < 0) return false;
+  if (f != 0 && acc > INT64_MAX / f) return false;
+  acc *= f;
+  return true;
+}
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// Fields common to both shapes.
+struct Common {
+  int32_t L_s, L_t, H, D, k, dtype;
+  double theta_src, theta_tgt;
+};
+
+int check_common(const Common& c) {
+  if (c.L_s < 1 || c.L_t < 1 || c.H < 1)
+    return fail(HELM_E_INVALID_ARG, "layer and head counts must be >= 1 (L_s=%d L_t=%d H=%d)",
+                c.L_s, c.L_t, c.H);
+  if (c.dtype != HELM_BF16 && c.dtype != HELM_F32)
+    return fail(HELM_E_DTYPE, "unknown dtype code %d (HELM_BF16=0, HELM_F32=1)", c.dtype);
+  if (c.D <= 0 || (c.D & 1))
+    return fail(HELM_E_PAIR_SHAPE, "head_dim must be positive and even for rotate-half RoPE (D=%d)", c.D);
+  if (c.D != 64 && c.D != 128)
+    return fail(HELM_E_PAIR_SHAPE, "head_dim %d is not supported (64 or 128)", c.D);
+  if (c.k < 1 || c.k > c.L_s)
+    return fail(HELM_E_INVALID_ARG, "k=%d must lie in 1..L_s (L_s=%d)", c.k, c.L_s);
+  if (c.k > 64) return fail(HELM_E_INVALID_ARG, "k=%d exceeds the supported maximum of 64", c.k);
+  if ((int64_t)c.L_t * c.H > 65535)
+    return fail(HELM_E_INVALID_ARG, "L_t*H=%lld exceeds 65535", (long long)c.L_t * c.H);
+  if (!(c.theta_src > 0.0) || !std::isfinite(c.theta_src) || !(c.theta_tgt > 0.0) ||
+      !std::isfinite(c.theta_tgt))
+    return fail(HELM_E_INVALID_ARG, "RoPE bases must be finite and > 0 (src=%g tgt=%g)", c.theta_src,
+                c.theta_tgt);
+  return HELM_OK;
+}
+
+Common common_of(const helm_shape_t* s) {
+  return {s->n_src_layers, s->n_tgt_layers, s->n_kv_heads, s->head_dim, s->k, s->dtype,
+          s->rope_theta_src, s->rope_theta_tgt};
+}
+Common common_of(const helm_paged_shape_t* s) {
+  return {s->n_src_layers, s->n_tgt_layers, s->n_kv_heads, s->head_dim, s->k, s->dtype,
+          s->rope_theta_src, s->rope_theta_tgt};
+}
+
+size_t elem_bytes(int32_t dtype) { return dtype == HELM_BF16 ? 2 : 4; }
+
+// Workspace: [rope_src: N*D/2 float2][rope_tgt: same]{[src_row: N int32][dst_row: N int32]}
+struct Workspace {
+  size_t rope_bytes = 0, rows_bytes = 0, total = 0;
+};
+
+bool workspace_layout(int64_t n_tok, int32_t D, bool paged, Workspace& w) {
+  int64_t rb = n_tok;
+  if (!mul_ok(rb, D / 2) || !mul_ok(rb, (int64_t)sizeof(float2))) return false;
+  w.rope_bytes = align_up((size_t)rb);
+  w.rows_bytes = paged ? align_up((size_t)n_tok * sizeof(int32_t)) : 0;
+  w.total = 2 * w.rope_bytes + 2 * w.rows_bytes;
+  if (w.total == 0) w.total = kAlign;   // never ask for a zero-byte buffer
+  return true;
+}
+
+// ---- device gate -------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];   // 0 unknown, 1 ok, 2 wrong arch
+
+int device_gate(int device) {
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return fail(HELM_E_NO_DEVICE, "no GPU is visible (%s)", e == hipSuccess ? "count 0" : hipGetErrorString(e));
+  }
+  if (device < 0) {
+    e = hipGetDevice(&device);
+    if (e != hipSuccess) return fail(HELM_E_NO_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  }
+  if (device >= count) return fail(HELM_E_NO_DEVICE, "device %d does not exist (%d visible)", device, count);
+  const int slot = device < kMaxDevices ? device : -1;
+  int st = slot >= 0 ? g_dev_state[slot].load(std::memory_order_relaxed) : 0;
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess) return fail(HELM_E_NO_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    st = helm_arch_supported(prop.gcnArchName) ? 1 : 2;
+    if (st == 2) {
+      if (slot >= 0) g_dev_state[slot].store(st, std::memory_order_relaxed);
+      return fail(HELM_E_ARCH, "device %d is %s; this library runs on gfx950 (MI355X) only", device,
+                  prop.gcnArchName);
+    }
+    if (slot >= 0) g_dev_state[slot].store(st, std::memory_order_relaxed);
+  }
+  if (st == 2) return fail(HELM_E_ARCH, "device %d is not a gfx950 part", device);
+  return HELM_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return HELM_OK;
+  return fail(HELM_E_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+int run_transfer(helm::XferArgs& a, int32_t dtype, const int32_t* src_pos, const int32_t* tgt_pos,
+                 double th_s, double th_t, hipStream_t stream) {
+  int rc = launch_status(helm::launch_rope_tables(src_pos, tgt_pos, a.n_tok, a.D, th_s, th_t,
+                                                  const_cast<float2*>(a.rope_src),
+                                                  const_cast<float2*>(a.rope_tgt), stream),
+                         "RoPE table kernel launch");
+  if (rc != HELM_OK) return rc;
+  if (dtype == HELM_BF16 && helm::mfma_supports(a))
+    rc = launch_status(helm::launch_transfer_mfma(a, stream), "matrix-core transfer kernel launch");
+  else
+    rc = launch_status(helm::launch_transfer_generic(a, dtype == HELM_BF16 ? helm::Dtype::BF16 : helm::Dtype::F32,
+                                                     stream),
+                       "transfer kernel launch");
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int helm_abi_version(void) { return HELM_ABI_VERSION; }
+
+const char* helm_last_error(void) { return g_err; }
+
+const char* helm_status_string(int status) {
+  switch (status) {
+    case HELM_OK: return "HELM_OK";
+    case HELM_E_INVALID_ARG: return "HELM_E_INVALID_ARG";
+    case HELM_E_PAIR_SHAPE: return "HELM_E_PAIR_SHAPE";
+    case HELM_E_LAYER_SEL: return "HELM_E_LAYER_SEL";
+    case HELM_E_NO_DEVICE: return "HELM_E_NO_DEVICE";
+    case HELM_E_DTYPE: return "HELM_E_DTYPE";
+    case HELM_E_ARCH: return "HELM_E_ARCH";
+    case HELM_E_WORKSPACE: return "HELM_E_WORKSPACE";
+    case HELM_E_ALIAS: return "HELM_E_ALIAS";
+    case HELM_E_PAGED_TABLE: return "HELM_E_PAGED_TABLE";
+    case HELM_E_LAUNCH: return "HELM_E_LAUNCH";
+    default: return "unknown";
+  }
+}
+
+int helm_arch_supported(const char* name) {
+  if (!name) return 0;
+  // "gfx950" optionally followed by target features (":sramecc+:xnack-").
+  return std::strncmp(name, "gfx950", 6) == 0 && (name[6] == '\0' || name[6] == ':') ? 1 : 0;
+}
+
+int helm_device_check(int device) {
+  clear_error();
+  return device_gate(device);
+}
+
+size_t helm_kv_workspace_bytes(const helm_shape_t* s) {
+  clear_error();
+  if (!s) { fail(HELM_E_INVALID_ARG, "shape is NULL"); return 0; }
+  if (check_common(common_of(s)) != HELM_OK) return 0;
+  if (s->n_tokens < 0) { fail(HELM_E_INVALID_ARG, "n_tokens < 0"); return 0; }
+  Workspace w;
+  if (!workspace_layout(s->n_tokens, s->head_dim, false, w)) { fail(HELM_E_INVALID_ARG, "size overflow"); return 0; }
+  return w.total;
+}
+
+size_t helm_kv_paged_workspace_bytes(const helm_paged_shape_t* s) {
+  clear_error();
+  if (!s) { fail(HELM_E_INVALID_ARG, "shape is NULL"); return 0; }
+  if (check_common(common_of(s)) != HELM_OK) return 0;
+  if (s->n_tokens_total < 0) { fail(HELM_E_INVALID_ARG, "n_tokens_total < 0"); return 0; }
+  Workspace w;
+  if (!workspace_layout(s->n_tokens_total, s->head_dim, true, w)) { fail(HELM_E_INVALID_ARG, "size overflow"); return 0; }
+  return w.total;
+}
+
+int helm_mapper_check(const helm_shape_t* s, const int32_t* sel) {
+  clear_error();
+  if (!s || !sel) return fail(HELM_E_INVALID_ARG, "shape or layer_sel_host is NULL");
+  int rc = check_common(common_of(s));
+  if (rc != HELM_OK) return rc;
+  for (int64_t l = 0; l < s->n_tgt_layers; ++l)
+    for (int64_t j = 0; j < s->k; ++j) {
+      const int32_t v = sel[l * s->k + j];
+      if (v < 0 || v >= s->n_src_layers)
+        return fail(HELM_E_LAYER_SEL, "layer_sel[%lld][%lld] = %d lies outside [0, %d)", (long long)l,
+                    (long long)j, v, s->n_src_layers);
+    }
+  return HELM_OK;
+}
+
+int helm_paged_check(const helm_paged_shape_t* s, const int32_t* sbt, const int32_t* tbt,
+                     const int32_t* cu) {
+  clear_error();
+  if (!s || !sbt || !tbt || !cu) return fail(HELM_E_INVALID_ARG, "a NULL argument");
+  int rc = check_common(common_of(s));
+  if (rc != HELM_OK) return rc;
+  if (s->block_size < 1 || s->n_requests < 1 || s->max_blocks_src < 1 || s->max_blocks_tgt < 1 ||
+      s->n_src_blocks < 1 || s->n_tgt_blocks < 1)
+    return fail(HELM_E_INVALID_ARG, "paged sizes must be >= 1");
+  if (cu[0] != 0) return fail(HELM_E_PAGED_TABLE, "cu_seqlens[0] = %d, expected 0", cu[0]);
+  const int32_t B = s->block_size;
+  std::vector<uint8_t> used((size_t)s->n_tgt_blocks, 0);
+  for (int32_t r = 0; r < s->n_requests; ++r) {
+    const int64_t len = (int64_t)cu[r + 1] - cu[r];
+    if (len < 0) return fail(HELM_E_PAGED_TABLE, "cu_seqlens decreases at request %d", r);
+    const int64_t pages = (len + B - 1) / B;
+    if (pages > s->max_blocks_src || pages > s->max_blocks_tgt)
+      return fail(HELM_E_PAGED_TABLE, "request %d needs %lld pages; tables hold %d / %d", r,
+                  (long long)pages, s->max_blocks_src, s->max_blocks_tgt);
+    for (int64_t p = 0; p < pages; ++p) {
+      const int32_t a = sbt[(int64_t)r * s->max_blocks_src + p];
+      const int32_t b = tbt[(int64_t)r * s->max_blocks_tgt + p];
+      if (a < 0 || a >= s->n_src_blocks)
+        return fail(HELM_E_PAGED_TABLE, "src_block_table[%d][%lld] = %d lies outside [0, %d)", r,
+                    (long long)p, a, s->n_src_blocks);
+      if (b < 0 || b >= s->n_tgt_blocks)
+        return fail(HELM_E_PAGED_TABLE, "tgt_block_table[%d][%lld] = %d lies outside [0, %d)", r,
+                    (long long)p, b, s->n_tgt_blocks);
+      if (used[(size_t)b])
+        return fail(HELM_E_PAGED_TABLE, "target block %d is used twice (request %d, page %lld)", b, r,
+                    (long long)p);
+      used[(size_t)b] = 1;
+    }
+  }
+  if ((int64_t)cu[s->n_requests] != s->n_tokens_total)
+    return fail(HELM_E_PAGED_TABLE, "cu_seqlens[R] = %d but n_tokens_total = %lld", cu[s->n_requests],
+                (long long)s->n_tokens_total);
+  return HELM_OK;
+}
+
+int helm_kv_transfer(const void* src_k, const void* src_v, const int32_t* src_pos,
+                     const int32_t* tgt_pos, const int32_t* layer_sel, const void* W_k,
+                     const float* b_k, const void* W_v, const float* b_v, void* out_k, void* out_v,
+                     const helm_shape_t* s) {
+  clear_error();
+  if (!s) return fail(HELM_E_INVALID_ARG, "shape is NULL");
+  int rc = check_common(common_of(s));
+  if (rc != HELM_OK) return rc;
+  if (s->n_tokens < 0) return fail(HELM_E_INVALID_ARG, "n_tokens = %lld < 0", (long long)s->n_tokens);
+  if (s->n_tokens > 0x7fffffffLL) return fail(HELM_E_INVALID_ARG, "n_tokens exceeds 2^31-1");
+  if (s->n_tokens == 0) return HELM_OK;   // nothing to map; no pointer or device is touched
+  if (!src_k || !src_v || !src_pos || !tgt_pos || !layer_sel || !W_k || !b_k || !W_v || !b_v || !out_k ||
+      !out_v)
+    return fail(HELM_E_INVALID_ARG, "a tensor pointer is NULL");
+
+  const int64_t es = (int64_t)elem_bytes(s->dtype);
+  int64_t src_b = s->n_src_layers, out_b = s->n_tgt_layers, w_b = s->n_tgt_layers, b_b = s->n_tgt_layers;
+  if (!mul_ok(src_b, s->n_kv_heads) || !mul_ok(src_b, s->n_tokens) || !mul_ok(src_b, s->head_dim) ||
+      !mul_ok(src_b, es) || !mul_ok(out_b, s->n_kv_heads) || !mul_ok(out_b, s->n_tokens) ||
+      !mul_ok(out_b, s->head_dim) || !mul_ok(out_b, es) || !mul_ok(w_b, s->n_kv_heads) ||
+      !mul_ok(w_b, (int64_t)s->k * s->head_dim) || !mul_ok(w_b, s->head_dim) || !mul_ok(w_b, es) ||
+      !mul_ok(b_b, s->n_kv_heads) || !mul_ok(b_b, (int64_t)s->head_dim * 4))
+    return fail(HELM_E_INVALID_ARG, "tensor sizes overflow int64");
+
+  const int64_t pos_b = s->n_tokens * 4, sel_b = (int64_t)s->n_tgt_layers * s->k * 4;
+  const struct { const void* p; int64_t n; const char* name; } ins[] = {
+      {src_k, src_b, "src_k"}, {src_v, src_b, "src_v"}, {src_pos, pos_b, "src_pos"},
+      {tgt_pos, pos_b, "tgt_pos"}, {layer_sel, sel_b, "layer_sel"}, {W_k, w_b, "W_k"},
+      {b_k, b_b, "b_k"}, {W_v, w_b, "W_v"}, {b_v, b_b, "b_v"}};
+  for (const auto& in : ins) {
+    if (overlaps(out_k, out_b, in.p, in.n)) return fail(HELM_E_ALIAS, "out_k overlaps %s", in.name);
+    if (overlaps(out_v, out_b, in.p, in.n)) return fail(HELM_E_ALIAS, "out_v overlaps %s", in.name);
+  }
+  if (overlaps(out_k, out_b, out_v, out_b)) return fail(HELM_E_ALIAS, "out_k overlaps out_v");
+
+  Workspace w;
+  if (!workspace_layout(s->n_tokens, s->head_dim, false, w)) return fail(HELM_E_INVALID_ARG, "size overflow");
+  if (!s->workspace || s->workspace_bytes < w.total)
+    return fail(HELM_E_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", s->workspace_bytes,
+                s->workspace, w.total);
+  if ((uintptr_t)s->workspace % kAlign)
+    return fail(HELM_E_WORKSPACE, "workspace %p is not %zu-byte aligned", s->workspace, kAlign);
+  for (const auto& in : ins)
+    if (overlaps(s->workspace, (int64_t)w.total, in.p, in.n))
+      return fail(HELM_E_ALIAS, "workspace overlaps %s", in.name);
+  if (overlaps(s->workspace, (int64_t)w.total, out_k, out_b) || overlaps(s->workspace, (int64_t)w.total, out_v, out_b))
+    return fail(HELM_E_ALIAS, "workspace overlaps an output");
+
+  rc = device_gate(-1);
+  if (rc != HELM_OK) return rc;
+  if (s->n_tokens == 0) return HELM_OK;
+
+  char* ws = (char*)s->workspace;
+  helm::XferArgs a{};
+  a.src_k = src_k; a.src_v = src_v; a.layer_sel = layer_sel;
+  a.W_k = W_k; a.b_k = b_k; a.W_v = W_v; a.b_v = b_v; a.out_k = out_k; a.out_v = out_v;
+  a.rope_src = (const float2*)ws;
+  a.rope_tgt = (const float2*)(ws + w.rope_bytes);
+  a.src_row = nullptr; a.dst_row = nullptr;
+  a.n_tok = s->n_tokens;
+  a.L_s = s->n_src_layers; a.L_t = s->n_tgt_layers; a.H = s->n_kv_heads; a.D = s->head_dim; a.k = s->k;
+  a.src_tok = s->head_dim; a.src_head = s->n_tokens * s->head_dim; a.src_layer = a.src_head * s->n_kv_heads;
+  a.dst_tok = a.src_tok; a.dst_head = a.src_head; a.dst_layer = a.src_layer;
+  return run_transfer(a, s->dtype, src_pos, tgt_pos, s->rope_theta_src, s->rope_theta_tgt,
+                      (hipStream_t)s->stream);
+}
+
+int helm_kv_transfer_paged(const void* src_k_pool, const void* src_v_pool, const int32_t* src_bt,
+                           const int32_t* tgt_bt, const int32_t* cu, const int32_t* src_pos,
+                           const int32_t* tgt_pos, const int32_t* layer_sel, const void* W_k,
+                           const float* b_k, const void* W_v, const float* b_v, void* tgt_k_pool,
+                           void* tgt_v_pool, const helm_paged_shape_t* s) {
+  clear_error();
+  if (!s) return fail(HELM_E_INVALID_ARG, "shape is NULL");
+  int rc = check_common(common_of(s));
+  if (rc != HELM_OK) return rc;
+  if (s->block_size < 1 || s->n_requests < 1 || s->max_blocks_src < 1 || s->max_blocks_tgt < 1 ||
+      s->n_src_blocks < 1 || s->n_tgt_blocks < 1)
+    return fail(HELM_E_INVALID_ARG, "paged sizes must be >= 1");
+  if (s->n_tokens_total < 0 || s->n_tokens_total > 0x7fffffffLL)
+    return fail(HELM_E_INVALID_ARG, "n_tokens_total = %lld outside [0, 2^31)", (long long)s->n_tokens_total);
+  if (s->n_tokens_total == 0) return HELM_OK;   // nothing to map; no pointer or device is touched
+  if ((int64_t)s->n_src_blocks * s->block_size > 0x7fffffffLL ||
+      (int64_t)s->n_tgt_blocks * s->block_size > 0x7fffffffLL)
+    return fail(HELM_E_INVALID_ARG, "pool slot counts must stay below 2^31");
+  if (!src_k_pool || !src_v_pool || !src_bt || !tgt_bt || !cu || !src_pos || !tgt_pos || !layer_sel || !W_k ||
+      !b_k || !W_v || !b_v || !tgt_k_pool || !tgt_v_pool)
+    return fail(HELM_E_INVALID_ARG, "a tensor pointer is NULL");
+
+  const int64_t es = (int64_t)elem_bytes(s->dtype);
+  int64_t src_b = s->n_src_layers, out_b = s->n_tgt_layers, w_b = s->n_tgt_layers, b_b = s->n_tgt_layers;
+  if (!mul_ok(src_b, s->n_src_blocks) || !mul_ok(src_b, s->block_size) || !mul_ok(src_b, s->n_kv_heads) ||
+      !mul_ok(src_b, s->head_dim) || !mul_ok(src_b, es) || !mul_ok(out_b, s->n_tgt_blocks) ||
+      !mul_ok(out_b, s->block_size) || !mul_ok(out_b, s->n_kv_heads) || !mul_ok(out_b, s->head_dim) ||
+      !mul_ok(out_b, es) || !mul_ok(w_b, s->n_kv_heads) || !mul_ok(w_b, (int64_t)s->k * s->head_dim) ||
+      !mul_ok(w_b, s->head_dim) || !mul_ok(w_b, es) || !mul_ok(b_b, s->n_kv_heads) ||
+      !mul_ok(b_b, (int64_t)s->head_dim * 4))
+    return fail(HELM_E_INVALID_ARG, "tensor sizes overflow int64");
+  const int64_t pos_b = s->n_tokens_total * 4, sel_b = (int64_t)s->n_tgt_layers * s->k * 4;
+  const int64_t sbt_b = (int64_t)s->n_requests * s->max_blocks_src * 4;
+  const int64_t tbt_b = (int64_t)s->n_requests * s->max_blocks_tgt * 4;
+  const struct { const void* p; int64_t n; const char* name; } ins[] = {
+      {src_k_pool, src_b, "src_k_pool"}, {src_v_pool, src_b, "src_v_pool"}, {src_bt, sbt_b, "src_block_table"},
+      {tgt_bt, tbt_b, "tgt_block_table"}, {cu, (int64_t)(s->n_requests + 1) * 4, "cu_seqlens"},
+      {src_pos, pos_b, "src_pos"}, {tgt_pos, pos_b, "tgt_pos"}, {layer_sel, sel_b, "layer_sel"},
+      {W_k, w_b, "W_k"}, {b_k, b_b, "b_k"}, {W_v, w_b, "W_v"}, {b_v, b_b, "b_v"}};
+  for (const auto& in : ins) {
+    if (overlaps(tgt_k_pool, out_b, in.p, in.n)) return fail(HELM_E_ALIAS, "tgt_k_pool overlaps %s", in.name);
+    if (overlaps(tgt_v_pool, out_b, in.p, in.n)) return fail(HELM_E_ALIAS, "tgt_v_pool overlaps %s", in.name);
+  }
+  if (overlaps(tgt_k_pool, out_b, tgt_v_pool, out_b)) return fail(HELM_E_ALIAS, "tgt_k_pool overlaps tgt_v_pool");
+
+  Workspace w;
+  if (!workspace_layout(s->n_tokens_total, s->head_dim, true, w)) return fail(HELM_E_INVALID_ARG, "size overflow");
+  if (!s->workspace || s->workspace_bytes < w.total)
+    return fail(HELM_E_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", s->workspace_bytes,
+                s->workspace, w.total);
+  if ((uintptr_t)s->workspace % kAlign)
+    return fail(HELM_E_WORKSPACE, "workspace %p is not %zu-byte aligned", s->workspace, kAlign);
+  for (const auto& in : ins)
+    if (overlaps(s->workspace, (int64_t)w.total, in.p, in.n))
+      return fail(HELM_E_ALIAS, "workspace overlaps %s", in.name);
+  if (overlaps(s->workspace, (int64_t)w.total, tgt_k_pool, out_b) ||
+      overlaps(s->workspace, (int64_t)w.total, tgt_v_pool, out_b))
+    return fail(HELM_E_ALIAS, "workspace overlaps an output pool");
+
+  rc = device_gate(-1);
+  if (rc != HELM_OK) return rc;
+  if (s->n_tokens_total == 0) return HELM_OK;
+
+  char* ws = (char*)s->workspace;
+  helm::XferArgs a{};
+  a.src_k = src_k_pool; a.src_v = src_v_pool; a.layer_sel = layer_sel;
+  a.W_k = W_k; a.b_k = b_k; a.W_v = W_v; a.b_v = b_v; a.out_k = tgt_k_pool; a.out_v = tgt_v_pool;
+  a.rope_src = (const float2*)ws;
+  a.rope_tgt = (const float2*)(ws + w.rope_bytes);
+  int32_t* src_row = (int32_t*)(ws + 2 * w.rope_bytes);
+  int32_t* dst_row = (int32_t*)(ws + 2 * w.rope_bytes + w.rows_bytes);
+  a.src_row = src_row; a.dst_row = dst_row;
+  a.n_tok = s->n_tokens_total;
+  a.L_s = s->n_src_layers; a.L_t = s->n_tgt_layers; a.H = s->n_kv_heads; a.D = s->head_dim; a.k = s->k;
+  a.src_tok = (int64_t)s->n_kv_heads * s->head_dim; a.src_head = s->head_dim;
+  a.src_layer = (int64_t)s->n_src_blocks * s->block_size * a.src_tok;
+  a.dst_tok = a.src_tok; a.dst_head = a.src_head;
+  a.dst_layer = (int64_t)s->n_tgt_blocks * s->block_size * a.dst_tok;
+
+  const hipStream_t stream = (hipStream_t)s->stream;
+  rc = launch_status(helm::launch_paged_rows(cu, s->n_requests, src_bt, s->max_blocks_src, s->n_src_blocks,
+                                             tgt_bt, s->max_blocks_tgt, s->n_tgt_blocks, s->block_size,
+                                             s->n_tokens_total, src_row, dst_row, stream),
+                     "paged slot kernel launch");
+  if (rc != HELM_OK) return rc;
+  return run_transfer(a, s->dtype, src_pos, tgt_pos, s->rope_theta_src, s->rope_theta_tgt, stream);
+}
+
+}  // extern "C"

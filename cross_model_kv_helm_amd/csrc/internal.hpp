@@ -1,0 +1,59 @@
+// internal.hpp — declarations shared by the library's translation units.
+// Not installed; the public interface is include/helm_kv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace helm {
+
+// One transfer, in the form every kernel consumes.  Source rows and target
+// rows are addressed through strides so that the contiguous layout
+// [L, H, T, D] and the paged layout [L, n_blocks * block_size, H, D] share
+// the kernels:
+//   source element (s, h, n, d) = src + s*src_layer + h*src_head + row*src_tok + d
+// with row = n (contiguous) or row = src_row[n] (paged, -1 = skip token).
+struct XferArgs {
+  const void* src_k;
+  const void* src_v;
+  const int32_t* layer_sel;   // [L_t, k]
+  const void* W_k;            // [L_t, H, k*D, D]
+  const float* b_k;           // [L_t, H, D]
+  const void* W_v;
+  const float* b_v;
+  void* out_k;
+  void* out_v;
+  const float2* rope_src;     // [n_tok, D/2] (cos, sin) at src_pos, theta_src
+  const float2* rope_tgt;     // [n_tok, D/2] (cos, sin) at tgt_pos, theta_tgt
+  const int32_t* src_row;     // [n_tok] or nullptr (identity)
+  const int32_t* dst_row;     // [n_tok] or nullptr (identity)
+  int64_t n_tok;
+  int32_t L_s, L_t, H, D, k;
+  int64_t src_layer, src_head, src_tok;   // element strides
+  int64_t dst_layer, dst_head, dst_tok;
+};
+
+enum class Dtype : int { BF16 = 0, F32 = 1 };
+
+// K1: cos/sin tables of the RoPE angles for src_pos and tgt_pos.
+hipError_t launch_rope_tables(const int32_t* src_pos, const int32_t* tgt_pos, int64_t n_tok,
+                              int32_t D, double theta_src, double theta_tgt,
+                              float2* rope_src, float2* rope_tgt, hipStream_t stream);
+
+// Paged prologue: per packed token, the physical source and target slot
+// (block * block_size + offset), or -1 when a table entry is out of range.
+hipError_t launch_paged_rows(const int32_t* cu_seqlens, int32_t n_requests,
+                             const int32_t* src_bt, int32_t max_blocks_src, int32_t n_src_blocks,
+                             const int32_t* tgt_bt, int32_t max_blocks_tgt, int32_t n_tgt_blocks,
+                             int32_t block_size, int64_t n_tok,
+                             int32_t* src_row, int32_t* dst_row, hipStream_t stream);
+
+// Portable transfer kernel: fp32 vector arithmetic, any supported D/k/dtype.
+hipError_t launch_transfer_generic(const XferArgs& a, Dtype dt, hipStream_t stream);
+
+// Matrix-core transfer kernel for bf16 storage.  Returns hipErrorNotSupported
+// (and enqueues nothing) when the shape is outside what it handles.
+hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream);
+bool mfma_supports(const XferArgs& a);
+
+}  // namespace helm

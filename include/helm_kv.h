@@ -1,0 +1,219 @@
+/*
+ * helm_kv.h — C ABI of the MI355X (gfx950) cross-model KV-cache transfer.
+ *
+ * The operation (pages: "Helm Intelligent Routing", section "Why carrying the
+ * cache across is the hard part"; the Qwen3 cache-mapping write-up, section
+ * "A linear bridge, strangely enough, suffices", its fit/map listing and its
+ * strip-RoPE / map / apply-RoPE diagram).  For every target layer l < L_t,
+ * KV head h < H and token t < T, with half = D/2 and the rotate-half RoPE
+ * rotation R(p; theta) that turns pair (i, i+half) by p * theta^(-2i/D):
+ *
+ *   x_k = concat_{j<k} R(-src_pos[t]; theta_src) src_k[layer_sel[l,j], h, t, :]
+ *   x_v = concat_{j<k} src_v[layer_sel[l,j], h, t, :]
+ *   out_k[l, h, t, :] = R(+tgt_pos[t]; theta_tgt) (x_k · W_k[l, h] + b_k[l, h])
+ *   out_v[l, h, t, :] =                            x_v · W_v[l, h] + b_v[l, h]
+ *
+ * i.e. un-rotate the pilot's keys into content space at their source
+ * positions, gather the same KV head from the k selected source layers (in
+ * the order of the layer_sel row), apply the per-(target layer, head) affine
+ * map — one for keys, one for values, W stored in-major [k*D][D] as in the
+ * listing's x @ w + b — and re-rotate the mapped keys at the positions they
+ * take in the target sequence.  The re-rotation is always applied; there is
+ * no switch to skip it.
+ *
+ * Precision.  bf16 storage: the un-rotated key is formed in fp32 and rounded
+ * once (nearest-even) to bf16 as the operand of a bf16 x bf16 matrix-core
+ * product with fp32 accumulation; bias and forward rotation are fp32; the
+ * result is rounded once (nearest-even) to bf16.  fp32 storage: the whole
+ * path is fp32.  RoPE angles are formed in fp64 (p * w_i) and their cos/sin
+ * rounded once to fp32, so positions up to 2^31 keep full accuracy.
+ *
+ * Pair requirements ("Helm Intelligent Routing", section "Requirements"):
+ * source and target share the KV-head count H and the head dimension D;
+ * their layer counts may differ.
+ *
+ * Conventions for every entry point.
+ *   - Every pointer to tensor data is a DEVICE pointer owned by the caller
+ *     (e.g. a torch tensor's data_ptr()); the library never frees, keeps or
+ *     allocates memory.  Tensors are dense, row-major, in the layouts given.
+ *   - Calls are asynchronous on shape->stream (a hipStream_t; NULL = the
+ *     null stream).  A HELM_OK return means the work was enqueued; device
+ *     faults surface at the caller's next synchronisation.
+ *   - All validation happens on the host before anything is enqueued: a call
+ *     that returns an error has written nothing, so the caller can fall back
+ *     to a normal target prefill ("Helm Intelligent Routing", section "What
+ *     happens when a transfer cannot be used": a refused transfer never fails
+ *     a request).  helm_last_error() then names the specific reason.
+ *   - Device-side tables (layer_sel, block tables, cu_seqlens) are not read
+ *     by the host.  Check them once with helm_mapper_check /
+ *     helm_paged_check on host copies.  The kernels still bounds-check every
+ *     index they read: a target layer whose layer_sel row holds an index
+ *     outside [0, L_s), or a token whose block id lies outside its pool, is
+ *     left unwritten instead of reading or writing out of bounds.
+ *   - Thread safety: calls may be made from several host threads; the only
+ *     library state is a per-thread error string and a per-device cache of
+ *     the device check.
+ */
+#ifndef HELM_KV_H
+#define HELM_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HELM_ABI_VERSION 1
+
+/* Status codes.  HELM_E_NO_DEVICE is 4 like the calibration tool's "no
+ * accelerator on this host" exit code ("Helm Intelligent Routing", section
+ * "What calibration does, and what it costs"). */
+typedef enum {
+  HELM_OK = 0,
+  HELM_E_INVALID_ARG = 1,  /* null pointer, non-positive size, k outside 1..L_s, overflow */
+  HELM_E_PAIR_SHAPE = 2,   /* D odd or unsupported for the dtype */
+  HELM_E_LAYER_SEL = 3,    /* a layer_sel entry outside [0, L_s) (helm_mapper_check) */
+  HELM_E_NO_DEVICE = 4,    /* no GPU visible */
+  HELM_E_DTYPE = 5,        /* unknown dtype code */
+  HELM_E_ARCH = 6,         /* the current device is not gfx950 */
+  HELM_E_WORKSPACE = 7,    /* workspace missing, misaligned or too small */
+  HELM_E_ALIAS = 8,        /* an output byte range overlaps an input or the other output */
+  HELM_E_PAGED_TABLE = 9,  /* bad cu_seqlens or block table (helm_paged_check) */
+  HELM_E_LAUNCH = 10       /* a HIP call failed; helm_last_error() holds its text */
+} helm_status_t;
+
+/* Storage dtype of caches and maps.  Biases are always fp32. */
+typedef enum { HELM_BF16 = 0, HELM_F32 = 1 } helm_dtype_t;
+
+/* Supported head dimensions: D = 64 or 128 (both dtypes). */
+
+/* Contiguous transfer shape.
+ *   src_k, src_v : [L_s, H, T, D]      dtype; keys stored rotated at src_pos
+ *   src_pos      : [T]                 int32, any values (negative allowed)
+ *   tgt_pos      : [T]                 int32, positions in the target sequence
+ *   layer_sel    : [L_t, k]            int32 in [0, L_s); duplicates allowed
+ *   W_k, W_v     : [L_t, H, k*D, D]    dtype, in-major (row m = input feature)
+ *   b_k, b_v     : [L_t, H, D]         fp32
+ *   out_k, out_v : [L_t, H, T, D]      dtype; fully overwritten
+ * Workspace: device memory of at least helm_kv_workspace_bytes(shape)
+ * bytes, 256-byte aligned, not shared with a concurrent call. */
+typedef struct {
+  int32_t n_src_layers;    /* L_s >= 1 */
+  int32_t n_tgt_layers;    /* L_t >= 1 */
+  int32_t n_kv_heads;      /* H >= 1 */
+  int32_t head_dim;        /* D in {64, 128} */
+  int32_t k;               /* 1 <= k <= L_s */
+  int32_t dtype;           /* helm_dtype_t */
+  int64_t n_tokens;        /* T >= 0; T = 0 returns HELM_OK without touching
+                              any pointer or the device */
+  double rope_theta_src;   /* > 0; the pilot's RoPE base */
+  double rope_theta_tgt;   /* > 0; the target's RoPE base */
+  void* stream;            /* hipStream_t */
+  void* workspace;         /* device scratch */
+  size_t workspace_bytes;
+} helm_shape_t;
+
+/* Paged transfer shape.  Pools are per-layer paged caches with pages of
+ * block_size token slots (16 in the benchmarked workload):
+ *   src_k_pool, src_v_pool : [L_s, n_src_blocks, block_size, H, D] dtype
+ *   tgt_k_pool, tgt_v_pool : [L_t, n_tgt_blocks, block_size, H, D] dtype
+ *   src_block_table        : [R, max_blocks_src] int32
+ *   tgt_block_table        : [R, max_blocks_tgt] int32
+ *   cu_seqlens             : [R+1] int32, cu[0] = 0, non-decreasing,
+ *                            cu[R] = n_tokens_total
+ *   src_pos, tgt_pos       : [n_tokens_total] int32 over packed tokens
+ * Token t of request r (packed index cu[r] + t) is read from slot
+ * t % block_size of block src_block_table[r][t / block_size] of every
+ * selected source layer and written to slot t % block_size of block
+ * tgt_block_table[r][t / block_size] of every target layer.  No other slot
+ * of the target pools is touched.  Two tokens must never share a target
+ * slot (helm_paged_check tests that the used target entries are distinct). */
+typedef struct {
+  int32_t n_src_layers, n_tgt_layers, n_kv_heads, head_dim, k, dtype;
+  int32_t block_size;      /* >= 1 */
+  int32_t n_requests;      /* R >= 1 */
+  int32_t max_blocks_src;  /* row stride of src_block_table */
+  int32_t max_blocks_tgt;  /* row stride of tgt_block_table */
+  int32_t n_src_blocks;    /* blocks per source pool layer */
+  int32_t n_tgt_blocks;    /* blocks per target pool layer */
+  int64_t n_tokens_total;  /* cu_seqlens[R]; the host passes it (no device read);
+                              0 returns HELM_OK without touching anything */
+  double rope_theta_src, rope_theta_tgt;
+  void* stream;
+  void* workspace;
+  size_t workspace_bytes;
+} helm_paged_shape_t;
+
+/* The contiguous transfer (definition at the top of this file).
+ * Returns HELM_OK once the kernels are enqueued on shape->stream, or an
+ * error with nothing enqueued.  out_k / out_v must not overlap any input. */
+int helm_kv_transfer(const void* src_k, const void* src_v,
+                     const int32_t* src_pos, const int32_t* tgt_pos,
+                     const int32_t* layer_sel,
+                     const void* W_k, const float* b_k,
+                     const void* W_v, const float* b_v,
+                     void* out_k, void* out_v,
+                     const helm_shape_t* shape);
+
+/* The same transfer on paged caches driven by block tables (knlp "Routing"
+ * page, request-flow figure: the selection is applied to the block table and
+ * only the selected blocks are written into the paged cache; "Helm
+ * Intelligent Routing", section "Current limitation": the installer writes
+ * into the inference engine's paged cache).  Same return convention. */
+int helm_kv_transfer_paged(const void* src_k_pool, const void* src_v_pool,
+                           const int32_t* src_block_table, const int32_t* tgt_block_table,
+                           const int32_t* cu_seqlens,
+                           const int32_t* src_pos, const int32_t* tgt_pos,
+                           const int32_t* layer_sel,
+                           const void* W_k, const float* b_k,
+                           const void* W_v, const float* b_v,
+                           void* tgt_k_pool, void* tgt_v_pool,
+                           const helm_paged_shape_t* shape);
+
+/* Workspace bytes the call with this shape needs (0 on an invalid shape;
+ * helm_last_error() then says why).  Pure host arithmetic. */
+size_t helm_kv_workspace_bytes(const helm_shape_t* shape);
+size_t helm_kv_paged_workspace_bytes(const helm_paged_shape_t* shape);
+
+/* Registration-time check of a mapper ("Helm Intelligent Routing", section
+ * "Requirements": an impossible pair is refused with the specific reason
+ * when it is registered).  layer_sel_host: HOST copy [L_t, k].  Checks the
+ * shape fields and that every entry lies in [0, L_s).  No device access. */
+int helm_mapper_check(const helm_shape_t* shape, const int32_t* layer_sel_host);
+
+/* Host-side check of a paged batch: cu_seqlens starts at 0, is
+ * non-decreasing and ends at n_tokens_total; every request fits its table
+ * rows; every used block id lies inside its pool; the used target block ids
+ * are pairwise distinct (so no two tokens race for a slot).  All pointers
+ * are HOST copies.  No device access. */
+int helm_paged_check(const helm_paged_shape_t* shape,
+                     const int32_t* src_block_table_host,
+                     const int32_t* tgt_block_table_host,
+                     const int32_t* cu_seqlens_host);
+
+/* Checks that `device` (or the current device when device < 0) exists and
+ * is a gfx950 part.  HELM_E_NO_DEVICE / HELM_E_ARCH otherwise (hardware the
+ * gate refuses keeps the whole feature off: "Helm Intelligent Routing",
+ * section "Safety rails that always apply"). */
+int helm_device_check(int device);
+
+/* Pure function behind the arch gate: 1 when a gcnArchName string (e.g.
+ * "gfx950:sramecc+:xnack-") names a supported target, else 0. */
+int helm_arch_supported(const char* gcn_arch_name);
+
+/* The calling thread's last error text ("" after success).  Owned by the
+ * library; valid until the thread's next call. */
+const char* helm_last_error(void);
+
+/* Static name of a status code ("HELM_OK", ...; "unknown" otherwise). */
+const char* helm_status_string(int status);
+
+/* HELM_ABI_VERSION of the built library. */
+int helm_abi_version(void);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif /* HELM_KV_H */

@@ -385,7 +385,9 @@ int oracle_max_threads(void) {
 /* out[l, h, t, :] = round_dtype(R(pos[t]; theta) in[l, h, t, :]) for a cache
  * [n_layers, H, T, D] stored in dtype (same storage for in and out; they may
  * alias).  This is how a model leaves keys in its cache: rotated at the
- * position each token was produced at.  Returns 0, or 1 on a bad argument. */
+ * position each token was produced at.  The cos/sin of a token's angles are
+ * evaluated once per token and reused for its n_layers*H rows.
+ * Returns 0, or 1 on a bad argument. */
 int oracle_encode_keys(const void* in, void* out, int32_t dtype,
                        int64_t n_layers, int64_t H, int64_t T, int32_t D,
                        const int32_t* pos, double theta, int32_t n_threads) {
@@ -396,34 +398,45 @@ int oracle_encode_keys(const void* in, void* out, int32_t dtype,
 #else
   (void)n_threads;
 #endif
-  const int64_t n_rows = n_layers * H * T;
+  const int32_t half = D / 2;
   int bad = 0;
 #pragma omp parallel
   {
-    double* buf = (double*)malloc(sizeof(double) * (size_t)(2 * D));
-    if (!buf) {
+    double* cs = (double*)malloc(sizeof(double) * (size_t)(2 * half));
+    if (!cs) {
 #pragma omp atomic write
       bad = 1;
     } else {
 #pragma omp for schedule(static)
-      for (int64_t r = 0; r < n_rows; ++r) {
-        const int64_t t = r % T;
-        for (int32_t d = 0; d < D; ++d) buf[d] = load_elem(in, dtype, r * D + d);
-        oracle_rope(buf, buf + D, D, (double)pos[t], theta);
-        for (int32_t d = 0; d < D; ++d) {
-          const double v = round_to_dtype(buf[D + d], dtype);
-          if (dtype == ORACLE_BF16) {
-            float f = (float)v;  /* exact: v is a bf16 value */
-            uint32_t u;
-            memcpy(&u, &f, sizeof u);
-            ((uint16_t*)out)[r * D + d] = (uint16_t)(u >> 16);
-          } else {
-            ((float*)out)[r * D + d] = (float)v;
+      for (int64_t t = 0; t < T; ++t) {
+        for (int32_t i = 0; i < half; ++i) {
+          const double a = (double)pos[t] * oracle_rope_freq(i, D, theta);
+          cs[2 * i] = cos(a);
+          cs[2 * i + 1] = sin(a);
+        }
+        for (int64_t lh = 0; lh < n_layers * H; ++lh) {
+          const int64_t r = lh * T + t;
+          for (int32_t i = 0; i < half; ++i) {
+            const double lo = load_elem(in, dtype, r * D + i);
+            const double hi = load_elem(in, dtype, r * D + i + half);
+            const double o[2] = {lo * cs[2 * i] - hi * cs[2 * i + 1], hi * cs[2 * i] + lo * cs[2 * i + 1]};
+            const int64_t idx[2] = {r * D + i, r * D + i + half};
+            for (int q = 0; q < 2; ++q) {
+              const double v = round_to_dtype(o[q], dtype);
+              if (dtype == ORACLE_BF16) {
+                float f = (float)v;  /* exact: v is a bf16 value */
+                uint32_t u;
+                memcpy(&u, &f, sizeof u);
+                ((uint16_t*)out)[idx[q]] = (uint16_t)(u >> 16);
+              } else {
+                ((float*)out)[idx[q]] = (float)v;
+              }
+            }
           }
         }
       }
     }
-    free(buf);
+    free(cs);
   }
   return bad;
 }

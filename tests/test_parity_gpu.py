@@ -1,0 +1,254 @@
+"""GPU parity: the HIP library against the fp64 oracle on identical seeded inputs.
+
+Every call goes through the C ABI (via the ctypes binding).  Small cases are
+compared element by element in full; full-size workloads are compared on
+sampled rows (every (layer, head) slab, with first/last tokens and tile edges
+always included) in exactly the launch configuration the benchmark times.
+Tolerances: see tests/parity.py.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import parity
+from tests.parity import Case, check_case, log, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library():
+    import cross_model_kv_helm_amd as hk
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert hk.helm_device_check(-1) == 0, hk.helm_last_error()
+    yield
+
+
+def W(name, **kw):
+    return dataclasses.replace(synth.CONFIGS[name], **kw)
+
+
+SMALL_BF16 = synth.Workload("small_bf16", 6, 5, 2, 128, 300, 3, "bf16", 1e6, "same", 11)
+
+
+# ---------------------------------------------------------------- small, full compare
+def test_tiny_fp32_full():
+    case = Case(synth.CONFIGS["tiny_fp32"])
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *out)
+
+
+def test_small_bf16_ragged_full():
+    case = Case(SMALL_BF16)
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *out)
+
+
+def test_small_bf16_d64_full():
+    case = Case(dataclasses.replace(SMALL_BF16, name="small_bf16_d64", head_dim=64, n_tokens=77, seed=12))
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *out)
+
+
+def test_fp32_d128_shift_full():
+    w = dataclasses.replace(SMALL_BF16, name="small_f32_shift", dtype="f32", positions="shift4096",
+                            n_tokens=70, seed=13)
+    case = Case(w)
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *out)
+
+
+def test_qwen3_06b_17b_t512_full():
+    case = Case(synth.CONFIGS["qwen3_0.6b_1.7b_t512"])
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *out)
+
+
+def test_qwen3_06b_17b_t2048_sampled():
+    w = synth.CONFIGS["qwen3_0.6b_1.7b_t2048"]
+    case = Case(w)
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *out, rows=sample_rows(w.n_tgt_layers, w.n_kv_heads, case.T, 24, 1))
+
+
+# ---------------------------------------------------------------- edge cases
+def test_single_token_and_duplicate_selection():
+    w = dataclasses.replace(SMALL_BF16, name="one_token_dup", n_tokens=1, k=3, seed=14)
+    sel = np.array([[2, 2, 0], [5, 1, 5], [0, 0, 0], [3, 4, 1], [1, 1, 2]], np.int32)
+    case = Case(w, layer_sel=sel, src_pos=[77], tgt_pos=[123456])
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *out)
+
+
+def test_k1_negative_and_large_positions_distinct_thetas():
+    w = dataclasses.replace(SMALL_BF16, name="k1_positions", k=1, n_tokens=200, seed=15)
+    rng = np.random.default_rng(3)
+    src = rng.integers(-100000, 2 ** 31 - 1, 200).astype(np.int32)
+    tgt = rng.integers(-(2 ** 31), 2 ** 31 - 1, 200).astype(np.int32)
+    case = Case(w, src_pos=src, tgt_pos=tgt)
+    # a target whose RoPE base differs from the pilot's
+    case.w = dataclasses.replace(w, theta=1e6)
+    d = case.dev
+    import cross_model_kv_helm_amd as hk
+    shape = (w.n_tgt_layers, w.n_kv_heads, case.T, w.head_dim)
+    ok_, ov_ = torch.empty(shape, dtype=torch.bfloat16, device="cuda"), torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    s = hk.make_shape(d["src_k"], d["W_k"], d["layer_sel"], 1e6, 5e5)
+    hk.helm_kv_transfer(d["src_k"], d["src_v"], d["src_pos"], d["tgt_pos"], d["layer_sel"], d["W_k"],
+                        d["b_k"], d["W_v"], d["b_v"], ok_, ov_, s)
+    torch.cuda.synchronize()
+    pb = case.problem()
+    pb.theta_tgt = 5e5
+    h = case.host
+    ref_k, ref_v = oracle.transfer_rows(pb, h["src_k"], h["src_v"], h["src_pos"], h["tgt_pos"], h["layer_sel"],
+                                        h["W_k"], h["b_k"], h["W_v"], h["b_v"])
+    D = w.head_dim
+    slab = np.arange(ref_k.size // D) // case.T
+    parity.compare(parity.storage_to_f64(parity.to_np_storage(ok_)).reshape(-1, D), ref_k.reshape(-1, D),
+                   slab, "bf16", "k1_positions K")
+    parity.compare(parity.storage_to_f64(parity.to_np_storage(ov_)).reshape(-1, D), ref_v.reshape(-1, D),
+                   slab, "bf16", "k1_positions V")
+
+
+def test_zero_tokens_writes_nothing():
+    import cross_model_kv_helm_amd as hk
+    w = dataclasses.replace(SMALL_BF16, n_tokens=0)
+    c = synth.contiguous_inputs(w, device="cuda", n_tokens=0)
+    out = torch.full((5, 2, 0, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    s = hk.make_shape(c["k_content"], c["W_k"], c["layer_sel"], 1e6, 1e6)
+    hk.helm_kv_transfer(c["k_content"], c["src_v"], c["src_pos"], c["tgt_pos"], c["layer_sel"], c["W_k"],
+                        c["b_k"], c["W_v"], c["b_v"], out, out.clone(), s)
+    torch.cuda.synchronize()
+
+
+def test_invalid_device_layer_sel_leaves_target_layer_unwritten():
+    """A layer_sel row with an index outside [0, L_s) that reaches the device
+    is not read: that target layer is left as it was; the others are mapped."""
+    w = dataclasses.replace(SMALL_BF16, name="bad_sel", n_tokens=40, seed=16)
+    case = Case(w)
+    sel = case.host["layer_sel"].copy()
+    sel[2, 1] = 99
+    case.dev["layer_sel"] = torch.from_numpy(sel).cuda()
+    shape = (w.n_tgt_layers, w.n_kv_heads, case.T, w.head_dim)
+    sentinel = torch.full(shape, 3.0, dtype=torch.bfloat16, device="cuda")
+    out = (sentinel.clone(), sentinel.clone())
+    case.run_gpu(out)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0][2], sentinel[2]) and torch.equal(out[1][2], sentinel[2])
+    good = np.array([l for l in range(5) if l != 2])
+    rows = np.concatenate([(l * w.n_kv_heads + h) * case.T + np.arange(case.T)
+                           for l in good for h in range(w.n_kv_heads)])
+    case.host["layer_sel"] = np.where(sel == 99, 0, sel).astype(np.int32)
+    check_case(case, *out, rows=rows, label="valid rows of ")
+
+
+def test_bitwise_deterministic():
+    case = Case(dataclasses.replace(SMALL_BF16, name="det", n_tokens=513, seed=17))
+    a = case.run_gpu()
+    b = case.run_gpu()
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+
+
+# ---------------------------------------------------------------- paged
+class PagedCase:
+    def __init__(self, w: synth.Workload, lens=None):
+        self.w = w
+        self.lay = lay = synth.paged_layout(w, lens=lens)
+        c = synth.paged_content(w, lay, device="cuda")
+        dt = parity.oracle_dtype(w)
+        k_enc = oracle.encode_keys(parity.to_np_storage(c.pop("k_content")), lay.src_pos, w.theta, dt)
+        k_dev = parity.from_np_storage(k_enc, "cuda")
+        del k_enc
+        self.dev = dict(c)
+        self.dev["src_k_pool"] = synth.scatter_to_pool(k_dev, lay, lay.src_bt, lay.n_src_blocks, synth.CANARY_BITS)
+        self.dev["src_v_pool"] = synth.scatter_to_pool(c["src_v"], lay, lay.src_bt, lay.n_src_blocks, synth.CANARY_BITS)
+        del k_dev, self.dev["src_v"]
+        for name, arr in (("src_bt", lay.src_bt), ("tgt_bt", lay.tgt_bt), ("cu", lay.cu_seqlens)):
+            self.dev[name] = torch.from_numpy(arr).cuda()
+        self.host = {k: parity.to_np_storage(v) for k, v in self.dev.items()}
+
+    def run_gpu(self):
+        import cross_model_kv_helm_amd as hk
+        d, w, lay = self.dev, self.w, self.lay
+        tk = synth.empty_target_pool(w, lay, "cuda")
+        tv = synth.empty_target_pool(w, lay, "cuda")
+        s = hk.make_paged_shape(d["src_k_pool"], tk, d["W_k"], d["layer_sel"], d["src_bt"], d["tgt_bt"],
+                                lay.n_tokens, w.theta, w.theta)
+        assert hk.helm_paged_check(s, lay.src_bt, lay.tgt_bt, lay.cu_seqlens) == 0, hk.helm_last_error()
+        hk.helm_kv_transfer_paged(d["src_k_pool"], d["src_v_pool"], d["src_bt"], d["tgt_bt"], d["cu"],
+                                  d["src_pos"], d["tgt_pos"], d["layer_sel"], d["W_k"], d["b_k"], d["W_v"],
+                                  d["b_v"], tk, tv, s)
+        return tk, tv
+
+    def check(self, tk, tv, rows=None):
+        w, lay, h = self.w, self.lay, self.host
+        pb = oracle.Problem(w.n_src_layers, w.n_tgt_layers, w.n_kv_heads, w.head_dim, w.k,
+                            n_tokens=lay.n_tokens, theta_src=w.theta, theta_tgt=w.theta,
+                            dtype=parity.oracle_dtype(w))
+        pg = oracle.Paged(lay.block_size, len(lay.lens), lay.max_blocks, lay.max_blocks,
+                          lay.n_src_blocks, lay.n_tgt_blocks)
+        ref_k, ref_v, dst = oracle.transfer_paged_rows(
+            pb, pg, h["src_k_pool"], h["src_v_pool"], h["src_bt"], h["tgt_bt"], h["cu"], h["src_pos"],
+            h["tgt_pos"], h["layer_sel"], h["W_k"], h["b_k"], h["W_v"], h["b_v"], rows=rows)
+        D = w.head_dim
+        idx = torch.from_numpy(dst[:, None] + np.arange(D)[None, :]).cuda()
+        g_k = parity.storage_to_f64(parity.to_np_storage(tk.reshape(-1)[idx]))
+        g_v = parity.storage_to_f64(parity.to_np_storage(tv.reshape(-1)[idx]))
+        n_rows = np.arange(ref_k.shape[0]) if rows is None else rows
+        slab = n_rows // lay.n_tokens
+        parity.compare(g_k, ref_k, slab, w.dtype, f"{w.name} K")
+        parity.compare(g_v, ref_v, slab, w.dtype, f"{w.name} V")
+        # every slot no token owns still holds the canary
+        canary = np.int16(np.uint16(synth.CANARY_BITS).view(np.int16))
+        owned = torch.from_numpy(synth.slot_index(lay, lay.tgt_bt)).cuda()
+        for pool in (tk, tv):
+            flat = pool.view(w.n_tgt_layers, -1, w.n_kv_heads, D).view(torch.int16)
+            mask = torch.ones(flat.shape[1], dtype=torch.bool, device="cuda")
+            mask[owned] = False
+            assert bool((flat[:, mask] == canary).all()), "a slot outside every request was written"
+            assert not bool((flat[:, owned] == canary).any()), "an owned slot was not written"
+
+
+def test_paged_small_full():
+    w = synth.Workload("paged_small", 5, 4, 2, 128, 0, 2, "bf16", 1e6, "same", 31, paged=True,
+                       n_requests=5, max_offset=300)
+    pc = PagedCase(w, lens=[1, 16, 17, 40, 3])
+    tk, tv = pc.run_gpu()
+    torch.cuda.synchronize()
+    pc.check(tk, tv)
+
+
+def test_paged_32_requests_sampled():
+    w = synth.CONFIGS["paged_32req"]
+    pc = PagedCase(w)
+    log(f"paged: N={pc.lay.n_tokens} tokens, {pc.lay.n_src_blocks} src blocks")
+    tk, tv = pc.run_gpu()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    N = pc.lay.n_tokens
+    # every slab, each request's first and last token, plus random tokens
+    edges = np.concatenate([pc.lay.cu_seqlens[:-1], pc.lay.cu_seqlens[1:] - 1])
+    toks = np.unique(np.concatenate([edges, rng.integers(0, N, 32)]))
+    rows = np.concatenate([g * N + toks for g in range(w.n_tgt_layers * w.n_kv_heads)])
+    pc.check(tk, tv, rows=rows)
+
+
+# ---------------------------------------------------------------- full-size workloads
+def test_qwen3_14b_32b_t32k_sampled():
+    w = synth.CONFIGS["qwen3_14b_32b_t32k"]
+    case = Case(w)
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *out, rows=sample_rows(w.n_tgt_layers, w.n_kv_heads, case.T, 12, 2))
