@@ -1,0 +1,223 @@
+"""Benchmark of the cross-model KV-cache transfer on one MI355X.
+
+One step = one full transfer (RoPE tables + the transfer kernel) of the
+Qwen3-14B -> 32B-shaped workload: 40 source -> 64 target layers, 8 KV heads,
+head_dim 128, k = 4 selected source layers per target layer, 32,768 tokens,
+bf16 caches and maps, fp32 bias — the configuration the headline mapper time
+is quoted on (Qwen3 cache-mapping write-up, section "What the headline number
+actually covers").  Inputs are seeded synthetic draws (synth/) resident in
+HBM before the timed region.
+
+Prints ONE JSON line: mapped KV tokens/s (tokens whose K and V are written
+for every target layer and head), ms per 32K-token transfer, the roofline of
+the transfer kernel, and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 matrix cores
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_work(w, layer_sel, T):
+    """(bytes, flops) one transfer must move / compute at minimum.
+
+    bytes = every selected source layer read once (K and V) + the target
+    cache written once (K and V) + W and bias read once + positions.
+    flops = 2 * (K and V) * L_t * H * T * (k*D) * D (the two maps)."""
+    import numpy as np
+    L_t, H, D, k = w.n_tgt_layers, w.n_kv_heads, w.head_dim, w.k
+    used = len(np.unique(np.asarray(layer_sel)))
+    es = 2 if w.dtype == "bf16" else 4
+    src = 2 * used * H * T * D * es
+    tgt = 2 * L_t * H * T * D * es
+    wts = 2 * L_t * H * k * D * D * es + 2 * L_t * H * D * 4
+    pos = 2 * T * 4
+    flops = 2 * 2 * L_t * H * T * (k * D) * D
+    return src + tgt + wts + pos, flops, dict(src=src, tgt=tgt, weights=wts, positions=pos, used_src_layers=used)
+
+
+def encode_keys_on_gpu(hk, k_content, src_pos, theta):
+    """Position-encodes the synthetic content keys with the library itself
+    (k = 1, identity map, zero bias, un-rotation at position 0): the source
+    cache then holds R(src_pos) * key rounded to bf16, as a model leaves it."""
+    import torch
+    L, H, T, D = k_content.shape
+    dev = k_content.device
+    eye = torch.eye(D, dtype=k_content.dtype, device=dev).expand(L, H, D, D).contiguous()
+    zero_b = torch.zeros((L, H, D), dtype=torch.float32, device=dev)
+    sel = torch.arange(L, dtype=torch.int32, device=dev).reshape(L, 1)
+    zeros = torch.zeros_like(src_pos)
+    out_k = torch.empty_like(k_content)
+    out_v = torch.empty_like(k_content)
+    s = hk.make_shape(k_content, eye, sel, theta, theta)
+    hk.helm_kv_transfer(k_content, k_content, zeros, src_pos, sel, eye, zero_b, eye, zero_b, out_k, out_v, s)
+    torch.cuda.synchronize()
+    del out_v, eye
+    return out_k
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle (as is) on a bounded sample of the same workload: all
+    target layers and heads, K and V, for the first T_s tokens; T_s grows
+    until one run takes >= budget_s/4, then the run that follows is timed."""
+    import numpy as np
+    import oracle
+    import synth
+    from tests.parity import oracle_dtype, to_np_storage
+
+    threads = oracle.max_threads()
+    T_s, elapsed = 8, 0.0
+    while True:
+        c = synth.contiguous_inputs(w, device="cpu", n_tokens=T_s)
+        host = {k: to_np_storage(v) for k, v in c.items() if k != "k_content"}
+        host["src_k"] = oracle.encode_keys(to_np_storage(c["k_content"]), host["src_pos"], w.theta, oracle_dtype(w))
+        pb = oracle.Problem(w.n_src_layers, w.n_tgt_layers, w.n_kv_heads, w.head_dim, w.k, n_tokens=T_s,
+                            theta_src=w.theta, theta_tgt=w.theta, dtype=oracle_dtype(w), quantize_content=True)
+        t0 = time.perf_counter()
+        oracle.transfer_rows(pb, host["src_k"], host["src_v"], host["src_pos"], host["tgt_pos"],
+                             host["layer_sel"], host["W_k"], host["b_k"], host["W_v"], host["b_v"])
+        elapsed = time.perf_counter() - t0
+        log(f"cpu oracle: {T_s} tokens in {elapsed:.2f} s on {threads} threads")
+        if elapsed >= budget_s / 4 or T_s >= w.n_tokens:
+            break
+        T_s = min(w.n_tokens, int(T_s * max(2.0, min(8.0, budget_s / 2 / max(elapsed, 1e-3)))))
+    return {"value": T_s / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name} shapes (all {w.n_tgt_layers} target layers x {w.n_kv_heads} heads, K and V), "
+                      f"first {T_s} tokens, fp64 C oracle with OpenMP, {elapsed:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_14b_32b_t32k")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the transfer shards by KV head with no exchange, "
+              f"and this build runs on a single MI355X (got --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import cross_model_kv_helm_amd as hk
+    import synth
+
+    if not os.path.exists(hk.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if hk.helm_device_check(0) != 0:
+        raise SystemExit(f"device check failed: {hk.helm_last_error()}")
+
+    w = synth.CONFIGS[args.workload]
+    assert not w.paged, "bench.py times the contiguous workloads"
+    log(f"workload {w.name}: drawing inputs on the GPU")
+    c = synth.contiguous_inputs(w, device=dev)
+    src_k = encode_keys_on_gpu(hk, c.pop("k_content"), c["src_pos"], w.theta)
+    T = src_k.shape[2]
+    out_shape = (w.n_tgt_layers, w.n_kv_heads, T, w.head_dim)
+    out_k = torch.empty(out_shape, dtype=src_k.dtype, device=dev)
+    out_v = torch.empty(out_shape, dtype=src_k.dtype, device=dev)
+    shape = hk.make_shape(src_k, c["W_k"], c["layer_sel"], w.theta, w.theta)
+    shape.stream = hk.current_stream_ptr(dev)
+    ws = torch.empty(hk.helm_kv_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    # a buffer larger than the 256 MB last-level cache, rewritten between steps
+    # so small workloads are timed from HBM, not from cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if out_k.numel() * 4 < (1 << 30) else None
+
+    def step():
+        hk.helm_kv_transfer(src_k, c["src_v"], c["src_pos"], c["tgt_pos"], c["layer_sel"], c["W_k"], c["b_k"],
+                            c["W_v"], c["b_v"], out_k, out_v, shape, workspace=ws)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])   # ms
+    ms = float(per.mean())
+    log(f"per step: mean {ms:.4f} ms, median {np.median(per):.4f}, p10 {np.percentile(per, 10):.4f}, "
+        f"p90 {np.percentile(per, 90):.4f}; wall {wall:.3f} s")
+
+    B, F, parts = algorithmic_work(w, c["layer_sel"].cpu().numpy(), T)
+    t_s = ms * 1e-3
+    hbm_frac = B / t_s / HBM_PEAK
+    mfma_frac = F / t_s / MFMA_BF16_PEAK
+    t_hbm, t_mfma = B / HBM_PEAK, F / MFMA_BF16_PEAK
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": B / t_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": hbm_frac, "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": F / t_s / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                "frac": mfma_frac, "traffic": None}
+    roof["mfma_frac"] = mfma_frac
+    roof["hbm_frac"] = hbm_frac
+    roof["algorithmic_bytes"] = B
+    roof["algorithmic_flops"] = F
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    line = {
+        "metric": "mapped KV tokens/s (and ms per 32K-token transfer)",
+        "value": T / t_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "ms_per_transfer": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "src_layers": w.n_src_layers, "tgt_layers": w.n_tgt_layers,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "k": w.k, "tokens": T,
+                   "rope_theta": w.theta, "positions": w.positions, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "bytes_breakdown": parts,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -69,8 +69,9 @@ paged_rows_kernel(const int32_t* __restrict__ cu, int32_t R,
         if (b >= 0 && b < n_tgt_blocks) dr = (int32_t)((int64_t)b * bs + off);
       }
     }
-    src_row[n] = sr;
-    dst_row[n] = dr;
+    // a token is mapped only when both of its slots are valid
+    src_row[n] = (sr >= 0 && dr >= 0) ? sr : -1;
+    dst_row[n] = (sr >= 0 && dr >= 0) ? dr : -1;
   }
 }
 

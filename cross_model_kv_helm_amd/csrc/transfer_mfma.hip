@@ -29,9 +29,10 @@
 //     head.  All target layers of that head sweep the same tokens at about
 //     the same time, so each source row is fetched from HBM once and then
 //     served from that XCD's L2 to the ~6 target layers that select it.
-//   * Activation tile through LDS, double-buffered, one barrier per tile.
-//     Rows are XOR-swizzled in 16-byte chunks so the 16 lanes of a B-operand
-//     read hit distinct banks.
+//   * 16-token activation tiles through LDS, double-buffered, one barrier
+//     per tile.
+//     Rows are padded by 16 bytes so the 16 lanes of a B-operand read hit
+//     distinct banks.
 #include "internal.hpp"
 
 namespace helm {
@@ -44,7 +45,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;          // head dimension
 constexpr int kHalf = 64;
 constexpr int kThreads = 256;    // 4 waves
-constexpr int kTile = 32;        // tokens per tile (2 MFMA token blocks)
+constexpr int kTile = 16;        // tokens per tile (one MFMA token block)
+constexpr int kTB = kTile / 16;  // MFMA token blocks per tile
+constexpr int kStageRow = kD + 8; // W^T staging row: 128 inputs of one output column, padded
 
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -61,21 +64,27 @@ template <int KSEL>
 struct Cfg {
   static constexpr int KD = KSEL * kD;          // GEMM depth
   static constexpr int KSTEPS = KD / 32;        // 16x16x32 MFMA steps
-  static constexpr int CHUNKS = KD / 8;         // 16-byte chunks per LDS row
-  static constexpr int TILE_ELEMS = kTile * KD;
+  static constexpr int ROW = KD + 8;            // LDS row: one token, padded by 16 bytes
+  static constexpr int TILE_ELEMS = kTile * ROW;
 };
 
-// LDS element offset of chunk `c` (8 bf16) of token row `t`, swizzled.
+// LDS element offset of chunk `c` (8 bf16) of token row `t`.  The 16-byte
+// pad per row puts the 16 rows a B-operand read touches on distinct banks,
+// and keeps offsets additive so every k-step uses an immediate offset.
 template <int KSEL>
 __device__ __forceinline__ int lds_off(int t, int c) {
-  return t * Cfg<KSEL>::KD + ((c ^ (t & 15)) << 3);
+  return t * Cfg<KSEL>::ROW + (c << 3);
 }
 
 template <int KSEL>
 __global__ void __launch_bounds__(kThreads, 2)
 transfer_mfma_kernel(XferArgs a, int32_t n_groups, int64_t chunk_tokens, int64_t n_items) {
   using C = Cfg<KSEL>;
-  __shared__ __attribute__((aligned(16))) __bf16 xs[2][C::TILE_ELEMS];
+  // One LDS buffer serves two purposes: the W^T staging block while a group's
+  // weights are loaded, then the two activation tiles.
+  constexpr int kLdsElems = 2 * C::TILE_ELEMS > kD * kStageRow ? 2 * C::TILE_ELEMS : kD * kStageRow;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[kLdsElems];
+  __bf16 (*xs)[C::TILE_ELEMS] = reinterpret_cast<__bf16 (*)[C::TILE_ELEMS]>(lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,8 +99,7 @@ transfer_mfma_kernel(XferArgs a, int32_t n_groups, int64_t chunk_tokens, int64_t
     const int32_t h = g % a.H;
     const int32_t rest = g / a.H;
     const int32_t l = rest % a.L_t;
-    const bool is_k = rest >= a.L_t;   // values first? no: rest < L_t -> K
-    const bool keys = !is_k;
+    const bool keys = rest < a.L_t;    // groups [0, L_t*H) are keys, the rest values
     const int64_t t_begin = chunk * chunk_tokens;
     int64_t t_end = t_begin + chunk_tokens;
     if (t_end > a.n_tok) t_end = a.n_tok;
@@ -113,17 +121,37 @@ transfer_mfma_kernel(XferArgs a, int32_t n_groups, int64_t chunk_tokens, int64_t
     uint16_t* out = (uint16_t*)(keys ? a.out_k : a.out_v);
 
     // ---- W^T fragments for this wave's two 16-column blocks, in registers.
-    // lane holds W[m = 32s + 8*lgrp + i][n = ncol + lrow], i < 8.
+    // lane holds W[m = 32s + 8*lgrp + i][n = ncol + lrow], i < 8.  W is
+    // staged through LDS one 128-row block at a time, transposed on the way
+    // in (coalesced 16-byte global loads, 2-byte LDS stores), so that each
+    // fragment is one 16-byte LDS read.
     const int ncol0 = 16 * wave, ncol1 = kHalf + 16 * wave;
     bf16x8 wf[2][C::KSTEPS];
+    {
+      __bf16* stage = lds;                            // W^T block [kD][kStageRow]
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
+      for (int part = 0; part < KSEL; ++part) {
+        __syncthreads();                              // earlier readers of the buffer are done
+        const u32x4* gsrc = (const u32x4*)(W + (int64_t)part * kD * kD);
+#pragma unroll 2
+        for (int e = tid; e < kD * kD / 8; e += kThreads) {
+          const u32x4 v = gsrc[e];
+          const int m = e >> 4, n0 = (e & 15) << 3;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int m = 32 * s + 8 * lgrp + i;
-        wf[0][s][i] = __builtin_bit_cast(__bf16, W[(int64_t)m * kD + ncol0 + lrow]);
-        wf[1][s][i] = __builtin_bit_cast(__bf16, W[(int64_t)m * kD + ncol1 + lrow]);
+          for (int q = 0; q < 4; ++q) {
+            stage[(n0 + 2 * q) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] & 0xffffu));
+            stage[(n0 + 2 * q + 1) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] >> 16));
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int s = 4 * part + s4, m = 32 * s4 + 8 * lgrp;
+          wf[0][s] = *(const bf16x8*)&stage[(ncol0 + lrow) * kStageRow + m];
+          wf[1][s] = *(const bf16x8*)&stage[(ncol1 + lrow) * kStageRow + m];
+        }
       }
+      __syncthreads();                                // the buffer is reused by the first tile
     }
     // bias for the 4 columns this lane's accumulators hold in each block
     float b0[4], b1[4];
@@ -133,75 +161,77 @@ transfer_mfma_kernel(XferArgs a, int32_t n_groups, int64_t chunk_tokens, int64_t
       b1[j] = bias[ncol1 + 4 * lgrp + j];
     }
 
-    // ---- prologue assignment: thread -> (token pt, 16-byte chunk pc of the low half)
-    const int pt = tid >> 3;        // 0..31
-    const int pc = tid & 7;         // dims 8pc..8pc+7 and 64+8pc..
+    // ---- prologue assignment: thread -> (token pt, 16-byte chunk pc of the low
+    // half, layer parity pj): it loads dims 8pc.. and 64+8pc.. of layers pj, pj+2, ..
+    const int pt = tid >> 4;        // 0..15
+    const int pj = (tid >> 3) & 1;
+    const int pc = tid & 7;
+    constexpr int kMine = (KSEL + 1) / 2;   // layers per thread (upper bound)
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += kTile) {
       // -- gather (+ un-rotate) one tile into xs[buf]
       {
         const int64_t n = t0 + pt;
-        u32x4 lo[KSEL], hi[KSEL];
+        u32x4 lo[kMine], hi[kMine];
         bool have = n < t_end;
         int64_t row = 0;
         if (have) {
           row = a.src_row ? (int64_t)a.src_row[n] : n;
           have = row >= 0;
         }
+#pragma unroll
+        for (int q = 0; q < kMine; ++q) {
+          lo[q] = u32x4{0, 0, 0, 0};
+          hi[q] = u32x4{0, 0, 0, 0};
+        }
         if (have) {
 #pragma unroll
-          for (int j = 0; j < KSEL; ++j) {
-            const uint16_t* p = src + (int64_t)sel[j] * a.src_layer + (int64_t)h * a.src_head +
-                                row * a.src_tok + 8 * pc;
-            lo[j] = *(const u32x4*)p;
-            hi[j] = *(const u32x4*)(p + kHalf);
+          for (int q = 0; q < kMine; ++q) {
+            const int j = pj + 2 * q;
+            if (j < KSEL) {
+              const uint16_t* p = src + (int64_t)sel[j] * a.src_layer + (int64_t)h * a.src_head +
+                                  row * a.src_tok + 8 * pc;
+              lo[q] = *(const u32x4*)p;
+              hi[q] = *(const u32x4*)(p + kHalf);
+            }
           }
           if (keys) {
             const float4* cs4 = (const float4*)(a.rope_src + n * kHalf + 8 * pc);
-            float c[8], s[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float4 v = cs4[q];
-              c[2 * q] = v.x; s[2 * q] = v.y; c[2 * q + 1] = v.z; s[2 * q + 1] = v.w;
-            }
+            for (int e = 0; e < 4; ++e) {
+              const float4 v = cs4[e];   // (cos, sin) of dims 8pc+2e and 8pc+2e+1
 #pragma unroll
-            for (int j = 0; j < KSEL; ++j) {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float l0 = bf16lo(lo[j][q]), l1 = bf16hi(lo[j][q]);
-                const float h0 = bf16lo(hi[j][q]), h1 = bf16hi(hi[j][q]);
-                const float c0 = c[2 * q], s0 = s[2 * q], c1 = c[2 * q + 1], s1 = s[2 * q + 1];
+              for (int q = 0; q < kMine; ++q) {
+                const float l0 = bf16lo(lo[q][e]), l1 = bf16hi(lo[q][e]);
+                const float h0 = bf16lo(hi[q][e]), h1 = bf16hi(hi[q][e]);
                 // R(-p): (lo, hi) -> (lo c + hi s, hi c - lo s)
-                lo[j][q] = pack_bf16(fmaf(l0, c0, h0 * s0), fmaf(l1, c1, h1 * s1));
-                hi[j][q] = pack_bf16(fmaf(h0, c0, -(l0 * s0)), fmaf(h1, c1, -(l1 * s1)));
+                lo[q][e] = pack_bf16(fmaf(l0, v.x, h0 * v.y), fmaf(l1, v.z, h1 * v.w));
+                hi[q][e] = pack_bf16(fmaf(h0, v.x, -(l0 * v.y)), fmaf(h1, v.z, -(l1 * v.w)));
               }
             }
           }
-        } else {
-#pragma unroll
-          for (int j = 0; j < KSEL; ++j) {
-            lo[j] = u32x4{0, 0, 0, 0};
-            hi[j] = u32x4{0, 0, 0, 0};
-          }
         }
 #pragma unroll
-        for (int j = 0; j < KSEL; ++j) {
-          *(u32x4*)&xs[buf][lds_off<KSEL>(pt, 16 * j + pc)] = lo[j];
-          *(u32x4*)&xs[buf][lds_off<KSEL>(pt, 16 * j + 8 + pc)] = hi[j];
+        for (int q = 0; q < kMine; ++q) {
+          const int j = pj + 2 * q;
+          if (j < KSEL) {
+            *(u32x4*)&xs[buf][lds_off<KSEL>(pt, 16 * j + pc)] = lo[q];
+            *(u32x4*)&xs[buf][lds_off<KSEL>(pt, 16 * j + 8 + pc)] = hi[q];
+          }
         }
       }
       __syncthreads();
 
       // -- Y^T = W^T X^T for this wave's 32 columns x 32 tokens
-      f32x4 acc[2][2];
+      f32x4 acc[2][kTB];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tb = 0; tb < kTB; ++tb) acc[b][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
+        for (int tb = 0; tb < kTB; ++tb) {
           const int t = 16 * tb + lrow;
           const bf16x8 xf = *(const bf16x8*)&xs[buf][lds_off<KSEL>(t, 4 * s + lgrp)];
           acc[0][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[0][s], xf, acc[0][tb], 0, 0, 0);
@@ -211,7 +241,7 @@ transfer_mfma_kernel(XferArgs a, int32_t n_groups, int64_t chunk_tokens, int64_t
 
       // -- epilogue: bias, forward rotation (keys), store
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
+      for (int tb = 0; tb < kTB; ++tb) {
         const int64_t n = t0 + 16 * tb + lrow;
         if (n >= t_end) continue;
         const int64_t row = a.dst_row ? (int64_t)a.dst_row[n] : n;
@@ -264,7 +294,10 @@ int cu_count() {
 }  // namespace
 
 bool mfma_supports(const XferArgs& a) {
-  return a.D == kD && a.k >= 1 && a.k <= 4;
+  // 16-byte vector loads of source rows and W, 8-byte stores of outputs
+  auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
+  return a.D == kD && a.k >= 1 && a.k <= 4 && al(a.src_k, 16) && al(a.src_v, 16) && al(a.W_k, 16) &&
+         al(a.W_v, 16) && al(a.out_k, 8) && al(a.out_v, 8) && al(a.rope_src, 16) && al(a.rope_tgt, 16);
 }
 
 hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream) {

