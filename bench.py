@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_14b_32b_t32k")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB three times (the reference "
+                         "kernel that scales HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the transfer shards by KV head with no exchange, "
@@ -128,6 +131,17 @@ def main():
     torch.cuda.set_device(dev)
     if hk.helm_device_check(0) != 0:
         raise SystemExit(f"device check failed: {hk.helm_last_error()}")
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration_mib} MiB three times (reads {n} B, writes {n} B per copy)")
+        return
 
     w = synth.CONFIGS[args.workload]
     assert not w.paged, "bench.py times the contiguous workloads"

@@ -327,6 +327,7 @@ int helm_kv_transfer(const void* src_k, const void* src_v, const int32_t* src_po
   a.L_s = s->n_src_layers; a.L_t = s->n_tgt_layers; a.H = s->n_kv_heads; a.D = s->head_dim; a.k = s->k;
   a.src_tok = s->head_dim; a.src_head = s->n_tokens * s->head_dim; a.src_layer = a.src_head * s->n_kv_heads;
   a.dst_tok = a.src_tok; a.dst_head = a.src_head; a.dst_layer = a.src_layer;
+  a.src_rows = a.dst_rows = s->n_tokens;
   return run_transfer(a, s->dtype, src_pos, tgt_pos, s->rope_theta_src, s->rope_theta_tgt,
                       (hipStream_t)s->stream);
 }
@@ -409,6 +410,8 @@ int helm_kv_transfer_paged(const void* src_k_pool, const void* src_v_pool, const
   a.src_layer = (int64_t)s->n_src_blocks * s->block_size * a.src_tok;
   a.dst_tok = a.src_tok; a.dst_head = a.src_head;
   a.dst_layer = (int64_t)s->n_tgt_blocks * s->block_size * a.dst_tok;
+  a.src_rows = (int64_t)s->n_src_blocks * s->block_size;
+  a.dst_rows = (int64_t)s->n_tgt_blocks * s->block_size;
 
   const hipStream_t stream = (hipStream_t)s->stream;
   rc = launch_status(helm::launch_paged_rows(cu, s->n_requests, src_bt, s->max_blocks_src, s->n_src_blocks,

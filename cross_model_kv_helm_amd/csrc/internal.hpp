@@ -28,6 +28,7 @@ struct XferArgs {
   const int32_t* src_row;     // [n_tok] or nullptr (identity)
   const int32_t* dst_row;     // [n_tok] or nullptr (identity)
   int64_t n_tok;
+  int64_t src_rows, dst_rows;   // rows addressable per (layer, head): T, or pool slots
   int32_t L_s, L_t, H, D, k;
   int64_t src_layer, src_head, src_tok;   // element strides
   int64_t dst_layer, dst_head, dst_tok;

@@ -15,39 +15,59 @@
 //             always applied — and a nearest-even store to bf16.
 //
 // Design for MI355X:
-//   * W stays in registers.  A workgroup (4 waves, one per SIMD) owns one
-//     group at a time; wave w holds W[:, cols] for its 32 output columns
-//     {16w..16w+15} and {64+16w..64+16w+15} — RoPE partners n and n+64 land
-//     in the same lane, so the epilogue rotation needs no data exchange.
-//     For k = 4 that is 128 VGPRs per lane; two workgroups share a CU.
-//   * Persistent sweep over tokens.  Work items are (token chunk, group); a
-//     workgroup maps all tokens of its item in 32-token tiles, so W is read
-//     from HBM once per item, not once per tile.
+//   * Matrix instruction v_mfma_f32_32x32x16_bf16: it sustains its full rate
+//     from a single accumulator chain.  Each wave owns one 32-row block of
+//     Y^T: rows 0..15 are output columns 16q..16q+15 and rows 16..31 are
+//     columns 64+16q..64+16q+15 (q = wave within its group).  In the 32x32
+//     accumulator layout rows r and r+16 live in the same lane, so the RoPE
+//     partners n and n+64 meet in one lane and the rotation needs no
+//     exchange.  W stays in registers (128 VGPRs per wave for k = 4).
+//   * Ping-pong.  One workgroup of 8 waves per CU holds two groups: A (waves
+//     0-3) and B (waves 4-7); waves w and w+4 share a SIMD.  In every phase
+//     one group runs its matrix products and epilogue for a 32-token tile
+//     while the other group un-rotates the next tile into LDS, then they swap
+//     at a barrier.  So on each SIMD the matrix pipe of one wave overlaps the
+//     vector ALU work of the other.
+//   * Register prefetch.  Right after its matrix products a wave issues the
+//     global loads of the source rows of its next un-rotation; they land
+//     during its epilogue and the other group's phase.
+//   * Persistent sweep over tokens.  Work items are (token chunk, pair of
+//     target layers, head, K|V); a workgroup maps all tokens of its item, so W
+//     is read from HBM once per item.
 //   * XCD-aware order.  Workgroups are dispatched round-robin over the 8
 //     XCDs (id mod 8); with the head as the fastest-varying coordinate of the
-//     group index and 8 heads, every workgroup of an XCD works on the same
-//     head.  All target layers of that head sweep the same tokens at about
-//     the same time, so each source row is fetched from HBM once and then
-//     served from that XCD's L2 to the ~6 target layers that select it.
-//   * 16-token activation tiles through LDS, double-buffered, one barrier
-//     per tile.
-//     Rows are padded by 16 bytes so the 16 lanes of a B-operand read hit
-//     distinct banks.
+//     item index and 8 heads, every workgroup of an XCD works on the same
+//     head.  All 64 target layers of that head sweep the same tokens at about
+//     the same time, so a source row is fetched from HBM once and then served
+//     from that XCD's L2 to the ~6 target layers that select it.
+//   * Stores: lanes exchange half-rows (shfl across the two 32-lane halves)
+//     so each lane writes 8 consecutive bf16 (16 bytes) of one token row.
+//   * Buffer descriptors.  Source rows, cos/sin tables and output rows are
+//     addressed through 128-bit buffer descriptors whose bases are uniform
+//     (per layer and head) and live in scalar registers; a lane carries one
+//     32-bit byte offset.  The descriptors' record counts also make the
+//     hardware drop any access outside the tensor.
 #include "internal.hpp"
 
 namespace helm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kD = 128;          // head dimension
 constexpr int kHalf = 64;
-constexpr int kThreads = 256;    // 4 waves
-constexpr int kTile = 16;        // tokens per tile (one MFMA token block)
-constexpr int kTB = kTile / 16;  // MFMA token blocks per tile
-constexpr int kStageRow = kD + 8; // W^T staging row: 128 inputs of one output column, padded
+constexpr int kThreads = 512;    // 8 waves: groups A (0-3) and B (4-7)
+constexpr int kGroupThreads = 256;
+constexpr int kTile = 32;        // tokens per tile = MFMA B-block width
+constexpr int kStageRows = 64;   // W rows staged per pass
+constexpr int kStageRow = kStageRows + 8;  // W^T staging row (padded)
+constexpr int kCtRow = kHalf + 2;          // staged target (cos, sin) row: 64 float2 + pad
+constexpr int kRowBytes = kD * 2;          // one bf16 head row
+constexpr int kCsRowBytes = kHalf * 8;     // one token's 64 (cos, sin) pairs
 
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -60,219 +80,295 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Raw buffer over [base, base + bytes); accesses beyond it read 0 / are dropped.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int KSEL>
 struct Cfg {
   static constexpr int KD = KSEL * kD;          // GEMM depth
-  static constexpr int KSTEPS = KD / 32;        // 16x16x32 MFMA steps
+  static constexpr int KSTEPS = KD / 16;        // 32x32x16 MFMA steps
   static constexpr int ROW = KD + 8;            // LDS row: one token, padded by 16 bytes
   static constexpr int TILE_ELEMS = kTile * ROW;
+  // a group's LDS buffer holds its activation tile, and before that the W^T
+  // staging block (kD rows of kStageRow)
+  static constexpr int BUF_ELEMS = TILE_ELEMS > kD * kStageRow ? TILE_ELEMS : kD * kStageRow;
 };
 
-// LDS element offset of chunk `c` (8 bf16) of token row `t`.  The 16-byte
-// pad per row puts the 16 rows a B-operand read touches on distinct banks,
-// and keeps offsets additive so every k-step uses an immediate offset.
 template <int KSEL>
 __device__ __forceinline__ int lds_off(int t, int c) {
   return t * Cfg<KSEL>::ROW + (c << 3);
 }
 
+// What one thread prefetches for its share of a tile's un-rotation: 16-byte
+// chunks pc (low half) and pc+8 (high half) of token pt for each selected
+// layer.
 template <int KSEL>
-__global__ void __launch_bounds__(kThreads, 2)
-transfer_mfma_kernel(XferArgs a, int32_t n_groups, int64_t chunk_tokens, int64_t n_items) {
+struct Raw {
+  u32x4 lo[KSEL], hi[KSEL];
+  int32_t n;
+  bool have;
+};
+
+template <int KSEL>
+__global__ void __launch_bounds__(kThreads, 1)
+transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t n_items) {
   using C = Cfg<KSEL>;
-  // One LDS buffer serves two purposes: the W^T staging block while a group's
-  // weights are loaded, then the two activation tiles.
-  constexpr int kLdsElems = 2 * C::TILE_ELEMS > kD * kStageRow ? 2 * C::TILE_ELEMS : kD * kStageRow;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[kLdsElems];
-  __bf16 (*xs)[C::TILE_ELEMS] = reinterpret_cast<__bf16 (*)[C::TILE_ELEMS]>(lds);
+  __shared__ __attribute__((aligned(16))) __bf16 xs[2][C::BUF_ELEMS];    // one buffer per group
+  __shared__ __attribute__((aligned(16))) float bias_s[2][kD];
+  __shared__ __attribute__((aligned(16))) float2 ct_s[2][kTile * kCtRow];   // target (cos, sin), by tile parity
 
   const int tid = threadIdx.x;
+  // group (0 = A, 1 = B) and wave within the group are wave-uniform
+  const int gi = __builtin_amdgcn_readfirstlane(tid >> 8);
+  const int wq = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
+  const int gtid = tid & 255;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int lrow = lane & 15;      // MFMA row/col within a 16-block
-  const int lgrp = lane >> 4;      // MFMA k-group (0..3)
+  const int lr = lane & 31;                // MFMA A row / B column of this lane
+  const int lk = lane >> 5;                // MFMA k-half of this lane
+  const int wcol = 16 * wq;
+  const int my_col = lr < 16 ? wcol + lr : kHalf + wcol + (lr - 16);
+  const int pt = gtid >> 3;                // un-rotation share: token of the tile
+  const int pc = gtid & 7;                 //   and 16-byte chunk of the low half
+  __bf16* xg = xs[gi];
+  const int LP = (a.L_t + 1) / 2;
+  const int32_t n_tok = (int32_t)a.n_tok;
+  const rsrc_t cs_src = make_rsrc(a.rope_src, (uint32_t)n_tok * kCsRowBytes);
+  const rsrc_t cs_tgt = make_rsrc(a.rope_tgt, (uint32_t)n_tok * kCsRowBytes);
+  const uint32_t src_tok_b = (uint32_t)a.src_tok * 2, dst_tok_b = (uint32_t)a.dst_tok * 2;
+  const uint32_t src_bytes = (uint32_t)((a.src_rows - 1) * a.src_tok * 2 + kRowBytes);
+  const uint32_t dst_bytes = (uint32_t)((a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes);
 
-  int buf = 0;
-  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int32_t g = (int32_t)(item % n_groups);
-    const int64_t chunk = item / n_groups;
-    const int32_t h = g % a.H;
-    const int32_t rest = g / a.H;
-    const int32_t l = rest % a.L_t;
-    const bool keys = rest < a.L_t;    // groups [0, L_t*H) are keys, the rest values
-    const int64_t t_begin = chunk * chunk_tokens;
-    int64_t t_end = t_begin + chunk_tokens;
-    if (t_end > a.n_tok) t_end = a.n_tok;
+  for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int32_t pr = item % n_pairs;
+    const int32_t chunk = item / n_pairs;
+    const int32_t h = pr % a.H;
+    const int32_t rest = pr / a.H;
+    const bool keys = rest < LP;           // pairs [0, LP*H) are keys, the rest values
+    const int32_t l = 2 * (rest % LP) + gi;
+    const int32_t t_begin = chunk * chunk_tokens;
+    const int32_t t_end = min(t_begin + chunk_tokens, n_tok);
+    const int nt = (t_end - t_begin + kTile - 1) / kTile;
 
-    // selected source layers; an out-of-range entry skips the whole group
-    int32_t sel[KSEL];
-    bool valid = true;
+    // this group's selected source layers; a missing target layer (odd L_t)
+    // or an out-of-range entry makes the group idle (it still meets barriers)
+    bool active = l < a.L_t;
+    rsrc_t srs[KSEL];
 #pragma unroll
     for (int j = 0; j < KSEL; ++j) {
-      sel[j] = a.layer_sel[(int64_t)l * KSEL + j];
-      valid = valid && sel[j] >= 0 && sel[j] < a.L_s;
+      const int32_t sj = active ? a.layer_sel[l * KSEL + j] : 0;
+      active = active && sj >= 0 && sj < a.L_s;
+      const uint16_t* base = (const uint16_t*)(keys ? a.src_k : a.src_v) +
+                             (active ? (int64_t)sj * a.src_layer + (int64_t)h * a.src_head : 0);
+      srs[j] = make_rsrc(base, src_bytes);
     }
-    if (!valid) continue;   // uniform across the workgroup
-
-    const int32_t grp = l * a.H + h;
+    const int32_t grp = (active ? l : 0) * a.H + h;
     const uint16_t* W = (const uint16_t*)(keys ? a.W_k : a.W_v) + (int64_t)grp * C::KD * kD;
     const float* bias = (keys ? a.b_k : a.b_v) + (int64_t)grp * kD;
-    const uint16_t* src = (const uint16_t*)(keys ? a.src_k : a.src_v);
-    uint16_t* out = (uint16_t*)(keys ? a.out_k : a.out_v);
+    const rsrc_t dst = make_rsrc((const uint16_t*)(keys ? a.out_k : a.out_v) +
+                                     (active ? (int64_t)l * a.dst_layer + (int64_t)h * a.dst_head : 0),
+                                 dst_bytes);
 
-    // ---- W^T fragments for this wave's two 16-column blocks, in registers.
-    // lane holds W[m = 32s + 8*lgrp + i][n = ncol + lrow], i < 8.  W is
-    // staged through LDS one 128-row block at a time, transposed on the way
-    // in (coalesced 16-byte global loads, 2-byte LDS stores), so that each
+    // ---- W^T fragments of this wave's 32 columns, in registers: lane holds
+    // W[m = 16s + 8*lk + i][my_col], i < 8.  W is staged through this
+    // group's LDS tile 64 rows at a time, transposed on the way in
+    // (coalesced 16-byte global loads, 2-byte LDS stores), so that each
     // fragment is one 16-byte LDS read.
-    const int ncol0 = 16 * wave, ncol1 = kHalf + 16 * wave;
-    bf16x8 wf[2][C::KSTEPS];
-    {
-      __bf16* stage = lds;                            // W^T block [kD][kStageRow]
+    bf16x8 wf[C::KSTEPS];
 #pragma unroll
-      for (int part = 0; part < KSEL; ++part) {
-        __syncthreads();                              // earlier readers of the buffer are done
-        const u32x4* gsrc = (const u32x4*)(W + (int64_t)part * kD * kD);
+    for (int part = 0; part < C::KD / kStageRows; ++part) {
+      __syncthreads();                               // earlier readers of xs are done
+      if (active) {
+        const u32x4* gsrc = (const u32x4*)(W + (int64_t)part * kStageRows * kD);
 #pragma unroll 2
-        for (int e = tid; e < kD * kD / 8; e += kThreads) {
+        for (int e = gtid; e < kStageRows * kD / 8; e += kGroupThreads) {
           const u32x4 v = gsrc[e];
           const int m = e >> 4, n0 = (e & 15) << 3;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            stage[(n0 + 2 * q) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] & 0xffffu));
-            stage[(n0 + 2 * q + 1) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] >> 16));
-          }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int s = 4 * part + s4, m = 32 * s4 + 8 * lgrp;
-          wf[0][s] = *(const bf16x8*)&stage[(ncol0 + lrow) * kStageRow + m];
-          wf[1][s] = *(const bf16x8*)&stage[(ncol1 + lrow) * kStageRow + m];
-        }
-      }
-      __syncthreads();                                // the buffer is reused by the first tile
-    }
-    // bias for the 4 columns this lane's accumulators hold in each block
-    float b0[4], b1[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      b0[j] = bias[ncol0 + 4 * lgrp + j];
-      b1[j] = bias[ncol1 + 4 * lgrp + j];
-    }
-
-    // ---- prologue assignment: thread -> (token pt, 16-byte chunk pc of the low
-    // half, layer parity pj): it loads dims 8pc.. and 64+8pc.. of layers pj, pj+2, ..
-    const int pt = tid >> 4;        // 0..15
-    const int pj = (tid >> 3) & 1;
-    const int pc = tid & 7;
-    constexpr int kMine = (KSEL + 1) / 2;   // layers per thread (upper bound)
-
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += kTile) {
-      // -- gather (+ un-rotate) one tile into xs[buf]
-      {
-        const int64_t n = t0 + pt;
-        u32x4 lo[kMine], hi[kMine];
-        bool have = n < t_end;
-        int64_t row = 0;
-        if (have) {
-          row = a.src_row ? (int64_t)a.src_row[n] : n;
-          have = row >= 0;
-        }
-#pragma unroll
-        for (int q = 0; q < kMine; ++q) {
-          lo[q] = u32x4{0, 0, 0, 0};
-          hi[q] = u32x4{0, 0, 0, 0};
-        }
-        if (have) {
-#pragma unroll
-          for (int q = 0; q < kMine; ++q) {
-            const int j = pj + 2 * q;
-            if (j < KSEL) {
-              const uint16_t* p = src + (int64_t)sel[j] * a.src_layer + (int64_t)h * a.src_head +
-                                  row * a.src_tok + 8 * pc;
-              lo[q] = *(const u32x4*)p;
-              hi[q] = *(const u32x4*)(p + kHalf);
-            }
-          }
-          if (keys) {
-            const float4* cs4 = (const float4*)(a.rope_src + n * kHalf + 8 * pc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float4 v = cs4[e];   // (cos, sin) of dims 8pc+2e and 8pc+2e+1
-#pragma unroll
-              for (int q = 0; q < kMine; ++q) {
-                const float l0 = bf16lo(lo[q][e]), l1 = bf16hi(lo[q][e]);
-                const float h0 = bf16lo(hi[q][e]), h1 = bf16hi(hi[q][e]);
-                // R(-p): (lo, hi) -> (lo c + hi s, hi c - lo s)
-                lo[q][e] = pack_bf16(fmaf(l0, v.x, h0 * v.y), fmaf(l1, v.z, h1 * v.w));
-                hi[q][e] = pack_bf16(fmaf(h0, v.x, -(l0 * v.y)), fmaf(h1, v.z, -(l1 * v.w)));
-              }
-            }
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < kMine; ++q) {
-          const int j = pj + 2 * q;
-          if (j < KSEL) {
-            *(u32x4*)&xs[buf][lds_off<KSEL>(pt, 16 * j + pc)] = lo[q];
-            *(u32x4*)&xs[buf][lds_off<KSEL>(pt, 16 * j + 8 + pc)] = hi[q];
+            xg[(n0 + 2 * q) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] & 0xffffu));
+            xg[(n0 + 2 * q + 1) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] >> 16));
           }
         }
       }
       __syncthreads();
+      if (active) {
+#pragma unroll
+        for (int s4 = 0; s4 < kStageRows / 16; ++s4)
+          wf[(kStageRows / 16) * part + s4] = *(const bf16x8*)&xg[my_col * kStageRow + 16 * s4 + 8 * lk];
+      }
+    }
+    if (active && gtid < kD / 4) ((float4*)bias_s[gi])[gtid] = ((const float4*)bias)[gtid];
+    __syncthreads();                                 // xs is reused for tiles; bias is visible
 
-      // -- Y^T = W^T X^T for this wave's 32 columns x 32 tokens
-      f32x4 acc[2][kTB];
+    // ---- per-thread pieces of the tile pipeline
+    auto load_raw = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
+      const int32_t n = t_begin + tile * kTile + pt;
+      r.n = n;
+      r.have = active && tile < nt && n < t_end;
+      int32_t row = n;
+      if (r.have && a.src_row) {
+        row = a.src_row[n];
+        r.have = row >= 0;
+      }
+      if (r.have) {
+        const uint32_t off = (uint32_t)row * src_tok_b + 16 * pc;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int j = 0; j < KSEL; ++j) {
+          r.lo[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off, 0, 0);
+          r.hi[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off + kHalf * 2, 0, 0);
+        }
+      }
+    };
+    auto store_tile = [&](Raw<KSEL>& r) __attribute__((always_inline)) {   // un-rotate (keys), write to LDS
+      if (!active) return;
+      if (!r.have) {
 #pragma unroll
-        for (int tb = 0; tb < kTB; ++tb) acc[b][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < KSEL; ++j) {
+          r.lo[j] = u32x4{0, 0, 0, 0};
+          r.hi[j] = u32x4{0, 0, 0, 0};
+        }
+      } else if (keys) {
+        const uint32_t coff = (uint32_t)r.n * kCsRowBytes + 64 * pc;
+        f32x4 cs[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          cs[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cs_src, coff + 16 * e, 0, 0));
+        // one layer at a time, so only one layer's values are unpacked to fp32
+#pragma unroll
+        for (int j = 0; j < KSEL; ++j) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x4 v = cs[e];    // (cos, sin) of dims 8pc+2e and 8pc+2e+1
+            const float l0 = bf16lo(r.lo[j][e]), l1 = bf16hi(r.lo[j][e]);
+            const float h0 = bf16lo(r.hi[j][e]), h1 = bf16hi(r.hi[j][e]);
+            // R(-p): (lo, hi) -> (lo c + hi s, hi c - lo s)
+            r.lo[j][e] = pack_bf16(fmaf(l0, v.x, h0 * v.y), fmaf(l1, v.z, h1 * v.w));
+            r.hi[j][e] = pack_bf16(fmaf(h0, v.x, -(l0 * v.y)), fmaf(h1, v.z, -(l1 * v.w)));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < KSEL; ++j) {
+        *(u32x4*)&xg[lds_off<KSEL>(pt, 16 * j + pc)] = r.lo[j];
+        *(u32x4*)&xg[lds_off<KSEL>(pt, 16 * j + 8 + pc)] = r.hi[j];
+      }
+    };
+    // Group A stages the target-side (cos, sin) of a tile for both groups'
+    // epilogues: thread -> token pt, frequencies 8pc..8pc+7.
+    auto stage_ct = [&](int tile) __attribute__((always_inline)) {
+      const int32_t n = t_begin + tile * kTile + pt;
+      if (keys && tile < nt && n < t_end) {
+        const uint32_t coff = (uint32_t)n * kCsRowBytes + 64 * pc;
+        f32x4* d = (f32x4*)&ct_s[tile & 1][pt * kCtRow + 8 * pc];
+        u32x4 v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_raw_buffer_load_b128(cs_tgt, coff + 16 * e, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = __builtin_bit_cast(f32x4, v[e]);
+      }
+    };
+    auto compute_tile = [&](int tile, Raw<KSEL>& next) __attribute__((always_inline)) {
+      if (!active) return;
+      const int32_t n = t_begin + tile * kTile + lr;
+      const bool live = n < t_end;
+      // Y^T[32 columns x 32 tokens] = W^T X^T for this wave
+      // B fragments stream from LDS with kAhead reads in flight, so the
+      // matrix pipe never waits on LDS latency
+      constexpr int kAhead = 4;
+      f32x16 acc = {};
+      bf16x8 xf[kAhead];
+#pragma unroll
+      for (int s = 0; s < kAhead; ++s) xf[s] = *(const bf16x8*)&xg[lds_off<KSEL>(lr, 2 * s + lk)];
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
-#pragma unroll
-        for (int tb = 0; tb < kTB; ++tb) {
-          const int t = 16 * tb + lrow;
-          const bf16x8 xf = *(const bf16x8*)&xs[buf][lds_off<KSEL>(t, 4 * s + lgrp)];
-          acc[0][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[0][s], xf, acc[0][tb], 0, 0, 0);
-          acc[1][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[1][s], xf, acc[1][tb], 0, 0, 0);
-        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], xf[s % kAhead], acc, 0, 0, 0);
+        if (s + kAhead < C::KSTEPS) xf[s % kAhead] = *(const bf16x8*)&xg[lds_off<KSEL>(lr, 2 * (s + kAhead) + lk)];
       }
-
-      // -- epilogue: bias, forward rotation (keys), store
+      // issue order: kAhead reads, then (matrix product, read) pairs, then the tail
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) {
-        const int64_t n = t0 + 16 * tb + lrow;
-        if (n >= t_end) continue;
-        const int64_t row = a.dst_row ? (int64_t)a.dst_row[n] : n;
-        if (row < 0) continue;
-        float o0[4], o1[4];
+      for (int s = 0; s < C::KSTEPS - kAhead; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+      // prefetch the source rows of this group's next un-rotation; they
+      // land during the epilogue and the other group's phase
+      __builtin_amdgcn_sched_barrier(0);
+      load_raw(tile + 1, next);
+      // epilogue.  Accumulator j < 8 is column wcol + 8*(j/4) + 4*lk + j%4
+      // of token n; j + 8 is its partner 64 columns up.
+      uint2 plo[2], phi[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int c0 = wcol + 8 * g + 4 * lk;
+        const float4 bl = *(const float4*)&bias_s[gi][c0];
+        const float4 bh = *(const float4*)&bias_s[gi][c0 + kHalf];
+        float y0[4] = {acc[4 * g] + bl.x, acc[4 * g + 1] + bl.y, acc[4 * g + 2] + bl.z, acc[4 * g + 3] + bl.w};
+        float y1[4] = {acc[8 + 4 * g] + bh.x, acc[9 + 4 * g] + bh.y, acc[10 + 4 * g] + bh.z,
+                       acc[11 + 4 * g] + bh.w};
         if (keys) {
-          const float4* cs4 = (const float4*)(a.rope_tgt + n * kHalf + ncol0 + 4 * lgrp);
-          const float4 v0 = cs4[0], v1 = cs4[1];
-          const float c[4] = {v0.x, v0.z, v1.x, v1.z}, s[4] = {v0.y, v0.w, v1.y, v1.w};
+          const float4* cp = (const float4*)&ct_s[tile & 1][lr * kCtRow + c0];
+          const float4 v0 = cp[0], v1 = cp[1];
+          const float cc[4] = {v0.x, v0.z, v1.x, v1.z};
+          const float ss[4] = {v0.y, v0.w, v1.y, v1.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float y0 = acc[0][tb][j] + b0[j], y1 = acc[1][tb][j] + b1[j];
             // R(+p'): (lo, hi) -> (lo c - hi s, hi c + lo s)
-            o0[j] = fmaf(y0, c[j], -(y1 * s[j]));
-            o1[j] = fmaf(y1, c[j], y0 * s[j]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            o0[j] = acc[0][tb][j] + b0[j];
-            o1[j] = acc[1][tb][j] + b1[j];
+            const float o0 = fmaf(y0[j], cc[j], -(y1[j] * ss[j]));
+            const float o1 = fmaf(y1[j], cc[j], y0[j] * ss[j]);
+            y0[j] = o0;
+            y1[j] = o1;
           }
         }
-        uint16_t* q = out + (int64_t)l * a.dst_layer + (int64_t)h * a.dst_head + row * a.dst_tok;
-        uint2 w0, w1;
-        w0.x = pack_bf16(o0[0], o0[1]); w0.y = pack_bf16(o0[2], o0[3]);
-        w1.x = pack_bf16(o1[0], o1[1]); w1.y = pack_bf16(o1[2], o1[3]);
-        *(uint2*)(q + ncol0 + 4 * lgrp) = w0;
-        *(uint2*)(q + ncol1 + 4 * lgrp) = w1;
+        plo[g].x = pack_bf16(y0[0], y0[1]); plo[g].y = pack_bf16(y0[2], y0[3]);
+        phi[g].x = pack_bf16(y1[0], y1[1]); phi[g].y = pack_bf16(y1[2], y1[3]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      buf ^= 1;
+      // lane lk = 0 gathers columns wcol+0..7, lane lk = 1 columns wcol+8..15
+      const uint2 slo = lk ? plo[0] : plo[1], shi = lk ? phi[0] : phi[1];
+      uint2 rlo, rhi;
+      rlo.x = __shfl_xor(slo.x, 32); rlo.y = __shfl_xor(slo.y, 32);
+      rhi.x = __shfl_xor(shi.x, 32); rhi.y = __shfl_xor(shi.y, 32);
+      if (live) {
+        const int32_t row = a.dst_row ? a.dst_row[n] : n;
+        if (row >= 0) {
+          const uint32_t off = (uint32_t)row * dst_tok_b + 2 * (wcol + 8 * lk);
+          const u32x4 wlo = lk ? u32x4{rlo.x, rlo.y, plo[1].x, plo[1].y} : u32x4{plo[0].x, plo[0].y, rlo.x, rlo.y};
+          const u32x4 whi = lk ? u32x4{rhi.x, rhi.y, phi[1].x, phi[1].y} : u32x4{phi[0].x, phi[0].y, rhi.x, rhi.y};
+          __builtin_amdgcn_raw_buffer_store_b128(wlo, dst, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(whi, dst, off + kHalf * 2, 0, 0);
+        }
+      }
+    };
+
+    // ---- ping-pong over tiles.  Phase 2i: A computes tile i, B un-rotates
+    // tile i.  Phase 2i+1: B computes tile i, A un-rotates tile i+1.  Group
+    // A also stages tile i's target (cos, sin) while it prepares tile i; both
+    // groups read it in their epilogues of tile i.  A group's compute phase
+    // prefetches the source rows its next preparation needs.
+    Raw<KSEL> raw;
+    load_raw(0, raw);
+    if (gi == 0) {
+      stage_ct(0);
+      store_tile(raw);
+    }
+    __syncthreads();
+    for (int i = 0; i < nt; ++i) {
+      if (gi == 0) compute_tile(i, raw);
+      else store_tile(raw);
+      __syncthreads();
+      if (gi == 1) {
+        compute_tile(i, raw);
+      } else if (i + 1 < nt) {
+        stage_ct(i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        store_tile(raw);
+      }
+      __syncthreads();
     }
   }
 }
@@ -294,31 +390,38 @@ int cu_count() {
 }  // namespace
 
 bool mfma_supports(const XferArgs& a) {
-  // 16-byte vector loads of source rows and W, 8-byte stores of outputs
+  // 16-byte vector loads of source rows, W and bias, 16-byte stores of
+  // outputs, and every buffer descriptor's byte range below 4 GiB
   auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
-  return a.D == kD && a.k >= 1 && a.k <= 4 && al(a.src_k, 16) && al(a.src_v, 16) && al(a.W_k, 16) &&
-         al(a.W_v, 16) && al(a.out_k, 8) && al(a.out_v, 8) && al(a.rope_src, 16) && al(a.rope_tgt, 16);
+  const int64_t lim = 0xffffffffLL;
+  const bool ranges = a.n_tok * kCsRowBytes <= lim && (a.src_rows - 1) * a.src_tok * 2 + kRowBytes <= lim &&
+                      (a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes <= lim && a.n_tok < 0x7fffffffLL;
+  return ranges && a.D == kD && a.k >= 1 && a.k <= 4 && al(a.src_k, 16) && al(a.src_v, 16) && al(a.W_k, 16) &&
+         al(a.W_v, 16) && al(a.out_k, 16) && al(a.out_v, 16) && al(a.rope_src, 16) && al(a.rope_tgt, 16) &&
+         al(a.b_k, 16) && al(a.b_v, 16);
 }
 
 hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream) {
   if (!mfma_supports(a)) return hipErrorNotSupported;
   if (a.n_tok <= 0) return hipSuccess;
-  const int64_t n_groups = (int64_t)a.L_t * a.H * 2;
-  const int64_t slots = 2LL * cu_count();   // two workgroups per CU
-  // Split tokens into chunks only when there are fewer groups than slots.
+  const int64_t n_pairs = (int64_t)((a.L_t + 1) / 2) * a.H * 2;
+  const int64_t slots = cu_count();   // one 8-wave workgroup per CU
+  // Split tokens into chunks only when there are fewer pairs than CUs.
   int64_t n_chunks = 1;
-  if (n_groups < slots) n_chunks = (slots + n_groups - 1) / n_groups;
+  if (n_pairs < slots) n_chunks = (slots + n_pairs - 1) / n_pairs;
   int64_t chunk_tokens = (a.n_tok + n_chunks - 1) / n_chunks;
   chunk_tokens = (chunk_tokens + kTile - 1) / kTile * kTile;
   n_chunks = (a.n_tok + chunk_tokens - 1) / chunk_tokens;
-  const int64_t n_items = n_groups * n_chunks;
+  const int64_t n_items = n_pairs * n_chunks;
+  if (n_items > 0x7fffffffLL) return hipErrorInvalidValue;
   const int64_t grid = n_items < slots ? n_items : slots;
   const dim3 g((unsigned)grid), b(kThreads);
+  const int32_t np = (int32_t)n_pairs, ct = (int32_t)chunk_tokens, ni = (int32_t)n_items;
   switch (a.k) {
-    case 1: hipLaunchKernelGGL(transfer_mfma_kernel<1>, g, b, 0, stream, a, (int32_t)n_groups, chunk_tokens, n_items); break;
-    case 2: hipLaunchKernelGGL(transfer_mfma_kernel<2>, g, b, 0, stream, a, (int32_t)n_groups, chunk_tokens, n_items); break;
-    case 3: hipLaunchKernelGGL(transfer_mfma_kernel<3>, g, b, 0, stream, a, (int32_t)n_groups, chunk_tokens, n_items); break;
-    default: hipLaunchKernelGGL(transfer_mfma_kernel<4>, g, b, 0, stream, a, (int32_t)n_groups, chunk_tokens, n_items); break;
+    case 1: hipLaunchKernelGGL(transfer_mfma_kernel<1>, g, b, 0, stream, a, np, ct, ni); break;
+    case 2: hipLaunchKernelGGL(transfer_mfma_kernel<2>, g, b, 0, stream, a, np, ct, ni); break;
+    case 3: hipLaunchKernelGGL(transfer_mfma_kernel<3>, g, b, 0, stream, a, np, ct, ni); break;
+    default: hipLaunchKernelGGL(transfer_mfma_kernel<4>, g, b, 0, stream, a, np, ct, ni); break;
   }
   return hipGetLastError();
 }
