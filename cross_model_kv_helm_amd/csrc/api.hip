@@ -83,14 +83,15 @@ Common common_of(const helm_paged_shape_t* s) {
 
 size_t elem_bytes(int32_t dtype) { return dtype == HELM_BF16 ? 2 : 4; }
 
-// Workspace: [rope_src: N*D/2 float2][rope_tgt: same]{[src_row: N int32][dst_row: N int32]}
+// Workspace: [rope_src: ceil(N/32)*32*D/2 float2][rope_tgt: same]{[src_row: N int32][dst_row: N int32]}
 struct Workspace {
   size_t rope_bytes = 0, rows_bytes = 0, total = 0;
 };
 
 bool workspace_layout(int64_t n_tok, int32_t D, bool paged, Workspace& w) {
-  int64_t rb = n_tok;
-  if (!mul_ok(rb, D / 2) || !mul_ok(rb, (int64_t)sizeof(float2))) return false;
+  if (n_tok > INT64_MAX / 2) return false;
+  int64_t rb = helm::rope_table_entries(n_tok, D / 2);
+  if (!mul_ok(rb, (int64_t)sizeof(float2))) return false;
   w.rope_bytes = align_up((size_t)rb);
   w.rows_bytes = paged ? align_up((size_t)n_tok * sizeof(int32_t)) : 0;
   w.total = 2 * w.rope_bytes + 2 * w.rows_bytes;

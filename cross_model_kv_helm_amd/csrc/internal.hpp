@@ -23,8 +23,8 @@ struct XferArgs {
   const float* b_v;
   void* out_k;
   void* out_v;
-  const float2* rope_src;     // [n_tok, D/2] (cos, sin) at src_pos, theta_src
-  const float2* rope_tgt;     // [n_tok, D/2] (cos, sin) at tgt_pos, theta_tgt
+  const float2* rope_src;     // (cos, sin) at src_pos, theta_src, in rope_index layout
+  const float2* rope_tgt;     // (cos, sin) at tgt_pos, theta_tgt, in rope_index layout
   const int32_t* src_row;     // [n_tok] or nullptr (identity)
   const int32_t* dst_row;     // [n_tok] or nullptr (identity)
   int64_t n_tok;
@@ -35,6 +35,23 @@ struct XferArgs {
 };
 
 enum class Dtype : int { BF16 = 0, F32 = 1 };
+
+// Layout of the (cos, sin) tables written by K1, blocked by 32-token tiles so
+// that a wave's 16-byte loads of a tile's table are contiguous: within the
+// block of tokens [32b, 32b+32), the pair of (token t, frequency i) lives at
+//   float2 index  b*32*half + e*(32*half/4) + (t%32)*(half/8)*2 + (i/8)*2 + (i%2)
+// with e = (i%8)/2, i.e. [e][t%32][i/8][2 pairs].  half = D/2 (a multiple of 8).
+constexpr int kRopeBlock = 32;
+__host__ __device__ inline int64_t rope_index(int64_t t, int32_t i, int32_t half) {
+  const int64_t b = t / kRopeBlock;
+  const int32_t tt = (int32_t)(t - b * kRopeBlock);
+  const int32_t e = (i & 7) >> 1;
+  return b * kRopeBlock * half + (int64_t)e * (kRopeBlock * half / 4) + (int64_t)tt * (half / 4) +
+         (i >> 3) * 2 + (i & 1);
+}
+inline int64_t rope_table_entries(int64_t n_tok, int32_t half) {
+  return (n_tok + kRopeBlock - 1) / kRopeBlock * kRopeBlock * half;
+}
 
 // K1: cos/sin tables of the RoPE angles for src_pos and tgt_pos.
 hipError_t launch_rope_tables(const int32_t* src_pos, const int32_t* tgt_pos, int64_t n_tok,

@@ -40,8 +40,11 @@
 //     head.  All 64 target layers of that head sweep the same tokens at about
 //     the same time, so a source row is fetched from HBM once and then served
 //     from that XCD's L2 to the ~6 target layers that select it.
-//   * Stores: lanes exchange half-rows (shfl across the two 32-lane halves)
-//     so each lane writes 8 consecutive bf16 (16 bytes) of one token row.
+//   * Stores through LDS: the epilogue writes its 32x32 block into the
+//     group's LDS output tile; in the group's next phase each wave stores
+//     whole 256-byte token rows (16 bytes per lane), so every store touches
+//     full cache lines.  The tile's (cos, sin) tables use a tile-blocked
+//     layout for the same reason: each 16-byte load of a wave is contiguous.
 //   * Buffer descriptors.  Source rows, cos/sin tables and output rows are
 //     addressed through 128-bit buffer descriptors whose bases are uniform
 //     (per layer and head) and live in scalar registers; a lane carries one
@@ -66,8 +69,9 @@ constexpr int kTile = 32;        // tokens per tile = MFMA B-block width
 constexpr int kStageRows = 64;   // W rows staged per pass
 constexpr int kStageRow = kStageRows + 8;  // W^T staging row (padded)
 constexpr int kCtRow = kHalf + 2;          // staged target (cos, sin) row: 64 float2 + pad
+constexpr int kOtRow = kD + 8;             // staged output row: 128 bf16 + pad
 constexpr int kRowBytes = kD * 2;          // one bf16 head row
-constexpr int kCsRowBytes = kHalf * 8;     // one token's 64 (cos, sin) pairs
+constexpr int kCsTileBytes = kTile * kHalf * 8;   // one tile's (cos, sin) block (rope_index layout)
 
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -78,6 +82,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   v[0] = (__bf16)a;   // round to nearest even
   v[1] = (__bf16)b;
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Workgroup barrier that orders LDS accesses only.  The barriers of this
+// kernel hand LDS tiles between waves; no wave reads another's global
+// stores, so outstanding global loads and stores may stay in flight across
+// it (a full __syncthreads() would wait for all of them every phase).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Raw buffer over [base, base + bytes); accesses beyond it read 0 / are dropped.
@@ -111,13 +125,29 @@ struct Raw {
   bool have;
 };
 
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+// Copies `bytes` (a multiple of 1024) from global memory into LDS with the
+// global->LDS DMA path: each instruction moves 1 KB (16 bytes per lane of
+// one wave), with no registers in between.  `wave_in_group` / `waves` split
+// the instructions among the waves of a group.
+__device__ __forceinline__ void dma_to_lds(const void* gsrc, void* ldst, int bytes, int wave_in_group, int waves,
+                                          int lane) {
+  for (int off = wave_in_group * 1024; off < bytes; off += waves * 1024)
+    __builtin_amdgcn_global_load_lds((const char*)gsrc + off + 16 * lane, (lds_void_t)((char*)ldst + off), 16, 0, 0);
+}
+
 template <int KSEL>
 __global__ void __launch_bounds__(kThreads, 1)
 transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t n_items) {
   using C = Cfg<KSEL>;
   __shared__ __attribute__((aligned(16))) __bf16 xs[2][C::BUF_ELEMS];    // one buffer per group
   __shared__ __attribute__((aligned(16))) float bias_s[2][kD];
-  __shared__ __attribute__((aligned(16))) float2 ct_s[2][kTile * kCtRow];   // target (cos, sin), by tile parity
+  __shared__ __attribute__((aligned(16))) __bf16 ot_s[2][kTile * kOtRow];    // one output tile per group
+  // (cos, sin) blocks of a tile in the tile-blocked table layout, by tile
+  // parity: source side for the un-rotation, target side for the epilogue
+  __shared__ __attribute__((aligned(16))) float2 cs_s[2][kTile * kHalf];
+  __shared__ __attribute__((aligned(16))) float2 ct_s[2][kTile * kHalf];
 
   const int tid = threadIdx.x;
   // group (0 = A, 1 = B) and wave within the group are wave-uniform
@@ -134,8 +164,6 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
   __bf16* xg = xs[gi];
   const int LP = (a.L_t + 1) / 2;
   const int32_t n_tok = (int32_t)a.n_tok;
-  const rsrc_t cs_src = make_rsrc(a.rope_src, (uint32_t)n_tok * kCsRowBytes);
-  const rsrc_t cs_tgt = make_rsrc(a.rope_tgt, (uint32_t)n_tok * kCsRowBytes);
   const uint32_t src_tok_b = (uint32_t)a.src_tok * 2, dst_tok_b = (uint32_t)a.dst_tok * 2;
   const uint32_t src_bytes = (uint32_t)((a.src_rows - 1) * a.src_tok * 2 + kRowBytes);
   const uint32_t dst_bytes = (uint32_t)((a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes);
@@ -147,9 +175,10 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
     const int32_t rest = pr / a.H;
     const bool keys = rest < LP;           // pairs [0, LP*H) are keys, the rest values
     const int32_t l = 2 * (rest % LP) + gi;
-    const int32_t t_begin = chunk * chunk_tokens;
+    const int32_t t_begin = chunk * chunk_tokens;   // a multiple of kTile
     const int32_t t_end = min(t_begin + chunk_tokens, n_tok);
     const int nt = (t_end - t_begin + kTile - 1) / kTile;
+    const int32_t blk0 = t_begin / kTile;  // table block of the item's first tile
 
     // this group's selected source layers; a missing target layer (odd L_t)
     // or an out-of-range entry makes the group idle (it still meets barriers)
@@ -178,7 +207,7 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
     bf16x8 wf[C::KSTEPS];
 #pragma unroll
     for (int part = 0; part < C::KD / kStageRows; ++part) {
-      __syncthreads();                               // earlier readers of xs are done
+      lds_barrier();                                 // earlier readers of xs are done
       if (active) {
         const u32x4* gsrc = (const u32x4*)(W + (int64_t)part * kStageRows * kD);
 #pragma unroll 2
@@ -192,7 +221,7 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       if (active) {
 #pragma unroll
         for (int s4 = 0; s4 < kStageRows / 16; ++s4)
@@ -200,7 +229,6 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
       }
     }
     if (active && gtid < kD / 4) ((float4*)bias_s[gi])[gtid] = ((const float4*)bias)[gtid];
-    __syncthreads();                                 // xs is reused for tiles; bias is visible
 
     // ---- per-thread pieces of the tile pipeline
     auto load_raw = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
@@ -221,7 +249,15 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         }
       }
     };
-    auto store_tile = [&](Raw<KSEL>& r) __attribute__((always_inline)) {   // un-rotate (keys), write to LDS
+    // Group A fetches a tile's two (cos, sin) blocks into LDS (keys only).
+    auto fetch_tables = [&](int tile, float2* cs_dst, float2* ct_dst) __attribute__((always_inline)) {
+      if (keys && tile < nt) {
+        const size_t boff = (size_t)(blk0 + tile) * (kTile * kHalf);
+        dma_to_lds(a.rope_src + boff, cs_dst, kCsTileBytes, wq, 4, lane);
+        dma_to_lds(a.rope_tgt + boff, ct_dst, kCsTileBytes, wq, 4, lane);
+      }
+    };
+    auto store_tile = [&](Raw<KSEL>& r, const float2* cs_tab) __attribute__((always_inline)) {
       if (!active) return;
       if (!r.have) {
 #pragma unroll
@@ -230,11 +266,11 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
           r.hi[j] = u32x4{0, 0, 0, 0};
         }
       } else if (keys) {
-        const uint32_t coff = (uint32_t)r.n * kCsRowBytes + 64 * pc;
+        // tile-blocked table: piece e of (token pt, chunk pc) at e*4KB + pt*128 + pc*16
         f32x4 cs[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          cs[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cs_src, coff + 16 * e, 0, 0));
+          cs[e] = *(const f32x4*)((const char*)cs_tab + e * (kCsTileBytes / 4) + 128 * pt + 16 * pc);
         // one layer at a time, so only one layer's values are unpacked to fp32
 #pragma unroll
         for (int j = 0; j < KSEL; ++j) {
@@ -256,27 +292,17 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         *(u32x4*)&xg[lds_off<KSEL>(pt, 16 * j + 8 + pc)] = r.hi[j];
       }
     };
-    // Group A stages the target-side (cos, sin) of a tile for both groups'
-    // epilogues: thread -> token pt, frequencies 8pc..8pc+7.
-    auto stage_ct = [&](int tile) __attribute__((always_inline)) {
-      const int32_t n = t_begin + tile * kTile + pt;
-      if (keys && tile < nt && n < t_end) {
-        const uint32_t coff = (uint32_t)n * kCsRowBytes + 64 * pc;
-        f32x4* d = (f32x4*)&ct_s[tile & 1][pt * kCtRow + 8 * pc];
-        u32x4 v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_raw_buffer_load_b128(cs_tgt, coff + 16 * e, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = __builtin_bit_cast(f32x4, v[e]);
-      }
-    };
+    // Y^T = W^T X^T, bias, forward rotation into the LDS output tile.  Group
+    // A also fetches the next tile's tables and waits for its copies before
+    // the phase ends.
     auto compute_tile = [&](int tile, Raw<KSEL>& next) __attribute__((always_inline)) {
       if (!active) return;
-      const int32_t n = t_begin + tile * kTile + lr;
-      const bool live = n < t_end;
-      // Y^T[32 columns x 32 tokens] = W^T X^T for this wave
-      // B fragments stream from LDS with kAhead reads in flight, so the
-      // matrix pipe never waits on LDS latency
+      const float2* ct_tab = ct_s[tile & 1];
+      // prefetch first: the source rows of this group's next un-rotation and
+      // (group A) the next tile's tables; they land during the products
+      load_raw(tile + 1, next);
+      if (gi == 0) fetch_tables(tile + 1, cs_s[(tile + 1) & 1], ct_s[(tile + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
       constexpr int kAhead = 4;
       f32x16 acc = {};
       bf16x8 xf[kAhead];
@@ -287,21 +313,10 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], xf[s % kAhead], acc, 0, 0, 0);
         if (s + kAhead < C::KSTEPS) xf[s % kAhead] = *(const bf16x8*)&xg[lds_off<KSEL>(lr, 2 * (s + kAhead) + lk)];
       }
-      // issue order: kAhead reads, then (matrix product, read) pairs, then the tail
-      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS - kAhead; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
-      // prefetch the source rows of this group's next un-rotation; they
-      // land during the epilogue and the other group's phase
       __builtin_amdgcn_sched_barrier(0);
-      load_raw(tile + 1, next);
       // epilogue.  Accumulator j < 8 is column wcol + 8*(j/4) + 4*lk + j%4
-      // of token n; j + 8 is its partner 64 columns up.
-      uint2 plo[2], phi[2];
+      // of token lr; j + 8 is its partner 64 columns up.
+      __bf16* ot = ot_s[gi];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int c0 = wcol + 8 * g + 4 * lk;
@@ -311,8 +326,11 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         float y1[4] = {acc[8 + 4 * g] + bh.x, acc[9 + 4 * g] + bh.y, acc[10 + 4 * g] + bh.z,
                        acc[11 + 4 * g] + bh.w};
         if (keys) {
-          const float4* cp = (const float4*)&ct_s[tile & 1][lr * kCtRow + c0];
-          const float4 v0 = cp[0], v1 = cp[1];
+          // columns c0..c0+3 are pieces e = (c0%8)/2 and e+1 of chunk c0/8
+          const char* tb = (const char*)ct_tab + 128 * lr + 16 * (c0 >> 3);
+          const int e0 = (c0 & 7) >> 1;
+          const float4 v0 = *(const float4*)(tb + e0 * (kCsTileBytes / 4));
+          const float4 v1 = *(const float4*)(tb + (e0 + 1) * (kCsTileBytes / 4));
           const float cc[4] = {v0.x, v0.z, v1.x, v1.z};
           const float ss[4] = {v0.y, v0.w, v1.y, v1.w};
 #pragma unroll
@@ -324,52 +342,59 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
             y1[j] = o1;
           }
         }
-        plo[g].x = pack_bf16(y0[0], y0[1]); plo[g].y = pack_bf16(y0[2], y0[3]);
-        phi[g].x = pack_bf16(y1[0], y1[1]); phi[g].y = pack_bf16(y1[2], y1[3]);
-        __builtin_amdgcn_sched_barrier(0);
+        *(uint2*)&ot[lr * kOtRow + c0] = make_uint2(pack_bf16(y0[0], y0[1]), pack_bf16(y0[2], y0[3]));
+        *(uint2*)&ot[lr * kOtRow + c0 + kHalf] = make_uint2(pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]));
       }
-      // lane lk = 0 gathers columns wcol+0..7, lane lk = 1 columns wcol+8..15
-      const uint2 slo = lk ? plo[0] : plo[1], shi = lk ? phi[0] : phi[1];
-      uint2 rlo, rhi;
-      rlo.x = __shfl_xor(slo.x, 32); rlo.y = __shfl_xor(slo.y, 32);
-      rhi.x = __shfl_xor(shi.x, 32); rhi.y = __shfl_xor(shi.y, 32);
-      if (live) {
-        const int32_t row = a.dst_row ? a.dst_row[n] : n;
-        if (row >= 0) {
-          const uint32_t off = (uint32_t)row * dst_tok_b + 2 * (wcol + 8 * lk);
-          const u32x4 wlo = lk ? u32x4{rlo.x, rlo.y, plo[1].x, plo[1].y} : u32x4{plo[0].x, plo[0].y, rlo.x, rlo.y};
-          const u32x4 whi = lk ? u32x4{rhi.x, rhi.y, phi[1].x, phi[1].y} : u32x4{phi[0].x, phi[0].y, rhi.x, rhi.y};
-          __builtin_amdgcn_raw_buffer_store_b128(wlo, dst, off, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b128(whi, dst, off + kHalf * 2, 0, 0);
+      if (gi == 0) __builtin_amdgcn_s_waitcnt(0);   // the table copies land before the barrier
+    };
+    // Writes a computed tile from this group's LDS output tile to the target
+    // cache: 16 threads per token row, 16 bytes each, so a wave stores whole
+    // 256-byte rows.
+    auto store_out = [&](int tile) __attribute__((always_inline)) {
+      if (!active) return;
+      const int seg = gtid & 15;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = (gtid >> 4) + 16 * hh;
+        const int32_t n = t_begin + tile * kTile + r;
+        if (n < t_end) {
+          const int32_t drow = a.dst_row ? a.dst_row[n] : n;
+          if (drow >= 0) {
+            const u32x4 v = *(const u32x4*)&ot_s[gi][r * kOtRow + 8 * seg];
+            __builtin_amdgcn_raw_buffer_store_b128(v, dst, (uint32_t)drow * dst_tok_b + 16 * seg, 0, 0);
+          }
         }
       }
     };
 
     // ---- ping-pong over tiles.  Phase 2i: A computes tile i, B un-rotates
-    // tile i.  Phase 2i+1: B computes tile i, A un-rotates tile i+1.  Group
-    // A also stages tile i's target (cos, sin) while it prepares tile i; both
-    // groups read it in their epilogues of tile i.  A group's compute phase
-    // prefetches the source rows its next preparation needs.
+    // tile i.  Phase 2i+1: B computes tile i, A un-rotates tile i+1.  A group
+    // stores its previous tile's output during its un-rotation phase.  The
+    // table buffers alternate with the tile parity.
     Raw<KSEL> raw;
     load_raw(0, raw);
-    if (gi == 0) {
-      stage_ct(0);
-      store_tile(raw);
-    }
-    __syncthreads();
+    if (gi == 0) fetch_tables(0, cs_s[0], ct_s[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();                                   // bias and the first tables are visible
+    if (gi == 0) store_tile(raw, cs_s[0]);
+    lds_barrier();
     for (int i = 0; i < nt; ++i) {
-      if (gi == 0) compute_tile(i, raw);
-      else store_tile(raw);
-      __syncthreads();
+      if (gi == 0) {
+        compute_tile(i, raw);
+      } else {
+        if (i > 0) store_out(i - 1);
+        store_tile(raw, cs_s[i & 1]);
+      }
+      lds_barrier();
       if (gi == 1) {
         compute_tile(i, raw);
-      } else if (i + 1 < nt) {
-        stage_ct(i + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        store_tile(raw);
+      } else {
+        store_out(i);
+        if (i + 1 < nt) store_tile(raw, cs_s[(i + 1) & 1]);
       }
-      __syncthreads();
+      lds_barrier();
     }
+    if (gi == 1 && nt > 0) store_out(nt - 1);
   }
 }
 
@@ -394,7 +419,7 @@ bool mfma_supports(const XferArgs& a) {
   // outputs, and every buffer descriptor's byte range below 4 GiB
   auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
   const int64_t lim = 0xffffffffLL;
-  const bool ranges = a.n_tok * kCsRowBytes <= lim && (a.src_rows - 1) * a.src_tok * 2 + kRowBytes <= lim &&
+  const bool ranges = (a.n_tok + kTile - 1) / kTile * kCsTileBytes <= lim && (a.src_rows - 1) * a.src_tok * 2 + kRowBytes <= lim &&
                       (a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes <= lim && a.n_tok < 0x7fffffffLL;
   return ranges && a.D == kD && a.k >= 1 && a.k <= 4 && al(a.src_k, 16) && al(a.src_v, 16) && al(a.W_k, 16) &&
          al(a.W_v, 16) && al(a.out_k, 16) && al(a.out_v, 16) && al(a.rope_src, 16) && al(a.rope_tgt, 16) &&
