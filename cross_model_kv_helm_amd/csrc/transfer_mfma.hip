@@ -9,7 +9,7 @@
 //             keys, un-rotate them at src_pos (R(-p)), rounding the content
 //             key once to bf16 — the operand type of the map;
 //   product   Y = X W on the matrix cores, bf16 x bf16 -> fp32
-//             (v_mfma_f32_16x16x32_bf16), computed as Y^T = W^T X^T so that
+//             (v_mfma_f32_32x32x16_bf16), computed as Y^T = W^T X^T so that
 //             a lane's accumulators hold 4 consecutive output columns;
 //   epilogue  + b, then for keys the forward rotation R(+p') at tgt_pos —
 //             always applied — and a nearest-even store to bf16.
@@ -28,9 +28,17 @@
 //     while the other group un-rotates the next tile into LDS, then they swap
 //     at a barrier.  So on each SIMD the matrix pipe of one wave overlaps the
 //     vector ALU work of the other.
-//   * Register prefetch.  Right after its matrix products a wave issues the
+//   * Register prefetch.  Before its matrix products a wave issues the
 //     global loads of the source rows of its next un-rotation; they land
-//     during its epilogue and the other group's phase.
+//     during its products, epilogue and the other group's phase.
+//   * No hidden waits.  gfx9 counts outstanding global loads and stores in
+//     one in-order counter, so a wait for any one result also waits for
+//     everything issued before it.  Every global access of the tile loop is
+//     therefore issued unconditionally (tokens outside the range get a byte
+//     offset beyond the descriptor, which the hardware turns into a zero
+//     load or a dropped store), and the paged row maps are loaded one phase
+//     before they are used: the only waits left are for data that has had a
+//     whole phase to arrive.
 //   * Persistent sweep over tokens.  Work items are (token chunk, pair of
 //     target layers, head, K|V); a workgroup maps all tokens of its item, so W
 //     is read from HBM once per item.
@@ -52,6 +60,8 @@
 //     hardware drop any access outside the tensor.
 #include "internal.hpp"
 
+#include <type_traits>
+
 namespace helm {
 namespace {
 
@@ -72,6 +82,12 @@ constexpr int kCtRow = kHalf + 2;          // staged target (cos, sin) row: 64 f
 constexpr int kOtRow = kD + 8;             // staged output row: 128 bf16 + pad
 constexpr int kRowBytes = kD * 2;          // one bf16 head row
 constexpr int kCsTileBytes = kTile * kHalf * 8;   // one tile's (cos, sin) block (rope_index layout)
+// Byte offset of a skipped token's row: beyond every descriptor's record
+// count (descriptors are limited to kMaxRange bytes), so its loads return
+// zero and its stores are dropped.  Adding a row's in-row offset (< 256)
+// cannot wrap.
+constexpr uint32_t kMaxRange = 0xffffff00u;
+constexpr uint32_t kSkipRow = 0xffffff00u;
 
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -121,23 +137,47 @@ __device__ __forceinline__ int lds_off(int t, int c) {
 template <int KSEL>
 struct Raw {
   u32x4 lo[KSEL], hi[KSEL];
-  int32_t n;
-  bool have;
+  int32_t row;        // paged: source slot of this thread's token of the next tile to load
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 
-// Copies `bytes` (a multiple of 1024) from global memory into LDS with the
-// global->LDS DMA path: each instruction moves 1 KB (16 bytes per lane of
-// one wave), with no registers in between.  `wave_in_group` / `waves` split
-// the instructions among the waves of a group.
-__device__ __forceinline__ void dma_to_lds(const void* gsrc, void* ldst, int bytes, int wave_in_group, int waves,
-                                          int lane) {
-  for (int off = wave_in_group * 1024; off < bytes; off += waves * 1024)
-    __builtin_amdgcn_global_load_lds((const char*)gsrc + off + 16 * lane, (lds_void_t)((char*)ldst + off), 16, 0, 0);
+// Copies 16 bytes per lane from a buffer into LDS (buffer->LDS DMA): lane
+// i reads the 16 bytes at byte offset soff + 16*i of the buffer described by
+// `rsrc` and they land at lds_base + 16*i, so one wave moves 1 KB with no
+// registers in between.  rsrc, soff and lds_base are wave-uniform.  Written
+// as inline assembly on purpose: the compiler cannot tell which LDS buffer a
+// copy targets and would otherwise make every later LDS access of the wave
+// wait for all outstanding global loads.  The kernel orders these copies
+// itself: the issuing wave waits (wait_vmcnt) before the barrier that
+// publishes the buffer, and no wave touches a buffer while a copy into it is
+// pending.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t soff, const void* lds_base, uint32_t lane16) {
+  const uint32_t m = (uint32_t)(uintptr_t)(lds_void_t)lds_base;
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(lane16), "s"(rsrc), "s"(soff), "s"(m)
+               : "memory", "m0");
 }
 
-template <int KSEL>
+// Plain buffer descriptor words for [base, base + bytes): the same fields
+// as make_rsrc, for use as an inline-assembly operand.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// Waits until at most N of this wave's global loads, stores and
+// global->LDS copies are outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int KSEL, bool PAGED>
 __global__ void __launch_bounds__(kThreads, 1)
 transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t n_items) {
   using C = Cfg<KSEL>;
@@ -161,12 +201,17 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
   const int my_col = lr < 16 ? wcol + lr : kHalf + wcol + (lr - 16);
   const int pt = gtid >> 3;                // un-rotation share: token of the tile
   const int pc = gtid & 7;                 //   and 16-byte chunk of the low half
+  // byte offset of this lane's first epilogue (cos, sin) piece in a tile's
+  // target-side table block: piece e = 2lk of chunk 2wq, token lr
+  const int ep_off = 2 * lk * (kCsTileBytes / 4) + 128 * lr + 32 * wq;
   __bf16* xg = xs[gi];
   const int LP = (a.L_t + 1) / 2;
   const int32_t n_tok = (int32_t)a.n_tok;
   const uint32_t src_tok_b = (uint32_t)a.src_tok * 2, dst_tok_b = (uint32_t)a.dst_tok * 2;
   const uint32_t src_bytes = (uint32_t)((a.src_rows - 1) * a.src_tok * 2 + kRowBytes);
   const uint32_t dst_bytes = (uint32_t)((a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes);
+  const uint32_t tab_bytes = (uint32_t)((a.n_tok + kTile - 1) / kTile * kCsTileBytes);
+  const u32x4 tab_src = rsrc_words(a.rope_src, tab_bytes), tab_tgt = rsrc_words(a.rope_tgt, tab_bytes);
 
   for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int32_t pr = item % n_pairs;
@@ -230,42 +275,42 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
     }
     if (active && gtid < kD / 4) ((float4*)bias_s[gi])[gtid] = ((const float4*)bias)[gtid];
 
+    int32_t drow[2] = {0, 0};   // paged: target slots of the rows this thread stores next
+
     // ---- per-thread pieces of the tile pipeline
+    // Issues the loads of tile `tile`'s source rows (this thread's token pt,
+    // chunks pc and pc+8 of each selected layer).  Skipped tokens load zeros.
     auto load_raw = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
       const int32_t n = t_begin + tile * kTile + pt;
-      r.n = n;
-      r.have = active && tile < nt && n < t_end;
-      int32_t row = n;
-      if (r.have && a.src_row) {
-        row = a.src_row[n];
-        r.have = row >= 0;
+      const bool ok = tile < nt && n < t_end;
+      uint32_t rowb;
+      if constexpr (PAGED) {
+        rowb = ok && r.row >= 0 ? (uint32_t)r.row * src_tok_b : kSkipRow;
+        // slot of the token one tile later, used by the next call
+        r.row = a.src_row[min(n + kTile, t_end - 1)];
+      } else {
+        rowb = ok ? (uint32_t)n * src_tok_b : kSkipRow;
       }
-      if (r.have) {
-        const uint32_t off = (uint32_t)row * src_tok_b + 16 * pc;
+      const uint32_t off = rowb + 16 * pc;
 #pragma unroll
-        for (int j = 0; j < KSEL; ++j) {
-          r.lo[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off, 0, 0);
-          r.hi[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off + kHalf * 2, 0, 0);
-        }
+      for (int j = 0; j < KSEL; ++j) {
+        r.lo[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off, 0, 0);
+        r.hi[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off + kHalf * 2, 0, 0);
       }
     };
-    // Group A fetches a tile's two (cos, sin) blocks into LDS (keys only).
-    auto fetch_tables = [&](int tile, float2* cs_dst, float2* ct_dst) __attribute__((always_inline)) {
+    // One of the four 1 KB pieces that this wave copies of a tile's (cos,
+    // sin) block (keys only): piece q of wave wq is bytes [(4q + wq) KB, +1 KB).
+    auto table_piece = [&](const u32x4& table, float2* dst, int tile, int q) __attribute__((always_inline)) {
       if (keys && tile < nt) {
-        const size_t boff = (size_t)(blk0 + tile) * (kTile * kHalf);
-        dma_to_lds(a.rope_src + boff, cs_dst, kCsTileBytes, wq, 4, lane);
-        dma_to_lds(a.rope_tgt + boff, ct_dst, kCsTileBytes, wq, 4, lane);
+        const uint32_t off = (4 * q + wq) * 1024;
+        dma16(table, (uint32_t)(blk0 + tile) * kCsTileBytes + off, (char*)dst + off, 16 * lane);
       }
     };
+    // Un-rotates (keys) the loaded rows and writes them into the group's
+    // activation tile.  A skipped token's row is zero in, and whatever it
+    // becomes only reaches its own output column, which is never stored.
     auto store_tile = [&](Raw<KSEL>& r, const float2* cs_tab) __attribute__((always_inline)) {
-      if (!active) return;
-      if (!r.have) {
-#pragma unroll
-        for (int j = 0; j < KSEL; ++j) {
-          r.lo[j] = u32x4{0, 0, 0, 0};
-          r.hi[j] = u32x4{0, 0, 0, 0};
-        }
-      } else if (keys) {
+      if (keys) {
         // tile-blocked table: piece e of (token pt, chunk pc) at e*4KB + pt*128 + pc*16
         f32x4 cs[4];
 #pragma unroll
@@ -292,26 +337,76 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         *(u32x4*)&xg[lds_off<KSEL>(pt, 16 * j + 8 + pc)] = r.hi[j];
       }
     };
-    // Y^T = W^T X^T, bias, forward rotation into the LDS output tile.  Group
-    // A also fetches the next tile's tables and waits for its copies before
-    // the phase ends.
-    auto compute_tile = [&](int tile, Raw<KSEL>& next) __attribute__((always_inline)) {
-      if (!active) return;
+    // Writes a computed tile from this group's LDS output tile to the target
+    // cache: 16 threads per token row, 16 bytes each, so a wave stores whole
+    // 256-byte rows.  Always exactly two stores per thread.
+    auto store_out = [&](int tile) __attribute__((always_inline)) {
+      const int seg = gtid & 15;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = (gtid >> 4) + 16 * hh;
+        const int32_t n = t_begin + tile * kTile + r;
+        const int32_t row = PAGED ? drow[hh] : n;
+        const uint32_t rowb = n < t_end && row >= 0 ? (uint32_t)row * dst_tok_b : kSkipRow;
+        const u32x4 v = *(const u32x4*)&ot_s[gi][r * kOtRow + 8 * seg];
+        __builtin_amdgcn_raw_buffer_store_b128(v, dst, rowb + 16 * seg, 0, 0);
+      }
+    };
+    // Matrix products Y^T = W^T X^T of tile `tile`, bias, forward rotation
+    // into the LDS output tile.  The global loads of the group's next
+    // un-rotation are issued first; with CS_DMA (group A) the copy of the
+    // next tile's source-side table is spread over the first products.
+    // Ends with every global access of this wave complete.
+    auto compute_tile = [&](int tile, Raw<KSEL>& raw, auto cs_dma) __attribute__((always_inline)) {
+      constexpr bool CS_DMA = decltype(cs_dma)::value;
+      float2* cs_next = cs_s[(tile + 1) & 1];
+      if (!active) {
+        if constexpr (CS_DMA) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) table_piece(tab_src, cs_next, tile + 1, q);
+        }
+        wait_vmcnt<0>();
+        return;
+      }
       const float2* ct_tab = ct_s[tile & 1];
-      // prefetch first: the source rows of this group's next un-rotation and
-      // (group A) the next tile's tables; they land during the products
-      load_raw(tile + 1, next);
-      if (gi == 0) fetch_tables(tile + 1, cs_s[(tile + 1) & 1], ct_s[(tile + 1) & 1]);
+      if constexpr (PAGED) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          drow[hh] = a.dst_row[min(t_begin + tile * kTile + (gtid >> 4) + 16 * hh, t_end - 1)];
+      }
+      load_raw(tile + 1, raw);
       __builtin_amdgcn_sched_barrier(0);
-      constexpr int kAhead = 4;
+      constexpr int kAhead = KSEL <= 2 ? C::KSTEPS : 4;   // LDS fragments read ahead
+      // step after whose product the epilogue's LDS reads are issued (with
+      // k >= 3 there are no registers to hold them during the products)
+      constexpr int kEpi = KSEL <= 2 ? C::KSTEPS - 4 : C::KSTEPS - 1;
       f32x16 acc = {};
       bf16x8 xf[kAhead];
+      float4 eb[4], ec[4];   // bias and (cos, sin) for the epilogue
 #pragma unroll
       for (int s = 0; s < kAhead; ++s) xf[s] = *(const bf16x8*)&xg[lds_off<KSEL>(lr, 2 * s + lk)];
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], xf[s % kAhead], acc, 0, 0, 0);
         if (s + kAhead < C::KSTEPS) xf[s % kAhead] = *(const bf16x8*)&xg[lds_off<KSEL>(lr, 2 * (s + kAhead) + lk)];
+        if constexpr (CS_DMA) {
+          if (s < 4) table_piece(tab_src, cs_next, tile + 1, s);
+        }
+        if (s == kEpi) {
+          // columns c0 = wcol + 8g + 4lk .. c0+3 of token lr are table
+          // pieces e = 2lk and 2lk+1 of chunk 2wq + g (tile-blocked layout)
+          const char* tb = (const char*)ct_tab + ep_off;
+          const float* bb = &bias_s[gi][wcol + 4 * lk];
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            eb[2 * g] = *(const float4*)(bb + 8 * g);
+            eb[2 * g + 1] = *(const float4*)(bb + 8 * g + kHalf);
+            if (keys) {
+              ec[2 * g] = *(const float4*)(tb + 16 * g);
+              ec[2 * g + 1] = *(const float4*)(tb + 16 * g + kCsTileBytes / 4);
+            }
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       // epilogue.  Accumulator j < 8 is column wcol + 8*(j/4) + 4*lk + j%4
@@ -320,17 +415,12 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int c0 = wcol + 8 * g + 4 * lk;
-        const float4 bl = *(const float4*)&bias_s[gi][c0];
-        const float4 bh = *(const float4*)&bias_s[gi][c0 + kHalf];
+        const float4 bl = eb[2 * g], bh = eb[2 * g + 1];
         float y0[4] = {acc[4 * g] + bl.x, acc[4 * g + 1] + bl.y, acc[4 * g + 2] + bl.z, acc[4 * g + 3] + bl.w};
         float y1[4] = {acc[8 + 4 * g] + bh.x, acc[9 + 4 * g] + bh.y, acc[10 + 4 * g] + bh.z,
                        acc[11 + 4 * g] + bh.w};
         if (keys) {
-          // columns c0..c0+3 are pieces e = (c0%8)/2 and e+1 of chunk c0/8
-          const char* tb = (const char*)ct_tab + 128 * lr + 16 * (c0 >> 3);
-          const int e0 = (c0 & 7) >> 1;
-          const float4 v0 = *(const float4*)(tb + e0 * (kCsTileBytes / 4));
-          const float4 v1 = *(const float4*)(tb + (e0 + 1) * (kCsTileBytes / 4));
+          const float4 v0 = ec[2 * g], v1 = ec[2 * g + 1];
           const float cc[4] = {v0.x, v0.z, v1.x, v1.z};
           const float ss[4] = {v0.y, v0.w, v1.y, v1.w};
 #pragma unroll
@@ -345,56 +435,62 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         *(uint2*)&ot[lr * kOtRow + c0] = make_uint2(pack_bf16(y0[0], y0[1]), pack_bf16(y0[2], y0[3]));
         *(uint2*)&ot[lr * kOtRow + c0 + kHalf] = make_uint2(pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]));
       }
-      if (gi == 0) __builtin_amdgcn_s_waitcnt(0);   // the table copies land before the barrier
-    };
-    // Writes a computed tile from this group's LDS output tile to the target
-    // cache: 16 threads per token row, 16 bytes each, so a wave stores whole
-    // 256-byte rows.
-    auto store_out = [&](int tile) __attribute__((always_inline)) {
-      if (!active) return;
-      const int seg = gtid & 15;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r = (gtid >> 4) + 16 * hh;
-        const int32_t n = t_begin + tile * kTile + r;
-        if (n < t_end) {
-          const int32_t drow = a.dst_row ? a.dst_row[n] : n;
-          if (drow >= 0) {
-            const u32x4 v = *(const u32x4*)&ot_s[gi][r * kOtRow + 8 * seg];
-            __builtin_amdgcn_raw_buffer_store_b128(v, dst, (uint32_t)drow * dst_tok_b + 16 * seg, 0, 0);
-          }
-        }
-      }
+      wait_vmcnt<0>();
     };
 
-    // ---- ping-pong over tiles.  Phase 2i: A computes tile i, B un-rotates
-    // tile i.  Phase 2i+1: B computes tile i, A un-rotates tile i+1.  A group
-    // stores its previous tile's output during its un-rotation phase.  The
-    // table buffers alternate with the tile parity.
-    Raw<KSEL> raw;
-    load_raw(0, raw);
-    if (gi == 0) fetch_tables(0, cs_s[0], ct_s[0]);
-    __builtin_amdgcn_s_waitcnt(0);
-    lds_barrier();                                   // bias and the first tables are visible
-    if (gi == 0) store_tile(raw, cs_s[0]);
-    lds_barrier();
-    for (int i = 0; i < nt; ++i) {
-      if (gi == 0) {
-        compute_tile(i, raw);
-      } else {
-        if (i > 0) store_out(i - 1);
-        store_tile(raw, cs_s[i & 1]);
+    // ---- ping-pong over tiles.  Phase 2i: A computes tile i while B
+    // un-rotates tile i; phase 2i+1: B computes tile i while A un-rotates
+    // tile i+1.  A group stores its previous tile's output at the start of
+    // its un-rotation phase.  Group A copies the tables: the source side of
+    // tile i+1 during its products of tile i (read from the next phase on)
+    // and the target side of tile i+1 during its un-rotation phase (read
+    // from the phase after).  Table buffers alternate with the tile parity.
+    // Each group runs its own copy of the loop, so every register value has
+    // one producer and one consumer; both copies meet the same barriers.
+    auto run = [&](auto group) __attribute__((always_inline)) {
+      constexpr int G = decltype(group)::value;
+      Raw<KSEL> raw;
+      if constexpr (PAGED) raw.row = nt > 0 ? a.src_row[t_begin + pt < t_end ? t_begin + pt : t_end - 1] : -1;
+      if (active) load_raw(0, raw);
+      if constexpr (G == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          table_piece(tab_src, cs_s[0], 0, q);
+          table_piece(tab_tgt, ct_s[0], 0, q);
+        }
       }
+      wait_vmcnt<0>();
+      lds_barrier();                                   // bias and the first tables are visible
+      if (G == 0 && active) store_tile(raw, cs_s[0]);
       lds_barrier();
-      if (gi == 1) {
-        compute_tile(i, raw);
-      } else {
-        store_out(i);
-        if (i + 1 < nt) store_tile(raw, cs_s[(i + 1) & 1]);
+      for (int i = 0; i < nt; ++i) {
+        if constexpr (G == 0) {
+          compute_tile(i, raw, std::integral_constant<bool, true>());
+          lds_barrier();
+#pragma unroll
+          for (int q = 0; q < 4; ++q) table_piece(tab_tgt, ct_s[(i + 1) & 1], i + 1, q);
+          if (active) {
+            store_out(i);
+            if (i + 1 < nt) store_tile(raw, cs_s[(i + 1) & 1]);
+          }
+          wait_vmcnt<2>();                             // the table copy; the two stores may stay in flight
+          lds_barrier();
+        } else {
+          if (active) {
+            if (i > 0) store_out(i - 1);
+            store_tile(raw, cs_s[i & 1]);
+          }
+          lds_barrier();
+          compute_tile(i, raw, std::integral_constant<bool, false>());
+          lds_barrier();
+        }
       }
-      lds_barrier();
-    }
-    if (gi == 1 && nt > 0) store_out(nt - 1);
+      if (G == 1 && active && nt > 0) store_out(nt - 1);
+    };
+    if (gi == 0)
+      run(std::integral_constant<int, 0>());
+    else
+      run(std::integral_constant<int, 1>());
   }
 }
 
@@ -416,10 +512,11 @@ int cu_count() {
 
 bool mfma_supports(const XferArgs& a) {
   // 16-byte vector loads of source rows, W and bias, 16-byte stores of
-  // outputs, and every buffer descriptor's byte range below 4 GiB
+  // outputs, and every buffer descriptor's byte range below kMaxRange
   auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
-  const int64_t lim = 0xffffffffLL;
-  const bool ranges = (a.n_tok + kTile - 1) / kTile * kCsTileBytes <= lim && (a.src_rows - 1) * a.src_tok * 2 + kRowBytes <= lim &&
+  const int64_t lim = kMaxRange;
+  const bool ranges = (a.n_tok + kTile - 1) / kTile * kCsTileBytes <= lim &&
+                      (a.src_rows - 1) * a.src_tok * 2 + kRowBytes <= lim &&
                       (a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes <= lim && a.n_tok < 0x7fffffffLL;
   return ranges && a.D == kD && a.k >= 1 && a.k <= 4 && al(a.src_k, 16) && al(a.src_v, 16) && al(a.W_k, 16) &&
          al(a.W_v, 16) && al(a.out_k, 16) && al(a.out_v, 16) && al(a.rope_src, 16) && al(a.rope_tgt, 16) &&
@@ -442,12 +539,22 @@ hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream) {
   const int64_t grid = n_items < slots ? n_items : slots;
   const dim3 g((unsigned)grid), b(kThreads);
   const int32_t np = (int32_t)n_pairs, ct = (int32_t)chunk_tokens, ni = (int32_t)n_items;
+  const bool paged = a.src_row != nullptr;
+  if (paged != (a.dst_row != nullptr)) return hipErrorInvalidValue;
+#define HELM_LAUNCH(K)                                                                  \
+  do {                                                                                  \
+    if (paged)                                                                          \
+      hipLaunchKernelGGL((transfer_mfma_kernel<K, true>), g, b, 0, stream, a, np, ct, ni); \
+    else                                                                                \
+      hipLaunchKernelGGL((transfer_mfma_kernel<K, false>), g, b, 0, stream, a, np, ct, ni); \
+  } while (0)
   switch (a.k) {
-    case 1: hipLaunchKernelGGL(transfer_mfma_kernel<1>, g, b, 0, stream, a, np, ct, ni); break;
-    case 2: hipLaunchKernelGGL(transfer_mfma_kernel<2>, g, b, 0, stream, a, np, ct, ni); break;
-    case 3: hipLaunchKernelGGL(transfer_mfma_kernel<3>, g, b, 0, stream, a, np, ct, ni); break;
-    default: hipLaunchKernelGGL(transfer_mfma_kernel<4>, g, b, 0, stream, a, np, ct, ni); break;
+    case 1: HELM_LAUNCH(1); break;
+    case 2: HELM_LAUNCH(2); break;
+    case 3: HELM_LAUNCH(3); break;
+    default: HELM_LAUNCH(4); break;
   }
+#undef HELM_LAUNCH
   return hipGetLastError();
 }
 

@@ -131,21 +131,25 @@ def test_zero_tokens_writes_nothing():
     torch.cuda.synchronize()
 
 
-def test_invalid_device_layer_sel_leaves_target_layer_unwritten():
+@pytest.mark.parametrize("bad,T", [(2, 40), (2, 3000), (3, 3000)])
+def test_invalid_device_layer_sel_leaves_target_layer_unwritten(bad, T):
     """A layer_sel row with an index outside [0, L_s) that reaches the device
-    is not read: that target layer is left as it was; the others are mapped."""
-    w = dataclasses.replace(SMALL_BF16, name="bad_sel", n_tokens=40, seed=16)
+    is not read: that target layer is left as it was; the others are mapped.
+    With 3000 tokens every work item spans several token tiles, and the
+    matrix-core kernel pairs target layers (2l, 2l+1): an invalid even layer
+    must not starve its odd partner of anything (its tables included)."""
+    w = dataclasses.replace(SMALL_BF16, name=f"bad_sel_{bad}_{T}", n_tokens=T, seed=16)
     case = Case(w)
     sel = case.host["layer_sel"].copy()
-    sel[2, 1] = 99
+    sel[bad, 1] = 99
     case.dev["layer_sel"] = torch.from_numpy(sel).cuda()
     shape = (w.n_tgt_layers, w.n_kv_heads, case.T, w.head_dim)
     sentinel = torch.full(shape, 3.0, dtype=torch.bfloat16, device="cuda")
     out = (sentinel.clone(), sentinel.clone())
     case.run_gpu(out)
     torch.cuda.synchronize()
-    assert torch.equal(out[0][2], sentinel[2]) and torch.equal(out[1][2], sentinel[2])
-    good = np.array([l for l in range(5) if l != 2])
+    assert torch.equal(out[0][bad], sentinel[bad]) and torch.equal(out[1][bad], sentinel[bad])
+    good = np.array([l for l in range(5) if l != bad])
     rows = np.concatenate([(l * w.n_kv_heads + h) * case.T + np.arange(case.T)
                            for l in good for h in range(w.n_kv_heads)])
     case.host["layer_sel"] = np.where(sel == 99, 0, sel).astype(np.int32)
