@@ -75,6 +75,7 @@ constexpr int kD = 128;          // head dimension
 constexpr int kHalf = 64;
 constexpr int kThreads = 512;    // 8 waves: groups A (0-3) and B (4-7)
 constexpr int kGroupThreads = 256;
+constexpr int kDepth = 4;        // source-row register sets of a data thread (prefetch depth)
 constexpr int kTile = 32;        // tokens per tile = MFMA B-block width
 constexpr int kStageRows = 64;   // W rows staged per pass
 constexpr int kStageRow = kStageRows + 8;  // W^T staging row (padded)
@@ -177,21 +178,26 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// PAGED: source and target rows come from the per-token slot maps
+// (a.src_row, a.dst_row; -1 = skip); otherwise row = token.
 template <int KSEL, bool PAGED>
 __global__ void __launch_bounds__(kThreads, 1)
 transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t n_items) {
   using C = Cfg<KSEL>;
-  __shared__ __attribute__((aligned(16))) __bf16 xs[2][C::BUF_ELEMS];    // one buffer per group
-  __shared__ __attribute__((aligned(16))) float bias_s[2][kD];
-  __shared__ __attribute__((aligned(16))) __bf16 ot_s[2][kTile * kOtRow];    // one output tile per group
-  // (cos, sin) blocks of a tile in the tile-blocked table layout, by tile
-  // parity: source side for the un-rotation, target side for the epilogue
+  constexpr int D = kDepth;
+  // activation tiles and output tiles by tile parity
+  __shared__ __attribute__((aligned(16))) __bf16 xs[2][C::BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) __bf16 ot_s[2][kTile * kOtRow];
+  // (cos, sin) blocks of a tile in the tile-blocked table layout, two
+  // buffers each: source side for the un-rotation, target side for the
+  // epilogue
   __shared__ __attribute__((aligned(16))) float2 cs_s[2][kTile * kHalf];
   __shared__ __attribute__((aligned(16))) float2 ct_s[2][kTile * kHalf];
 
   const int tid = threadIdx.x;
-  // group (0 = A, 1 = B) and wave within the group are wave-uniform
-  const int gi = __builtin_amdgcn_readfirstlane(tid >> 8);
+  // role (0 = matrix waves, 1 = data waves) and wave within the role are
+  // wave-uniform; wave q of each role runs on SIMD q
+  const int role = __builtin_amdgcn_readfirstlane(tid >> 8);
   const int wq = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
   const int gtid = tid & 255;
   const int lane = tid & 63;
@@ -204,8 +210,6 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
   // byte offset of this lane's first epilogue (cos, sin) piece in a tile's
   // target-side table block: piece e = 2lk of chunk 2wq, token lr
   const int ep_off = 2 * lk * (kCsTileBytes / 4) + 128 * lr + 32 * wq;
-  __bf16* xg = xs[gi];
-  const int LP = (a.L_t + 1) / 2;
   const int32_t n_tok = (int32_t)a.n_tok;
   const uint32_t src_tok_b = (uint32_t)a.src_tok * 2, dst_tok_b = (uint32_t)a.dst_tok * 2;
   const uint32_t src_bytes = (uint32_t)((a.src_rows - 1) * a.src_tok * 2 + kRowBytes);
@@ -218,76 +222,49 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
     const int32_t chunk = item / n_pairs;
     const int32_t h = pr % a.H;
     const int32_t rest = pr / a.H;
-    const bool keys = rest < LP;           // pairs [0, LP*H) are keys, the rest values
-    const int32_t l = 2 * (rest % LP) + gi;
+    const bool keys = rest < a.L_t;        // pairs [0, L_t*H) are keys, the rest values
+    const int32_t l = keys ? rest : rest - a.L_t;
     const int32_t t_begin = chunk * chunk_tokens;   // a multiple of kTile
     const int32_t t_end = min(t_begin + chunk_tokens, n_tok);
     const int nt = (t_end - t_begin + kTile - 1) / kTile;
     const int32_t blk0 = t_begin / kTile;  // table block of the item's first tile
 
-    // this group's selected source layers; a missing target layer (odd L_t)
-    // or an out-of-range entry makes the group idle (it still meets barriers)
-    bool active = l < a.L_t;
+    // the selected source layers; an out-of-range entry skips the item (the
+    // target layer is left unwritten)
+    bool active = true;
     rsrc_t srs[KSEL];
 #pragma unroll
     for (int j = 0; j < KSEL; ++j) {
-      const int32_t sj = active ? a.layer_sel[l * KSEL + j] : 0;
-      active = active && sj >= 0 && sj < a.L_s;
-      const uint16_t* base = (const uint16_t*)(keys ? a.src_k : a.src_v) +
-                             (active ? (int64_t)sj * a.src_layer + (int64_t)h * a.src_head : 0);
-      srs[j] = make_rsrc(base, src_bytes);
+      const int32_t sj = a.layer_sel[l * KSEL + j];
+      const bool ok = sj >= 0 && sj < a.L_s;
+      active = active && ok;
+      srs[j] = make_rsrc((const uint16_t*)(keys ? a.src_k : a.src_v) +
+                             (ok ? (int64_t)sj * a.src_layer + (int64_t)h * a.src_head : 0),
+                         src_bytes);
     }
-    const int32_t grp = (active ? l : 0) * a.H + h;
+    if (!active) continue;                 // uniform over the workgroup
+    const int32_t grp = l * a.H + h;
     const uint16_t* W = (const uint16_t*)(keys ? a.W_k : a.W_v) + (int64_t)grp * C::KD * kD;
     const float* bias = (keys ? a.b_k : a.b_v) + (int64_t)grp * kD;
-    const rsrc_t dst = make_rsrc((const uint16_t*)(keys ? a.out_k : a.out_v) +
-                                     (active ? (int64_t)l * a.dst_layer + (int64_t)h * a.dst_head : 0),
+    const rsrc_t dst = make_rsrc((const uint16_t*)(keys ? a.out_k : a.out_v) + (int64_t)l * a.dst_layer +
+                                     (int64_t)h * a.dst_head,
                                  dst_bytes);
 
-    // ---- W^T fragments of this wave's 32 columns, in registers: lane holds
-    // W[m = 16s + 8*lk + i][my_col], i < 8.  W is staged through this
-    // group's LDS tile 64 rows at a time, transposed on the way in
-    // (coalesced 16-byte global loads, 2-byte LDS stores), so that each
-    // fragment is one 16-byte LDS read.
-    bf16x8 wf[C::KSTEPS];
-#pragma unroll
-    for (int part = 0; part < C::KD / kStageRows; ++part) {
-      lds_barrier();                                 // earlier readers of xs are done
-      if (active) {
-        const u32x4* gsrc = (const u32x4*)(W + (int64_t)part * kStageRows * kD);
-#pragma unroll 2
-        for (int e = gtid; e < kStageRows * kD / 8; e += kGroupThreads) {
-          const u32x4 v = gsrc[e];
-          const int m = e >> 4, n0 = (e & 15) << 3;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            xg[(n0 + 2 * q) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] & 0xffffu));
-            xg[(n0 + 2 * q + 1) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] >> 16));
-          }
-        }
-      }
-      lds_barrier();
-      if (active) {
-#pragma unroll
-        for (int s4 = 0; s4 < kStageRows / 16; ++s4)
-          wf[(kStageRows / 16) * part + s4] = *(const bf16x8*)&xg[my_col * kStageRow + 16 * s4 + 8 * lk];
-      }
-    }
-    if (active && gtid < kD / 4) ((float4*)bias_s[gi])[gtid] = ((const float4*)bias)[gtid];
+    bf16x8 wf[C::KSTEPS];       // matrix waves: W^T fragments (see below)
+    bf16x8 wb = {}, ones = {};  // matrix waves: the bias step
 
-    int32_t drow[2] = {0, 0};   // paged: target slots of the rows this thread stores next
-
-    // ---- per-thread pieces of the tile pipeline
+    // ---- data-wave pieces
     // Issues the loads of tile `tile`'s source rows (this thread's token pt,
-    // chunks pc and pc+8 of each selected layer).  Skipped tokens load zeros.
+    // chunks pc and pc+8 of each selected layer).  Tokens outside the item
+    // load zeros.
     auto load_raw = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
       const int32_t n = t_begin + tile * kTile + pt;
       const bool ok = tile < nt && n < t_end;
       uint32_t rowb;
       if constexpr (PAGED) {
         rowb = ok && r.row >= 0 ? (uint32_t)r.row * src_tok_b : kSkipRow;
-        // slot of the token one tile later, used by the next call
-        r.row = a.src_row[min(n + kTile, t_end - 1)];
+        // slot of this thread's token of the next tile this register set loads
+        r.row = a.src_row[max(min(n + D * kTile, t_end - 1), 0)];
       } else {
         rowb = ok ? (uint32_t)n * src_tok_b : kSkipRow;
       }
@@ -298,18 +275,10 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         r.hi[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off + kHalf * 2, 0, 0);
       }
     };
-    // One of the four 1 KB pieces that this wave copies of a tile's (cos,
-    // sin) block (keys only): piece q of wave wq is bytes [(4q + wq) KB, +1 KB).
-    auto table_piece = [&](const u32x4& table, float2* dst, int tile, int q) __attribute__((always_inline)) {
-      if (keys && tile < nt) {
-        const uint32_t off = (4 * q + wq) * 1024;
-        dma16(table, (uint32_t)(blk0 + tile) * kCsTileBytes + off, (char*)dst + off, 16 * lane);
-      }
-    };
-    // Un-rotates (keys) the loaded rows and writes them into the group's
-    // activation tile.  A skipped token's row is zero in, and whatever it
-    // becomes only reaches its own output column, which is never stored.
-    auto store_tile = [&](Raw<KSEL>& r, const float2* cs_tab) __attribute__((always_inline)) {
+    // Un-rotates (keys) the loaded rows and writes them into an activation
+    // tile.  A skipped token's row is zero in, and whatever it becomes only
+    // reaches its own output column, which is never stored.
+    auto store_tile = [&](Raw<KSEL>& r, const float2* cs_tab, __bf16* xt) __attribute__((always_inline)) {
       if (keys) {
         // tile-blocked table: piece e of (token pt, chunk pc) at e*4KB + pt*128 + pc*16
         f32x4 cs[4];
@@ -333,92 +302,76 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
       }
 #pragma unroll
       for (int j = 0; j < KSEL; ++j) {
-        *(u32x4*)&xg[lds_off<KSEL>(pt, 16 * j + pc)] = r.lo[j];
-        *(u32x4*)&xg[lds_off<KSEL>(pt, 16 * j + 8 + pc)] = r.hi[j];
+        *(u32x4*)&xt[lds_off<KSEL>(pt, 16 * j + pc)] = r.lo[j];
+        *(u32x4*)&xt[lds_off<KSEL>(pt, 16 * j + 8 + pc)] = r.hi[j];
       }
     };
-    // Writes a computed tile from this group's LDS output tile to the target
-    // cache: 16 threads per token row, 16 bytes each, so a wave stores whole
-    // 256-byte rows.  Always exactly two stores per thread.
-    auto store_out = [&](int tile) __attribute__((always_inline)) {
+    // Writes a computed tile from an LDS output tile to the target cache: 16
+    // threads per token row, 16 bytes each, so a wave stores whole 256-byte
+    // rows.  Always exactly two stores per thread (tile -1 stores nothing).
+    auto store_out = [&](int tile, const __bf16* ot, const int32_t* drow) __attribute__((always_inline)) {
       const int seg = gtid & 15;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int r = (gtid >> 4) + 16 * hh;
         const int32_t n = t_begin + tile * kTile + r;
         const int32_t row = PAGED ? drow[hh] : n;
-        const uint32_t rowb = n < t_end && row >= 0 ? (uint32_t)row * dst_tok_b : kSkipRow;
-        const u32x4 v = *(const u32x4*)&ot_s[gi][r * kOtRow + 8 * seg];
+        const uint32_t rowb = tile >= 0 && n < t_end && row >= 0 ? (uint32_t)row * dst_tok_b : kSkipRow;
+        const u32x4 v = *(const u32x4*)&ot[r * kOtRow + 8 * seg];
         __builtin_amdgcn_raw_buffer_store_b128(v, dst, rowb + 16 * seg, 0, 0);
       }
     };
-    // Matrix products Y^T = W^T X^T of tile `tile`, bias, forward rotation
-    // into the LDS output tile.  The global loads of the group's next
-    // un-rotation are issued first; with CS_DMA (group A) the copy of the
-    // next tile's source-side table is spread over the first products.
-    // Ends with every global access of this wave complete.
-    auto compute_tile = [&](int tile, Raw<KSEL>& raw, auto cs_dma) __attribute__((always_inline)) {
-      constexpr bool CS_DMA = decltype(cs_dma)::value;
-      float2* cs_next = cs_s[(tile + 1) & 1];
-      if (!active) {
-        if constexpr (CS_DMA) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) table_piece(tab_src, cs_next, tile + 1, q);
-        }
-        wait_vmcnt<0>();
-        return;
+    // ---- matrix-wave pieces
+    // One of the four 1 KB pieces that this wave copies of a tile's (cos,
+    // sin) block (keys only): piece q of wave wq is bytes [(4q + wq) KB, +1 KB).
+    auto table_piece = [&](const u32x4& table, float2* dst_tab, int tile, int q) __attribute__((always_inline)) {
+      if (keys && tile < nt) {
+        const uint32_t off = (4 * q + wq) * 1024;
+        dma16(table, (uint32_t)(blk0 + tile) * kCsTileBytes + off, (char*)dst_tab + off, 16 * lane);
       }
-      const float2* ct_tab = ct_s[tile & 1];
-      if constexpr (PAGED) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          drow[hh] = a.dst_row[min(t_begin + tile * kTile + (gtid >> 4) + 16 * hh, t_end - 1)];
-      }
-      load_raw(tile + 1, raw);
-      __builtin_amdgcn_sched_barrier(0);
-      constexpr int kAhead = KSEL <= 2 ? C::KSTEPS : 4;   // LDS fragments read ahead
-      // step after whose product the epilogue's LDS reads are issued (with
-      // k >= 3 there are no registers to hold them during the products)
-      constexpr int kEpi = KSEL <= 2 ? C::KSTEPS - 4 : C::KSTEPS - 1;
-      f32x16 acc = {};
+    };
+    // Matrix products Y^T = W^T X^T + b of tile `tile` from xt and the
+    // forward rotation into the LDS output tile ot.  The copies of the next
+    // tables (target side of tile+1 into ct_next, source side of tile+2
+    // into cs_next) are spread over the first products; the wave ends with
+    // them complete.
+    auto compute_tile = [&](int tile, const __bf16* xt, const float2* ct_tab, float2* ct_next, float2* cs_next,
+                            __bf16* ot) __attribute__((always_inline)) {
+      constexpr int kAhead = C::KSTEPS < 8 ? C::KSTEPS : 8;   // LDS fragments read ahead
+      constexpr int kEpi = C::KSTEPS - 4;   // step after whose product the epilogue's LDS reads are issued
+      static_assert(8 <= C::KSTEPS, "every table copy is issued inside the products");
       bf16x8 xf[kAhead];
-      float4 eb[4], ec[4];   // bias and (cos, sin) for the epilogue
+      float4 ec[4];   // (cos, sin) for the epilogue
 #pragma unroll
-      for (int s = 0; s < kAhead; ++s) xf[s] = *(const bf16x8*)&xg[lds_off<KSEL>(lr, 2 * s + lk)];
+      for (int s = 0; s < kAhead; ++s) xf[s] = *(const bf16x8*)&xt[lds_off<KSEL>(lr, 2 * s + lk)];
+      f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, ones, f32x16{}, 0, 0, 0);
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], xf[s % kAhead], acc, 0, 0, 0);
-        if (s + kAhead < C::KSTEPS) xf[s % kAhead] = *(const bf16x8*)&xg[lds_off<KSEL>(lr, 2 * (s + kAhead) + lk)];
-        if constexpr (CS_DMA) {
-          if (s < 4) table_piece(tab_src, cs_next, tile + 1, s);
-        }
-        if (s == kEpi) {
+        if (s + kAhead < C::KSTEPS) xf[s % kAhead] = *(const bf16x8*)&xt[lds_off<KSEL>(lr, 2 * (s + kAhead) + lk)];
+        if (s < 4)
+          table_piece(tab_tgt, ct_next, tile + 1, s);
+        else if (s < 8)
+          table_piece(tab_src, cs_next, tile + 2, s - 4);
+        if (s == kEpi && keys) {
           // columns c0 = wcol + 8g + 4lk .. c0+3 of token lr are table
           // pieces e = 2lk and 2lk+1 of chunk 2wq + g (tile-blocked layout)
           const char* tb = (const char*)ct_tab + ep_off;
-          const float* bb = &bias_s[gi][wcol + 4 * lk];
 #pragma unroll
           for (int g = 0; g < 2; ++g) {
-            eb[2 * g] = *(const float4*)(bb + 8 * g);
-            eb[2 * g + 1] = *(const float4*)(bb + 8 * g + kHalf);
-            if (keys) {
-              ec[2 * g] = *(const float4*)(tb + 16 * g);
-              ec[2 * g + 1] = *(const float4*)(tb + 16 * g + kCsTileBytes / 4);
-            }
+            ec[2 * g] = *(const float4*)(tb + 16 * g);
+            ec[2 * g + 1] = *(const float4*)(tb + 16 * g + kCsTileBytes / 4);
           }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
       // epilogue.  Accumulator j < 8 is column wcol + 8*(j/4) + 4*lk + j%4
       // of token lr; j + 8 is its partner 64 columns up.
-      __bf16* ot = ot_s[gi];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int c0 = wcol + 8 * g + 4 * lk;
-        const float4 bl = eb[2 * g], bh = eb[2 * g + 1];
-        float y0[4] = {acc[4 * g] + bl.x, acc[4 * g + 1] + bl.y, acc[4 * g + 2] + bl.z, acc[4 * g + 3] + bl.w};
-        float y1[4] = {acc[8 + 4 * g] + bh.x, acc[9 + 4 * g] + bh.y, acc[10 + 4 * g] + bh.z,
-                       acc[11 + 4 * g] + bh.w};
+        float y0[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        float y1[4] = {acc[8 + 4 * g], acc[9 + 4 * g], acc[10 + 4 * g], acc[11 + 4 * g]};
         if (keys) {
           const float4 v0 = ec[2 * g], v1 = ec[2 * g + 1];
           const float cc[4] = {v0.x, v0.z, v1.x, v1.z};
@@ -435,62 +388,117 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         *(uint2*)&ot[lr * kOtRow + c0] = make_uint2(pack_bf16(y0[0], y0[1]), pack_bf16(y0[2], y0[3]));
         *(uint2*)&ot[lr * kOtRow + c0 + kHalf] = make_uint2(pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]));
       }
-      wait_vmcnt<0>();
+      wait_vmcnt<0>();   // the table copies have landed
     };
 
-    // ---- ping-pong over tiles.  Phase 2i: A computes tile i while B
-    // un-rotates tile i; phase 2i+1: B computes tile i while A un-rotates
-    // tile i+1.  A group stores its previous tile's output at the start of
-    // its un-rotation phase.  Group A copies the tables: the source side of
-    // tile i+1 during its products of tile i (read from the next phase on)
-    // and the target side of tile i+1 during its un-rotation phase (read
-    // from the phase after).  Table buffers alternate with the tile parity.
-    // Each group runs its own copy of the loop, so every register value has
-    // one producer and one consumer; both copies meet the same barriers.
-    auto run = [&](auto group) __attribute__((always_inline)) {
-      constexpr int G = decltype(group)::value;
-      Raw<KSEL> raw;
-      if constexpr (PAGED) raw.row = nt > 0 ? a.src_row[t_begin + pt < t_end ? t_begin + pt : t_end - 1] : -1;
-      if (active) load_raw(0, raw);
-      if constexpr (G == 0) {
+    // ---- the tile pipeline.  Phase i (i = 0 .. nt): the matrix waves
+    // compute tile i from xs[i%2] into ot_s[i%2] and copy the tables of the
+    // next tiles; the data waves store tile i-1 from ot_s[(i-1)%2],
+    // un-rotate tile i+1 into xs[(i+1)%2] and issue the loads of tile i+1+D
+    // into the register set that tile i+1 used (D sets, so loads have D-1
+    // phases to land).  A barrier ends every phase.  The phase loop is
+    // unrolled by 4 so that buffer parities and register sets are fixed per
+    // copy; the roles run separate loops that meet the same barriers.
+    static_assert(D == 4, "register sets cycle with the 4-fold unrolled phase loop");
+    lds_barrier();                                   // the previous item's readers of xs[0] are done
+    if (role == 0) {
+      // W^T fragments of this wave's 32 columns, in registers: lane holds
+      // W[m = 16s + 8*lk + i][my_col], i < 8.  The matrix waves stage W
+      // through xs[0] 64 rows at a time, transposed on the way in
+      // (coalesced 16-byte global loads, 2-byte LDS stores), so that each
+      // fragment is one 16-byte LDS read.  (Set up inside the role branch
+      // so that the fragments are live only where they are used.)
+      __bf16* stage = xs[0];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          table_piece(tab_src, cs_s[0], 0, q);
-          table_piece(tab_tgt, ct_s[0], 0, q);
+      for (int part = 0; part < C::KD / kStageRows; ++part) {
+        const u32x4* gsrc = (const u32x4*)(W + (int64_t)part * kStageRows * kD);
+#pragma unroll
+        for (int e = gtid; e < kStageRows * kD / 8; e += kGroupThreads) {
+          const u32x4 v = gsrc[e];
+          const int m = e >> 4, n0 = (e & 15) << 3;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            stage[(n0 + 2 * q) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] & 0xffffu));
+            stage[(n0 + 2 * q + 1) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] >> 16));
+          }
         }
+        lds_barrier();
+#pragma unroll
+        for (int s4 = 0; s4 < kStageRows / 16; ++s4)
+          wf[(kStageRows / 16) * part + s4] = *(const bf16x8*)&stage[my_col * kStageRow + 16 * s4 + 8 * lk];
+        lds_barrier();                               // the stage may be overwritten
+      }
+      // The bias enters the products as one more 16-deep step: A holds the
+      // column's fp32 bias split exactly into three bf16 parts (b = b1 + b2
+      // + b3), B holds ones in the matching rows, so the accumulator starts
+      // at b with no LDS traffic and no epilogue additions.
+      if (lk == 0) {
+        const float b = bias[my_col];
+        const __bf16 b1 = (__bf16)b;
+        const __bf16 b2 = (__bf16)(b - (float)b1);
+        const __bf16 b3 = (__bf16)(b - (float)b1 - (float)b2);
+        wb[0] = b1;
+        wb[1] = b2;
+        wb[2] = b3;
+        ones[0] = ones[1] = ones[2] = (__bf16)1.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        table_piece(tab_src, cs_s[0], 0, q);
+        table_piece(tab_tgt, ct_s[0], 0, q);
+        table_piece(tab_src, cs_s[1], 1, q);
       }
       wait_vmcnt<0>();
-      lds_barrier();                                   // bias and the first tables are visible
-      if (G == 0 && active) store_tile(raw, cs_s[0]);
-      lds_barrier();
-      for (int i = 0; i < nt; ++i) {
-        if constexpr (G == 0) {
-          compute_tile(i, raw, std::integral_constant<bool, true>());
-          lds_barrier();
-#pragma unroll
-          for (int q = 0; q < 4; ++q) table_piece(tab_tgt, ct_s[(i + 1) & 1], i + 1, q);
-          if (active) {
-            store_out(i);
-            if (i + 1 < nt) store_tile(raw, cs_s[(i + 1) & 1]);
-          }
-          wait_vmcnt<2>();                             // the table copy; the two stores may stay in flight
-          lds_barrier();
-        } else {
-          if (active) {
-            if (i > 0) store_out(i - 1);
-            store_tile(raw, cs_s[i & 1]);
-          }
-          lds_barrier();
-          compute_tile(i, raw, std::integral_constant<bool, false>());
-          lds_barrier();
-        }
+      lds_barrier();                                 // tables of tiles 0 (and 1) visible
+      lds_barrier();                                 // tile 0 un-rotated
+      auto phase = [&](int i, auto par) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;     // i % 2
+        if (i < nt) compute_tile(i, xs[P], ct_s[P], ct_s[P ^ 1], cs_s[P], ot_s[P]);
+        lds_barrier();
+      };
+      for (int i = 0; i <= nt; i += 4) {
+        phase(i, std::integral_constant<int, 0>());
+        phase(i + 1, std::integral_constant<int, 1>());
+        phase(i + 2, std::integral_constant<int, 0>());
+        phase(i + 3, std::integral_constant<int, 1>());
       }
-      if (G == 1 && active && nt > 0) store_out(nt - 1);
-    };
-    if (gi == 0)
-      run(std::integral_constant<int, 0>());
-    else
-      run(std::integral_constant<int, 1>());
+    } else {
+      Raw<KSEL> raw[D];
+      int32_t drow[2][2] = {{0, 0}, {0, 0}};   // paged: target slots of this thread's rows, by tile parity
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if constexpr (PAGED) raw[d].row = a.src_row[max(min(t_begin + d * kTile + pt, t_end - 1), 0)];
+        load_raw(d, raw[d]);
+      }
+#pragma unroll
+      for (int part = 0; part < C::KD / kStageRows; ++part) {   // the matrix waves stage W
+        lds_barrier();
+        lds_barrier();
+      }
+      lds_barrier();                                 // tables of tiles 0 (and 1) visible
+      store_tile(raw[0], cs_s[0], xs[0]);
+      load_raw(D, raw[0]);
+      lds_barrier();                                 // tile 0 un-rotated
+      auto phase = [&](int i, auto set) __attribute__((always_inline)) {
+        constexpr int S = decltype(set)::value;     // (i + 1) % D
+        constexpr int P = (S + 1) & 1;              // i % 2
+        store_out(i - 1, ot_s[P ^ 1], drow[P ^ 1]);
+        if constexpr (PAGED) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            drow[P][hh] = a.dst_row[max(min(t_begin + i * kTile + (gtid >> 4) + 16 * hh, t_end - 1), 0)];
+        }
+        if (i + 1 < nt) store_tile(raw[S], cs_s[P ^ 1], xs[P ^ 1]);
+        load_raw(i + 1 + D, raw[S]);
+        lds_barrier();
+      };
+      for (int i = 0; i <= nt; i += 4) {
+        phase(i, std::integral_constant<int, 1>());
+        phase(i + 1, std::integral_constant<int, 2>());
+        phase(i + 2, std::integral_constant<int, 3>());
+        phase(i + 3, std::integral_constant<int, 0>());
+      }
+    }
   }
 }
 
@@ -526,7 +534,7 @@ bool mfma_supports(const XferArgs& a) {
 hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream) {
   if (!mfma_supports(a)) return hipErrorNotSupported;
   if (a.n_tok <= 0) return hipSuccess;
-  const int64_t n_pairs = (int64_t)((a.L_t + 1) / 2) * a.H * 2;
+  const int64_t n_pairs = (int64_t)a.L_t * a.H * 2;
   const int64_t slots = cu_count();   // one 8-wave workgroup per CU
   // Split tokens into chunks only when there are fewer pairs than CUs.
   int64_t n_chunks = 1;
