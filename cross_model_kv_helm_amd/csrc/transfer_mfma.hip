@@ -75,7 +75,7 @@ constexpr int kD = 128;          // head dimension
 constexpr int kHalf = 64;
 constexpr int kThreads = 512;    // 8 waves: groups A (0-3) and B (4-7)
 constexpr int kGroupThreads = 256;
-constexpr int kDepth = 4;        // source-row register sets of a data thread (prefetch depth)
+constexpr int kDepth = 2;        // source-row register sets of a data thread (prefetch depth)
 constexpr int kTile = 32;        // tokens per tile = MFMA B-block width
 constexpr int kStageRows = 64;   // W rows staged per pass
 constexpr int kStageRow = kStageRows + 8;  // W^T staging row (padded)
@@ -134,10 +134,11 @@ __device__ __forceinline__ int lds_off(int t, int c) {
 
 // What one thread prefetches for its share of a tile's un-rotation: 16-byte
 // chunks pc (low half) and pc+8 (high half) of token pt for each selected
-// layer.
+// layer, and the (cos, sin) pairs of dims 8pc .. 8pc+7 of that token.
 template <int KSEL>
 struct Raw {
   u32x4 lo[KSEL], hi[KSEL];
+  f32x4 cs[4];
   int32_t row;        // paged: source slot of this thread's token of the next tile to load
 };
 
@@ -188,10 +189,8 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
   // activation tiles and output tiles by tile parity
   __shared__ __attribute__((aligned(16))) __bf16 xs[2][C::BUF_ELEMS];
   __shared__ __attribute__((aligned(16))) __bf16 ot_s[2][kTile * kOtRow];
-  // (cos, sin) blocks of a tile in the tile-blocked table layout, two
-  // buffers each: source side for the un-rotation, target side for the
-  // epilogue
-  __shared__ __attribute__((aligned(16))) float2 cs_s[2][kTile * kHalf];
+  // target-side (cos, sin) blocks of a tile (tile-blocked table layout) for
+  // the epilogue, by tile parity
   __shared__ __attribute__((aligned(16))) float2 ct_s[2][kTile * kHalf];
 
   const int tid = threadIdx.x;
@@ -215,7 +214,7 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
   const uint32_t src_bytes = (uint32_t)((a.src_rows - 1) * a.src_tok * 2 + kRowBytes);
   const uint32_t dst_bytes = (uint32_t)((a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes);
   const uint32_t tab_bytes = (uint32_t)((a.n_tok + kTile - 1) / kTile * kCsTileBytes);
-  const u32x4 tab_src = rsrc_words(a.rope_src, tab_bytes), tab_tgt = rsrc_words(a.rope_tgt, tab_bytes);
+  const u32x4 tab_tgt = rsrc_words(a.rope_tgt, tab_bytes);
 
   for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int32_t pr = item % n_pairs;
@@ -243,6 +242,9 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
                          src_bytes);
     }
     if (!active) continue;                 // uniform over the workgroup
+    // source-side tables (keys only: for values the descriptor is empty and
+    // its loads return zeros without touching memory)
+    const rsrc_t cs_rs = make_rsrc(a.rope_src, keys ? tab_bytes : 0u);
     const int32_t grp = l * a.H + h;
     const uint16_t* W = (const uint16_t*)(keys ? a.W_k : a.W_v) + (int64_t)grp * C::KD * kD;
     const float* bias = (keys ? a.b_k : a.b_v) + (int64_t)grp * kD;
@@ -257,7 +259,7 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
     // Issues the loads of tile `tile`'s source rows (this thread's token pt,
     // chunks pc and pc+8 of each selected layer).  Tokens outside the item
     // load zeros.
-    auto load_raw = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
+    auto raw_offset = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
       const int32_t n = t_begin + tile * kTile + pt;
       const bool ok = tile < nt && n < t_end;
       uint32_t rowb;
@@ -268,48 +270,65 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
       } else {
         rowb = ok ? (uint32_t)n * src_tok_b : kSkipRow;
       }
-      const uint32_t off = rowb + 16 * pc;
-#pragma unroll
-      for (int j = 0; j < KSEL; ++j) {
-        r.lo[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off, 0, 0);
-        r.hi[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off + kHalf * 2, 0, 0);
-      }
+      return rowb + 16 * pc;
     };
-    // Un-rotates (keys) the loaded rows and writes them into an activation
-    // tile.  A skipped token's row is zero in, and whatever it becomes only
-    // reaches its own output column, which is never stored.
-    auto store_tile = [&](Raw<KSEL>& r, const float2* cs_tab, __bf16* xt) __attribute__((always_inline)) {
-      if (keys) {
-        // tile-blocked table: piece e of (token pt, chunk pc) at e*4KB + pt*128 + pc*16
-        f32x4 cs[4];
+    auto load_layer = [&](Raw<KSEL>& r, uint32_t off, int j) __attribute__((always_inline)) {
+      r.lo[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off, 0, 0);
+      r.hi[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off + kHalf * 2, 0, 0);
+    };
+    // tile-blocked table: piece e of (token pt, chunk pc) at e*4KB + pt*128 + pc*16
+    auto load_tables = [&](Raw<KSEL>& r, int tile) __attribute__((always_inline)) {
+      const uint32_t toff = tile < nt ? (uint32_t)(blk0 + tile) * kCsTileBytes + 128 * pt + 16 * pc : kSkipRow;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          cs[e] = *(const f32x4*)((const char*)cs_tab + e * (kCsTileBytes / 4) + 128 * pt + 16 * pc);
-        // one layer at a time, so only one layer's values are unpacked to fp32
+      for (int e = 0; e < 4; ++e)
+        r.cs[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cs_rs, toff + e * (kCsTileBytes / 4), 0, 0));
+    };
+    auto load_raw = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
+      const uint32_t off = raw_offset(tile, r);
 #pragma unroll
-        for (int j = 0; j < KSEL; ++j) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const f32x4 v = cs[e];    // (cos, sin) of dims 8pc+2e and 8pc+2e+1
-            const float l0 = bf16lo(r.lo[j][e]), l1 = bf16hi(r.lo[j][e]);
-            const float h0 = bf16lo(r.hi[j][e]), h1 = bf16hi(r.hi[j][e]);
-            // R(-p): (lo, hi) -> (lo c + hi s, hi c - lo s)
-            r.lo[j][e] = pack_bf16(fmaf(l0, v.x, h0 * v.y), fmaf(l1, v.z, h1 * v.w));
-            r.hi[j][e] = pack_bf16(fmaf(h0, v.x, -(l0 * v.y)), fmaf(h1, v.z, -(l1 * v.w)));
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      for (int j = 0; j < KSEL; ++j) load_layer(r, off, j);
+      load_tables(r, tile);
+    };
+    // Un-rotates (keys) the register set's rows and writes them into an
+    // activation tile (when `use`), refilling the set with tile `next` layer
+    // by layer, so that the loads leave between the arithmetic instead of in
+    // one burst.  A skipped token's row is zero in, and whatever it becomes
+    // only reaches its own output column, which is never stored.
+    auto turn_tile = [&](Raw<KSEL>& r, bool use, __bf16* xt, int next) __attribute__((always_inline)) {
+      const uint32_t off = raw_offset(next, r);
 #pragma unroll
       for (int j = 0; j < KSEL; ++j) {
-        *(u32x4*)&xt[lds_off<KSEL>(pt, 16 * j + pc)] = r.lo[j];
-        *(u32x4*)&xt[lds_off<KSEL>(pt, 16 * j + 8 + pc)] = r.hi[j];
+        if (use) {
+          u32x4 lo = r.lo[j], hi = r.hi[j];
+          if (keys) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const f32x4 v = r.cs[e];    // (cos, sin) of dims 8pc+2e and 8pc+2e+1
+              const float l0 = bf16lo(lo[e]), l1 = bf16hi(lo[e]);
+              const float h0 = bf16lo(hi[e]), h1 = bf16hi(hi[e]);
+              // R(-p): (lo, hi) -> (lo c + hi s, hi c - lo s)
+              lo[e] = pack_bf16(fmaf(l0, v.x, h0 * v.y), fmaf(l1, v.z, h1 * v.w));
+              hi[e] = pack_bf16(fmaf(h0, v.x, -(l0 * v.y)), fmaf(h1, v.z, -(l1 * v.w)));
+            }
+          }
+          *(u32x4*)&xt[lds_off<KSEL>(pt, 16 * j + pc)] = lo;
+          *(u32x4*)&xt[lds_off<KSEL>(pt, 16 * j + 8 + pc)] = hi;
+        }
+        load_layer(r, off, j);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      load_tables(r, next);
     };
     // Writes a computed tile from an LDS output tile to the target cache: 16
     // threads per token row, 16 bytes each, so a wave stores whole 256-byte
-    // rows.  Always exactly two stores per thread (tile -1 stores nothing).
-    auto store_out = [&](int tile, const __bf16* ot, const int32_t* drow) __attribute__((always_inline)) {
+    // rows.  read_out fetches this thread's two 16-byte pieces from LDS;
+    // write_out issues exactly two stores (a negative tile stores nothing).
+    auto read_out = [&](const __bf16* ot, u32x4* v) __attribute__((always_inline)) {
+      const int seg = gtid & 15;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) v[hh] = *(const u32x4*)&ot[((gtid >> 4) + 16 * hh) * kOtRow + 8 * seg];
+    };
+    auto write_out = [&](int tile, const u32x4* v, const int32_t* drow) __attribute__((always_inline)) {
       const int seg = gtid & 15;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -317,8 +336,7 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         const int32_t n = t_begin + tile * kTile + r;
         const int32_t row = PAGED ? drow[hh] : n;
         const uint32_t rowb = tile >= 0 && n < t_end && row >= 0 ? (uint32_t)row * dst_tok_b : kSkipRow;
-        const u32x4 v = *(const u32x4*)&ot[r * kOtRow + 8 * seg];
-        __builtin_amdgcn_raw_buffer_store_b128(v, dst, rowb + 16 * seg, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v[hh], dst, rowb + 16 * seg, 0, 0);
       }
     };
     // ---- matrix-wave pieces
@@ -330,76 +348,82 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         dma16(table, (uint32_t)(blk0 + tile) * kCsTileBytes + off, (char*)dst_tab + off, 16 * lane);
       }
     };
-    // Matrix products Y^T = W^T X^T + b of tile `tile` from xt and the
-    // forward rotation into the LDS output tile ot.  The copies of the next
-    // tables (target side of tile+1 into ct_next, source side of tile+2
-    // into cs_next) are spread over the first products; the wave ends with
-    // them complete.
-    auto compute_tile = [&](int tile, const __bf16* xt, const float2* ct_tab, float2* ct_next, float2* cs_next,
-                            __bf16* ot) __attribute__((always_inline)) {
+    // Forward rotation of one finished accumulator block into the LDS
+    // output tile ot: half g of this lane's columns.  Accumulator j < 8 is
+    // column wcol + 8*(j/4) + 4*lk + j%4 of token lr; j + 8 is its partner
+    // 64 columns up.  ec holds the (cos, sin) pieces of those columns.
+    auto epilogue_half = [&](const f32x16& acc, const float4* ec, __bf16* ot, int g) __attribute__((always_inline)) {
+      const int c0 = wcol + 8 * g + 4 * lk;
+      float y0[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+      float y1[4] = {acc[8 + 4 * g], acc[9 + 4 * g], acc[10 + 4 * g], acc[11 + 4 * g]};
+      if (keys) {
+        const float4 v0 = ec[2 * g], v1 = ec[2 * g + 1];
+        const float cc[4] = {v0.x, v0.z, v1.x, v1.z};
+        const float ss[4] = {v0.y, v0.w, v1.y, v1.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // R(+p'): (lo, hi) -> (lo c - hi s, hi c + lo s)
+          const float o0 = fmaf(y0[j], cc[j], -(y1[j] * ss[j]));
+          const float o1 = fmaf(y1[j], cc[j], y0[j] * ss[j]);
+          y0[j] = o0;
+          y1[j] = o1;
+        }
+      }
+      *(uint2*)&ot[lr * kOtRow + c0] = make_uint2(pack_bf16(y0[0], y0[1]), pack_bf16(y0[2], y0[3]));
+      *(uint2*)&ot[lr * kOtRow + c0 + kHalf] = make_uint2(pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]));
+    };
+    // The (cos, sin) pieces of this lane's epilogue columns: pieces e = 2lk
+    // and 2lk+1 of chunks 2wq and 2wq+1, token lr (tile-blocked layout).
+    auto epilogue_tables = [&](const float2* ct_tab, float4* ec) __attribute__((always_inline)) {
+      if (keys) {
+        const char* tb = (const char*)ct_tab + ep_off;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          ec[2 * g] = *(const float4*)(tb + 16 * g);
+          ec[2 * g + 1] = *(const float4*)(tb + 16 * g + kCsTileBytes / 4);
+        }
+      }
+    };
+    // One matrix-wave phase: the products Y^T = W^T X^T + b of tile `tile`
+    // from xt into acc, with the epilogue of the previous tile (accp, target
+    // tables ct_prev, output tile ot_prev) and the copy of the target
+    // tables of `tile` (into ct_cur) interleaved between the products, whose
+    // dependent chain leaves the wave idle between issues.  The wave ends
+    // with the copy complete.
+    auto compute_tile = [&](int tile, const __bf16* xt, f32x16& acc, const f32x16& accp, const float2* ct_prev,
+                            __bf16* ot_prev, float2* ct_cur) __attribute__((always_inline)) {
       constexpr int kAhead = C::KSTEPS < 8 ? C::KSTEPS : 8;   // LDS fragments read ahead
-      constexpr int kEpi = C::KSTEPS - 4;   // step after whose product the epilogue's LDS reads are issued
-      static_assert(8 <= C::KSTEPS, "every table copy is issued inside the products");
+      static_assert(8 <= C::KSTEPS, "every table copy and epilogue piece is issued inside the products");
       bf16x8 xf[kAhead];
-      float4 ec[4];   // (cos, sin) for the epilogue
+      float4 ec[4];
 #pragma unroll
       for (int s = 0; s < kAhead; ++s) xf[s] = *(const bf16x8*)&xt[lds_off<KSEL>(lr, 2 * s + lk)];
-      f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, ones, f32x16{}, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, ones, f32x16{}, 0, 0, 0);
+      epilogue_tables(ct_prev, ec);
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], xf[s % kAhead], acc, 0, 0, 0);
         if (s + kAhead < C::KSTEPS) xf[s % kAhead] = *(const bf16x8*)&xt[lds_off<KSEL>(lr, 2 * (s + kAhead) + lk)];
-        if (s < 4)
-          table_piece(tab_tgt, ct_next, tile + 1, s);
-        else if (s < 8)
-          table_piece(tab_src, cs_next, tile + 2, s - 4);
-        if (s == kEpi && keys) {
-          // columns c0 = wcol + 8g + 4lk .. c0+3 of token lr are table
-          // pieces e = 2lk and 2lk+1 of chunk 2wq + g (tile-blocked layout)
-          const char* tb = (const char*)ct_tab + ep_off;
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            ec[2 * g] = *(const float4*)(tb + 16 * g);
-            ec[2 * g + 1] = *(const float4*)(tb + 16 * g + kCsTileBytes / 4);
-          }
-        }
+        if (s < 4) table_piece(tab_tgt, ct_cur, tile, s);
+        if (s == 4) epilogue_half(accp, ec, ot_prev, 0);
+        if (s == 6) epilogue_half(accp, ec, ot_prev, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // epilogue.  Accumulator j < 8 is column wcol + 8*(j/4) + 4*lk + j%4
-      // of token lr; j + 8 is its partner 64 columns up.
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int c0 = wcol + 8 * g + 4 * lk;
-        float y0[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-        float y1[4] = {acc[8 + 4 * g], acc[9 + 4 * g], acc[10 + 4 * g], acc[11 + 4 * g]};
-        if (keys) {
-          const float4 v0 = ec[2 * g], v1 = ec[2 * g + 1];
-          const float cc[4] = {v0.x, v0.z, v1.x, v1.z};
-          const float ss[4] = {v0.y, v0.w, v1.y, v1.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            // R(+p'): (lo, hi) -> (lo c - hi s, hi c + lo s)
-            const float o0 = fmaf(y0[j], cc[j], -(y1[j] * ss[j]));
-            const float o1 = fmaf(y1[j], cc[j], y0[j] * ss[j]);
-            y0[j] = o0;
-            y1[j] = o1;
-          }
-        }
-        *(uint2*)&ot[lr * kOtRow + c0] = make_uint2(pack_bf16(y0[0], y0[1]), pack_bf16(y0[2], y0[3]));
-        *(uint2*)&ot[lr * kOtRow + c0 + kHalf] = make_uint2(pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]));
-      }
       wait_vmcnt<0>();   // the table copies have landed
     };
 
-    // ---- the tile pipeline.  Phase i (i = 0 .. nt): the matrix waves
-    // compute tile i from xs[i%2] into ot_s[i%2] and copy the tables of the
-    // next tiles; the data waves store tile i-1 from ot_s[(i-1)%2],
-    // un-rotate tile i+1 into xs[(i+1)%2] and issue the loads of tile i+1+D
-    // into the register set that tile i+1 used (D sets, so loads have D-1
-    // phases to land).  A barrier ends every phase.  The phase loop is
-    // unrolled by 4 so that buffer parities and register sets are fixed per
-    // copy; the roles run separate loops that meet the same barriers.
-    static_assert(D == 4, "register sets cycle with the 4-fold unrolled phase loop");
+    // ---- the tile pipeline.  Phase i (i = 0 .. nt+1): the matrix waves
+    // compute tile i from xs[i%2] (accumulators kept in registers) while
+    // rotating tile i-1 into ot_s[(i-1)%2], and copy the target tables of
+    // tile i; the data waves store tile i-2 from ot_s[i%2], un-rotate tile
+    // i+1 into xs[(i+1)%2] and issue the loads of tile i+1+D (source rows
+    // and source-side tables) into the register set that tile i+1 used (D
+    // sets, so loads have D-1 phases to land).  A barrier ends every phase.  The
+    // phase loop is unrolled by 4 so that buffer parities and register sets
+    // are fixed per copy; the roles run separate loops that meet the same
+    // barriers.
+    static_assert(4 % D == 0, "register sets cycle with the 4-fold unrolled phase loop");
     lds_barrier();                                   // the previous item's readers of xs[0] are done
     if (role == 0) {
       // W^T fragments of this wave's 32 columns, in registers: lane holds
@@ -442,21 +466,23 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         wb[2] = b3;
         ones[0] = ones[1] = ones[2] = (__bf16)1.0f;
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        table_piece(tab_src, cs_s[0], 0, q);
-        table_piece(tab_tgt, ct_s[0], 0, q);
-        table_piece(tab_src, cs_s[1], 1, q);
-      }
-      wait_vmcnt<0>();
-      lds_barrier();                                 // tables of tiles 0 (and 1) visible
       lds_barrier();                                 // tile 0 un-rotated
+      f32x16 acc[2] = {{}, {}};   // accumulators by tile parity
       auto phase = [&](int i, auto par) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value;     // i % 2
-        if (i < nt) compute_tile(i, xs[P], ct_s[P], ct_s[P ^ 1], cs_s[P], ot_s[P]);
+        if (i < nt) {
+          // (in phase 0 the epilogue rotates an empty block into ot_s[1];
+          // the data waves never store it)
+          compute_tile(i, xs[P], acc[P], acc[P ^ 1], ct_s[P ^ 1], ot_s[P ^ 1], ct_s[P]);
+        } else if (i == nt) {
+          float4 ec[4];
+          epilogue_tables(ct_s[P ^ 1], ec);
+          epilogue_half(acc[P ^ 1], ec, ot_s[P ^ 1], 0);
+          epilogue_half(acc[P ^ 1], ec, ot_s[P ^ 1], 1);
+        }
         lds_barrier();
       };
-      for (int i = 0; i <= nt; i += 4) {
+      for (int i = 0; i <= nt + 1; i += 4) {
         phase(i, std::integral_constant<int, 0>());
         phase(i + 1, std::integral_constant<int, 1>());
         phase(i + 2, std::integral_constant<int, 0>());
@@ -475,28 +501,28 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         lds_barrier();
         lds_barrier();
       }
-      lds_barrier();                                 // tables of tiles 0 (and 1) visible
-      store_tile(raw[0], cs_s[0], xs[0]);
-      load_raw(D, raw[0]);
+      turn_tile(raw[0], true, xs[0], D);
       lds_barrier();                                 // tile 0 un-rotated
-      auto phase = [&](int i, auto set) __attribute__((always_inline)) {
-        constexpr int S = decltype(set)::value;     // (i + 1) % D
-        constexpr int P = (S + 1) & 1;              // i % 2
-        store_out(i - 1, ot_s[P ^ 1], drow[P ^ 1]);
+      auto phase = [&](int i, auto kk) __attribute__((always_inline)) {
+        constexpr int P = decltype(kk)::value & 1;          // i % 2
+        constexpr int S = (decltype(kk)::value + 1) % D;    // (i + 1) % D
+        // the output reads first: their latency hides behind the un-rotation
+        u32x4 ov[2];
+        read_out(ot_s[P], ov);
+        turn_tile(raw[S], i + 1 < nt, xs[P ^ 1], i + 1 + D);
+        write_out(i - 2, ov, drow[P]);
         if constexpr (PAGED) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
-            drow[P][hh] = a.dst_row[max(min(t_begin + i * kTile + (gtid >> 4) + 16 * hh, t_end - 1), 0)];
+            drow[P ^ 1][hh] = a.dst_row[max(min(t_begin + (i - 1) * kTile + (gtid >> 4) + 16 * hh, t_end - 1), 0)];
         }
-        if (i + 1 < nt) store_tile(raw[S], cs_s[P ^ 1], xs[P ^ 1]);
-        load_raw(i + 1 + D, raw[S]);
         lds_barrier();
       };
-      for (int i = 0; i <= nt; i += 4) {
-        phase(i, std::integral_constant<int, 1>());
-        phase(i + 1, std::integral_constant<int, 2>());
-        phase(i + 2, std::integral_constant<int, 3>());
-        phase(i + 3, std::integral_constant<int, 0>());
+      for (int i = 0; i <= nt + 1; i += 4) {
+        phase(i, std::integral_constant<int, 0>());
+        phase(i + 1, std::integral_constant<int, 1>());
+        phase(i + 2, std::integral_constant<int, 2>());
+        phase(i + 3, std::integral_constant<int, 3>());
       }
     }
   }
