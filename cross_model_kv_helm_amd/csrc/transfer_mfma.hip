@@ -190,8 +190,8 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
   __shared__ __attribute__((aligned(16))) __bf16 xs[2][C::BUF_ELEMS];
   __shared__ __attribute__((aligned(16))) __bf16 ot_s[2][kTile * kOtRow];
   // target-side (cos, sin) blocks of a tile (tile-blocked table layout) for
-  // the epilogue, by tile parity
-  __shared__ __attribute__((aligned(16))) float2 ct_s[2][kTile * kHalf];
+  // the epilogue, by tile index mod 3
+  __shared__ __attribute__((aligned(16))) float2 ct_s[3][kTile * kHalf];
 
   const int tid = threadIdx.x;
   // role (0 = matrix waves, 1 = data waves) and wave within the role are
@@ -387,11 +387,12 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
     // One matrix-wave phase: the products Y^T = W^T X^T + b of tile `tile`
     // from xt into acc, with the epilogue of the previous tile (accp, target
     // tables ct_prev, output tile ot_prev) and the copy of the target
-    // tables of `tile` (into ct_cur) interleaved between the products, whose
+    // tables of tile+1 (into ct_next) interleaved between the products, whose
     // dependent chain leaves the wave idle between issues.  The wave ends
-    // with the copy complete.
+    // with the copy of the previous phase complete; this phase's copy stays
+    // in flight until the end of the next one.
     auto compute_tile = [&](int tile, const __bf16* xt, f32x16& acc, const f32x16& accp, const float2* ct_prev,
-                            __bf16* ot_prev, float2* ct_cur) __attribute__((always_inline)) {
+                            __bf16* ot_prev, float2* ct_next) __attribute__((always_inline)) {
       constexpr int kAhead = C::KSTEPS < 8 ? C::KSTEPS : 8;   // LDS fragments read ahead
       static_assert(8 <= C::KSTEPS, "every table copy and epilogue piece is issued inside the products");
       bf16x8 xf[kAhead];
@@ -405,25 +406,28 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         __builtin_amdgcn_sched_barrier(0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], xf[s % kAhead], acc, 0, 0, 0);
         if (s + kAhead < C::KSTEPS) xf[s % kAhead] = *(const bf16x8*)&xt[lds_off<KSEL>(lr, 2 * (s + kAhead) + lk)];
-        if (s < 4) table_piece(tab_tgt, ct_cur, tile, s);
+        if (s < 4) table_piece(tab_tgt, ct_next, tile + 1, s);
         if (s == 4) epilogue_half(accp, ec, ot_prev, 0);
         if (s == 6) epilogue_half(accp, ec, ot_prev, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<0>();   // the table copies have landed
+      // the matrix waves issue no other global accesses: the previous
+      // phase's four copies are complete once at most these four remain
+      wait_vmcnt<4>();
     };
 
     // ---- the tile pipeline.  Phase i (i = 0 .. nt+1): the matrix waves
     // compute tile i from xs[i%2] (accumulators kept in registers) while
-    // rotating tile i-1 into ot_s[(i-1)%2], and copy the target tables of
-    // tile i; the data waves store tile i-2 from ot_s[i%2], un-rotate tile
-    // i+1 into xs[(i+1)%2] and issue the loads of tile i+1+D (source rows
-    // and source-side tables) into the register set that tile i+1 used (D
-    // sets, so loads have D-1 phases to land).  A barrier ends every phase.  The
-    // phase loop is unrolled by 4 so that buffer parities and register sets
-    // are fixed per copy; the roles run separate loops that meet the same
-    // barriers.
-    static_assert(4 % D == 0, "register sets cycle with the 4-fold unrolled phase loop");
+    // rotating tile i-1 into ot_s[(i-1)%2] with the target tables in
+    // ct_s[(i-1)%3], and copy the target tables of tile i+1 into
+    // ct_s[(i+1)%3]; the data waves store tile i-2 from ot_s[i%2], un-rotate
+    // tile i+1 into xs[(i+1)%2] and issue the loads of tile i+1+D (source
+    // rows and source-side tables) into the register set that tile i+1 used
+    // (D sets, so loads have D-1 phases to land).  A barrier ends every
+    // phase.  The phase loop is unrolled by 6 so that buffer indices and
+    // register sets are fixed per copy; the roles run separate loops that
+    // meet the same barriers.
+    static_assert(6 % D == 0, "register sets cycle with the 6-fold unrolled phase loop");
     lds_barrier();                                   // the previous item's readers of xs[0] are done
     if (role == 0) {
       // W^T fragments of this wave's 32 columns, in registers: lane holds
@@ -466,27 +470,35 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         wb[2] = b3;
         ones[0] = ones[1] = ones[2] = (__bf16)1.0f;
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) table_piece(tab_tgt, ct_s[0], 0, q);
+      wait_vmcnt<0>();
       lds_barrier();                                 // tile 0 un-rotated
       f32x16 acc[2] = {{}, {}};   // accumulators by tile parity
-      auto phase = [&](int i, auto par) __attribute__((always_inline)) {
-        constexpr int P = decltype(par)::value;     // i % 2
+      auto phase = [&](int i, auto kk) __attribute__((always_inline)) {
+        constexpr int K = decltype(kk)::value;      // i % 6
+        constexpr int P = K & 1, T = K % 3, Tp = (K + 2) % 3, Tn = (K + 1) % 3;
         if (i < nt) {
           // (in phase 0 the epilogue rotates an empty block into ot_s[1];
           // the data waves never store it)
-          compute_tile(i, xs[P], acc[P], acc[P ^ 1], ct_s[P ^ 1], ot_s[P ^ 1], ct_s[P]);
+          compute_tile(i, xs[P], acc[P], acc[P ^ 1], ct_s[Tp], ot_s[P ^ 1], ct_s[Tn]);
         } else if (i == nt) {
+          wait_vmcnt<0>();
           float4 ec[4];
-          epilogue_tables(ct_s[P ^ 1], ec);
+          epilogue_tables(ct_s[Tp], ec);
           epilogue_half(acc[P ^ 1], ec, ot_s[P ^ 1], 0);
           epilogue_half(acc[P ^ 1], ec, ot_s[P ^ 1], 1);
         }
+        (void)T;
         lds_barrier();
       };
-      for (int i = 0; i <= nt + 1; i += 4) {
+      for (int i = 0; i <= nt + 1; i += 6) {
         phase(i, std::integral_constant<int, 0>());
         phase(i + 1, std::integral_constant<int, 1>());
-        phase(i + 2, std::integral_constant<int, 0>());
-        phase(i + 3, std::integral_constant<int, 1>());
+        phase(i + 2, std::integral_constant<int, 2>());
+        phase(i + 3, std::integral_constant<int, 3>());
+        phase(i + 4, std::integral_constant<int, 4>());
+        phase(i + 5, std::integral_constant<int, 5>());
       }
     } else {
       Raw<KSEL> raw[D];
@@ -518,11 +530,13 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         }
         lds_barrier();
       };
-      for (int i = 0; i <= nt + 1; i += 4) {
+      for (int i = 0; i <= nt + 1; i += 6) {
         phase(i, std::integral_constant<int, 0>());
         phase(i + 1, std::integral_constant<int, 1>());
         phase(i + 2, std::integral_constant<int, 2>());
         phase(i + 3, std::integral_constant<int, 3>());
+        phase(i + 4, std::integral_constant<int, 4>());
+        phase(i + 5, std::integral_constant<int, 5>());
       }
     }
   }
