@@ -1,6 +1,6 @@
 """Benchmark of the cross-model KV-cache transfer on one MI355X.
 
-One step = one full transfer (RoPE tables + the transfer kernel) of the
+One step = one full transfer (RoPE table kernel + the transfer kernel) of the
 Qwen3-14B -> 32B-shaped workload: 40 source -> 64 target layers, 8 KV heads,
 head_dim 128, k = 4 selected source layers per target layer, 32,768 tokens,
 bf16 caches and maps, fp32 bias — the configuration the headline mapper time
@@ -11,10 +11,19 @@ HBM before the timed region.
 Prints ONE JSON line: mapped KV tokens/s (tokens whose K and V are written
 for every target layer and head), ms per 32K-token transfer, the roofline of
 the transfer kernel, and the CPU oracle's throughput on a bounded sample.
+
+The roofline's `achieved` divides the algorithmic work of one launch by the
+transfer kernel's own average duration, timed live with HIP events around
+the map stage alone (helm_kv_transfer_stage with HELM_STAGE_MAP, on the
+stream it is launched on).  `traffic` is the HBM byte count per launch that
+rocprofv3's FETCH_SIZE / WRITE_SIZE counters gave for this kernel source
+(profiles/transfer_mfma_qwen3_14b_32b_t32k_counters.md, scaled by a plain
+copy of known size); it is null when the kernel source has changed since.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -27,6 +36,28 @@ if ROOT not in sys.path:
 
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 matrix cores
+
+
+COUNTERS_MD = os.path.join(ROOT, "profiles", "transfer_mfma_qwen3_14b_32b_t32k_counters.md")
+KERNEL_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "transfer_mfma.hip")
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic():
+    """(bytes per launch, note) from the committed counter summary, or
+    (None, reason) when it is missing or was taken on another kernel source."""
+    try:
+        text = open(COUNTERS_MD).read()
+    except OSError:
+        return None, "no counter summary"
+    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(("sha256:", "hbm_bytes_per_launch:")))
+    if fields.get("sha256", "").strip() != kernel_source_digest():
+        return None, "counters were taken on another kernel source"
+    return float(fields["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE x2 + WRITE_SIZE (copy-calibrated)"
 
 
 def log(msg):
@@ -159,9 +190,9 @@ def main():
     # so small workloads are timed from HBM, not from cache
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if out_k.numel() * 4 < (1 << 30) else None
 
-    def step():
-        hk.helm_kv_transfer(src_k, c["src_v"], c["src_pos"], c["tgt_pos"], c["layer_sel"], c["W_k"], c["b_k"],
-                            c["W_v"], c["b_v"], out_k, out_v, shape, workspace=ws)
+    def step(stages=hk.HELM_STAGE_ALL):
+        hk.helm_kv_transfer_stage(stages, src_k, c["src_v"], c["src_pos"], c["tgt_pos"], c["layer_sel"], c["W_k"],
+                                  c["b_k"], c["W_v"], c["b_v"], out_k, out_v, shape, workspace=ws)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -187,22 +218,44 @@ def main():
     log(f"per step: mean {ms:.4f} ms, median {np.median(per):.4f}, p10 {np.percentile(per, 10):.4f}, "
         f"p90 {np.percentile(per, 90):.4f}; wall {wall:.3f} s")
 
+    # the transfer kernel alone: the map stage, reading the tables the steps
+    # above left in the workspace (same positions)
+    log(f"timing {args.steps} launches of the transfer kernel alone")
+    kstarts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    kends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        kstarts[i].record(stream)
+        step(hk.HELM_STAGE_MAP)
+        kends[i].record(stream)
+    torch.cuda.synchronize()
+    kper = np.array([s.elapsed_time(e) for s, e in zip(kstarts, kends)])
+    kms = float(kper.mean())
+    log(f"transfer kernel: mean {kms:.4f} ms, median {np.median(kper):.4f}")
+
     B, F, parts = algorithmic_work(w, c["layer_sel"].cpu().numpy(), T)
     t_s = ms * 1e-3
-    hbm_frac = B / t_s / HBM_PEAK
-    mfma_frac = F / t_s / MFMA_BF16_PEAK
+    t_k = kms * 1e-3
+    hbm_frac = B / t_k / HBM_PEAK
+    mfma_frac = F / t_k / MFMA_BF16_PEAK
     t_hbm, t_mfma = B / HBM_PEAK, F / MFMA_BF16_PEAK
     bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    traffic, traffic_note = recorded_traffic()
     if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": B / t_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": hbm_frac, "traffic": None}
+        roof = {"bound": "hbm", "achieved": B / t_k / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": hbm_frac, "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "achieved": F / t_s / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
-                "frac": mfma_frac, "traffic": None}
+        roof = {"bound": "mfma", "achieved": F / t_k / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                "frac": mfma_frac, "traffic": traffic}
+    roof["kernel"] = "transfer_mfma_kernel"
+    roof["kernel_ms"] = kms
     roof["mfma_frac"] = mfma_frac
     roof["hbm_frac"] = hbm_frac
     roof["algorithmic_bytes"] = B
     roof["algorithmic_flops"] = F
+    roof["traffic_source"] = traffic_note
 
     cpu = None
     if args.cpu_budget > 0:

@@ -23,7 +23,9 @@ STATUS = {0: "HELM_OK", 1: "HELM_E_INVALID_ARG", 2: "HELM_E_PAIR_SHAPE", 3: "HEL
           4: "HELM_E_NO_DEVICE", 5: "HELM_E_DTYPE", 6: "HELM_E_ARCH", 7: "HELM_E_WORKSPACE",
           8: "HELM_E_ALIAS", 9: "HELM_E_PAGED_TABLE", 10: "HELM_E_LAUNCH"}
 
-EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_paged", "helm_kv_workspace_bytes",
+HELM_STAGE_TABLES, HELM_STAGE_MAP, HELM_STAGE_ALL = 1, 2, 3
+
+EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_stage", "helm_kv_transfer_paged", "helm_kv_workspace_bytes",
             "helm_kv_paged_workspace_bytes", "helm_mapper_check", "helm_paged_check",
             "helm_device_check", "helm_arch_supported", "helm_last_error", "helm_status_string",
             "helm_abi_version")
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
         vp, i32p = ctypes.c_void_p, ctypes.c_void_p
         L.helm_kv_transfer.restype = ctypes.c_int
         L.helm_kv_transfer.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
+        L.helm_kv_transfer_stage.argtypes = [ctypes.c_int] + [vp] * 11 + [ctypes.POINTER(HelmShape)]
+        L.helm_kv_transfer_stage.restype = ctypes.c_int
         L.helm_kv_transfer_paged.restype = ctypes.c_int
         L.helm_kv_transfer_paged.argtypes = [vp] * 14 + [ctypes.POINTER(HelmPagedShape)]
         L.helm_kv_workspace_bytes.restype = ctypes.c_size_t
@@ -212,6 +216,15 @@ def helm_kv_transfer(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b
     stream when unset).  ``workspace``: a uint8 device tensor of at least
     helm_kv_workspace_bytes(shape) bytes; allocated here when omitted.
     Raises HelmError on a refused call (nothing is written then)."""
+    helm_kv_transfer_stage(HELM_STAGE_ALL, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v,
+                           out_k, out_v, shape, workspace)
+
+
+def helm_kv_transfer_stage(stages: int, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v,
+                           out_k, out_v, shape: HelmShape, workspace=None) -> None:
+    """One or both stages of the transfer (HELM_STAGE_TABLES, HELM_STAGE_MAP,
+    HELM_STAGE_ALL); the map stage reads the tables an earlier tables stage
+    left in the same ``workspace``."""
     import torch
     L_s, L_t, H, D, k, T = (shape.n_src_layers, shape.n_tgt_layers, shape.n_kv_heads,
                             shape.head_dim, shape.k, shape.n_tokens)
@@ -226,11 +239,13 @@ def helm_kv_transfer(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b
     ]
     if not shape.stream:
         shape.stream = current_stream_ptr(src_k.device)
+    if stages != HELM_STAGE_ALL and workspace is None:
+        raise ValueError("a single stage needs the caller's workspace (the tables live there)")
     if workspace is None:
         workspace = torch.empty(helm_kv_workspace_bytes(shape), dtype=torch.uint8, device=src_k.device)
     shape.workspace = workspace.data_ptr()
     shape.workspace_bytes = workspace.numel()
-    _raise(lib().helm_kv_transfer(*ptrs, ctypes.byref(shape)))
+    _raise(lib().helm_kv_transfer_stage(int(stages), *ptrs, ctypes.byref(shape)))
 
 
 def make_paged_shape(src_k_pool, tgt_k_pool, W_k, layer_sel, src_block_table, tgt_block_table,

@@ -139,12 +139,14 @@ int launch_status(hipError_t e, const char* what) {
 }
 
 int run_transfer(helm::XferArgs& a, int32_t dtype, const int32_t* src_pos, const int32_t* tgt_pos,
-                 double th_s, double th_t, hipStream_t stream) {
-  int rc = launch_status(helm::launch_rope_tables(src_pos, tgt_pos, a.n_tok, a.D, th_s, th_t,
-                                                  const_cast<float2*>(a.rope_src),
-                                                  const_cast<float2*>(a.rope_tgt), stream),
-                         "RoPE table kernel launch");
-  if (rc != HELM_OK) return rc;
+                 double th_s, double th_t, hipStream_t stream, int stages = HELM_STAGE_ALL) {
+  int rc = HELM_OK;
+  if (stages & HELM_STAGE_TABLES)
+    rc = launch_status(helm::launch_rope_tables(src_pos, tgt_pos, a.n_tok, a.D, th_s, th_t,
+                                                const_cast<float2*>(a.rope_src),
+                                                const_cast<float2*>(a.rope_tgt), stream),
+                       "RoPE table kernel launch");
+  if (rc != HELM_OK || !(stages & HELM_STAGE_MAP)) return rc;
   if (dtype == HELM_BF16 && helm::mfma_supports(a))
     rc = launch_status(helm::launch_transfer_mfma(a, stream), "matrix-core transfer kernel launch");
   else
@@ -265,11 +267,13 @@ int helm_paged_check(const helm_paged_shape_t* s, const int32_t* sbt, const int3
   return HELM_OK;
 }
 
-int helm_kv_transfer(const void* src_k, const void* src_v, const int32_t* src_pos,
-                     const int32_t* tgt_pos, const int32_t* layer_sel, const void* W_k,
-                     const float* b_k, const void* W_v, const float* b_v, void* out_k, void* out_v,
-                     const helm_shape_t* s) {
+int helm_kv_transfer_stage(int stages, const void* src_k, const void* src_v, const int32_t* src_pos,
+                           const int32_t* tgt_pos, const int32_t* layer_sel, const void* W_k,
+                           const float* b_k, const void* W_v, const float* b_v, void* out_k, void* out_v,
+                           const helm_shape_t* s) {
   clear_error();
+  if (stages < HELM_STAGE_TABLES || stages > HELM_STAGE_ALL)
+    return fail(HELM_E_INVALID_ARG, "stages = %d; expected 1 (tables), 2 (map) or 3 (both)", stages);
   if (!s) return fail(HELM_E_INVALID_ARG, "shape is NULL");
   int rc = check_common(common_of(s));
   if (rc != HELM_OK) return rc;
@@ -330,7 +334,15 @@ int helm_kv_transfer(const void* src_k, const void* src_v, const int32_t* src_po
   a.dst_tok = a.src_tok; a.dst_head = a.src_head; a.dst_layer = a.src_layer;
   a.src_rows = a.dst_rows = s->n_tokens;
   return run_transfer(a, s->dtype, src_pos, tgt_pos, s->rope_theta_src, s->rope_theta_tgt,
-                      (hipStream_t)s->stream);
+                      (hipStream_t)s->stream, stages);
+}
+
+int helm_kv_transfer(const void* src_k, const void* src_v, const int32_t* src_pos,
+                     const int32_t* tgt_pos, const int32_t* layer_sel, const void* W_k,
+                     const float* b_k, const void* W_v, const float* b_v, void* out_k, void* out_v,
+                     const helm_shape_t* s) {
+  return helm_kv_transfer_stage(HELM_STAGE_ALL, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v,
+                                out_k, out_v, s);
 }
 
 int helm_kv_transfer_paged(const void* src_k_pool, const void* src_v_pool, const int32_t* src_bt,

@@ -156,6 +156,32 @@ int helm_kv_transfer(const void* src_k, const void* src_v,
                      void* out_k, void* out_v,
                      const helm_shape_t* shape);
 
+/* helm_kv_transfer in two separately enqueued stages, for callers that map
+ * several batches of caches at the same positions, and for timing the map
+ * alone.  stages is a bit mask:
+ *   HELM_STAGE_TABLES (1)  write the RoPE (cos, sin) tables of src_pos /
+ *                          tgt_pos into shape->workspace;
+ *   HELM_STAGE_MAP    (2)  run the map, reading the tables already in the
+ *                          workspace: they must come from an earlier call
+ *                          with HELM_STAGE_TABLES (or helm_kv_transfer) on
+ *                          the same positions, thetas, n_tokens and
+ *                          head_dim, ordered before this one.  The library
+ *                          does not check that; stale tables give wrong keys.
+ *   HELM_STAGE_ALL    (3)  both, exactly helm_kv_transfer.
+ * Every pointer and shape check of helm_kv_transfer applies in every stage;
+ * same return convention. */
+#define HELM_STAGE_TABLES 1
+#define HELM_STAGE_MAP 2
+#define HELM_STAGE_ALL 3
+int helm_kv_transfer_stage(int stages,
+                           const void* src_k, const void* src_v,
+                           const int32_t* src_pos, const int32_t* tgt_pos,
+                           const int32_t* layer_sel,
+                           const void* W_k, const float* b_k,
+                           const void* W_v, const float* b_v,
+                           void* out_k, void* out_v,
+                           const helm_shape_t* shape);
+
 /* The same transfer on paged caches driven by block tables (knlp "Routing"
  * page, request-flow figure: the selection is applied to the block table and
  * only the selected blocks are written into the paged cache; "Helm

@@ -80,6 +80,14 @@ def test_invalid_shapes_refused(field, value, status):
     assert hk.helm_last_error()
 
 
+@pytest.mark.parametrize("stages", [0, 4, -1])
+def test_invalid_stage_refused(stages):
+    s = shape()
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(11)]
+    assert hk.lib().helm_kv_transfer_stage(stages, *fake, ctypes.byref(s)) == 1
+    assert "stages" in hk.helm_last_error()
+
+
 def test_null_pointer_refused():
     s = shape()
     ptrs = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(11)]

@@ -156,6 +156,27 @@ def test_invalid_device_layer_sel_leaves_target_layer_unwritten(bad, T):
     check_case(case, *out, rows=rows, label="valid rows of ")
 
 
+def test_staged_call_equals_full_call():
+    """Tables stage, then map stage (reading the tables from the same
+    workspace) gives bit-identical results to the one-call transfer."""
+    import cross_model_kv_helm_amd as hk
+    case = Case(dataclasses.replace(SMALL_BF16, name="staged", n_tokens=700, seed=19))
+    full = case.run_gpu()
+    d = case.dev
+    shape_ = (case.w.n_tgt_layers, case.w.n_kv_heads, case.T, case.w.head_dim)
+    out = (torch.empty(shape_, dtype=torch.bfloat16, device="cuda"),
+           torch.empty(shape_, dtype=torch.bfloat16, device="cuda"))
+    s = hk.make_shape(d["src_k"], d["W_k"], d["layer_sel"], case.w.theta, case.w.theta)
+    ws = torch.empty(hk.helm_kv_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    args = (d["src_k"], d["src_v"], d["src_pos"], d["tgt_pos"], d["layer_sel"], d["W_k"], d["b_k"], d["W_v"],
+            d["b_v"], out[0], out[1], s)
+    hk.helm_kv_transfer_stage(hk.HELM_STAGE_TABLES, *args, workspace=ws)
+    hk.helm_kv_transfer_stage(hk.HELM_STAGE_MAP, *args, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0].view(torch.int16), full[0].view(torch.int16))
+    assert torch.equal(out[1].view(torch.int16), full[1].view(torch.int16))
+
+
 def test_bitwise_deterministic():
     case = Case(dataclasses.replace(SMALL_BF16, name="det", n_tokens=513, seed=17))
     a = case.run_gpu()
