@@ -279,6 +279,23 @@ def test_qwen3_14b_32b_t32k_sampled():
     check_case(case, *out, rows=sample_rows(w.n_tgt_layers, w.n_kv_heads, case.T, 12, 2))
 
 
+@pytest.mark.parametrize("name", ["qwen3_14b_32b_t128k_shift", "qwen3_14b_32b_t128k_gap"])
+def test_qwen3_14b_32b_t128k_sampled(name):
+    """131,072 tokens, transferred prefix placed at target offset 4096, and a
+    1,000-position gap in the source positions at token 65,536: every sampled
+    row must be re-rotated at its own target position."""
+    w = synth.CONFIGS[name]
+    case = Case(w)
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    rows = sample_rows(w.n_tgt_layers, w.n_kv_heads, case.T, 6, 3)
+    # the rows either side of the gap, in every slab
+    edge = np.array([65535, 65536], dtype=np.int64)
+    rows = np.unique(np.concatenate([rows] + [g * case.T + edge for g in range(w.n_tgt_layers * w.n_kv_heads)]))
+    check_case(case, *out, rows=rows)
+    del out, case
+
+
 # ---------------------------------------------------------------- portable-kernel paths
 def test_k5_bf16_portable_kernel_full():
     """k = 5 is outside the matrix-core kernel's range: the portable kernel maps it."""
