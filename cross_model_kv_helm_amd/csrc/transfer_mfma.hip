@@ -186,6 +186,9 @@ __global__ void __launch_bounds__(kThreads, 1)
 transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t n_items) {
   using C = Cfg<KSEL>;
   constexpr int D = kDepth;
+  // contiguous caches: the matrix waves store the output tiles; paged: the
+  // data waves do (they hold the target slot maps)
+  constexpr bool kMatrixStores = !PAGED;
   // activation tiles and output tiles by tile parity
   __shared__ __attribute__((aligned(16))) __bf16 xs[2][C::BUF_ELEMS];
   __shared__ __attribute__((aligned(16))) __bf16 ot_s[2][kTile * kOtRow];
@@ -392,11 +395,13 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
     // with the copy of the previous phase complete; this phase's copy stays
     // in flight until the end of the next one.
     auto compute_tile = [&](int tile, const __bf16* xt, f32x16& acc, const f32x16& accp, const float2* ct_prev,
-                            __bf16* ot_prev, float2* ct_next) __attribute__((always_inline)) {
-      constexpr int kAhead = C::KSTEPS < 8 ? C::KSTEPS : 8;   // LDS fragments read ahead
+                            __bf16* ot_prev, float2* ct_next, const __bf16* ot_store) __attribute__((always_inline)) {
+      // LDS fragments read ahead (with k >= 3 the registers go to W)
+      constexpr int kAhead = C::KSTEPS < 8 ? C::KSTEPS : (KSEL >= 3 ? 4 : 8);
       static_assert(8 <= C::KSTEPS, "every table copy and epilogue piece is issued inside the products");
       bf16x8 xf[kAhead];
       float4 ec[4];
+      u32x4 ov[2];
 #pragma unroll
       for (int s = 0; s < kAhead; ++s) xf[s] = *(const bf16x8*)&xt[lds_off<KSEL>(lr, 2 * s + lk)];
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, ones, f32x16{}, 0, 0, 0);
@@ -409,11 +414,17 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         if (s < 4) table_piece(tab_tgt, ct_next, tile + 1, s);
         if (s == 4) epilogue_half(accp, ec, ot_prev, 0);
         if (s == 6) epilogue_half(accp, ec, ot_prev, 1);
+        if constexpr (kMatrixStores) {
+          if (s == 1) read_out(ot_store, ov);
+          if (s == C::KSTEPS - 1) write_out(tile - 2, ov, nullptr);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
-      // the matrix waves issue no other global accesses: the previous
-      // phase's four copies are complete once at most these four remain
-      wait_vmcnt<4>();
+      // The matrix waves' only other global accesses are their stores (two
+      // per phase, after the copies): the previous phase's four copies are
+      // complete once at most its stores and this phase's copies and stores
+      // remain.
+      wait_vmcnt<kMatrixStores ? 8 : 4>();
     };
 
     // ---- the tile pipeline.  Phase i (i = 0 .. nt+1): the matrix waves
@@ -481,13 +492,20 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         if (i < nt) {
           // (in phase 0 the epilogue rotates an empty block into ot_s[1];
           // the data waves never store it)
-          compute_tile(i, xs[P], acc[P], acc[P ^ 1], ct_s[Tp], ot_s[P ^ 1], ct_s[Tn]);
+          compute_tile(i, xs[P], acc[P], acc[P ^ 1], ct_s[Tp], ot_s[P ^ 1], ct_s[Tn], ot_s[P]);
         } else if (i == nt) {
           wait_vmcnt<0>();
           float4 ec[4];
           epilogue_tables(ct_s[Tp], ec);
           epilogue_half(acc[P ^ 1], ec, ot_s[P ^ 1], 0);
           epilogue_half(acc[P ^ 1], ec, ot_s[P ^ 1], 1);
+        }
+        if constexpr (kMatrixStores) {
+          if (i >= nt && i <= nt + 1) {   // the last two tiles' stores
+            u32x4 ov[2];
+            read_out(ot_s[P], ov);
+            write_out(i - 2, ov, nullptr);
+          }
         }
         (void)T;
         lds_barrier();
@@ -519,10 +537,14 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         constexpr int P = decltype(kk)::value & 1;          // i % 2
         constexpr int S = (decltype(kk)::value + 1) % D;    // (i + 1) % D
         // the output reads first: their latency hides behind the un-rotation
-        u32x4 ov[2];
-        read_out(ot_s[P], ov);
-        turn_tile(raw[S], i + 1 < nt, xs[P ^ 1], i + 1 + D);
-        write_out(i - 2, ov, drow[P]);
+        if constexpr (kMatrixStores) {
+          turn_tile(raw[S], i + 1 < nt, xs[P ^ 1], i + 1 + D);
+        } else {
+          u32x4 ov[2];
+          read_out(ot_s[P], ov);
+          turn_tile(raw[S], i + 1 < nt, xs[P ^ 1], i + 1 + D);
+          write_out(i - 2, ov, drow[P]);
+        }
         if constexpr (PAGED) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
