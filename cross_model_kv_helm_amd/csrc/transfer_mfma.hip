@@ -89,6 +89,7 @@ constexpr int kCsTileBytes = kTile * kHalf * 8;   // one tile's (cos, sin) block
 // cannot wrap.
 constexpr uint32_t kMaxRange = 0xffffff00u;
 constexpr uint32_t kSkipRow = 0xffffff00u;
+constexpr int kStoreNT = 2;      // cache-policy bits of the output stores: nt (streaming)
 
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -179,22 +180,34 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// PAGED: source and target rows come from the per-token slot maps
-// (a.src_row, a.dst_row; -1 = skip); otherwise row = token.
-template <int KSEL, bool PAGED>
-__global__ void __launch_bounds__(kThreads, 1)
-transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t n_items) {
+// The workgroup's LDS tiles.
+template <int KSEL>
+struct Smem {
+  // activation tiles and output tiles by tile parity
+  __attribute__((aligned(16))) __bf16 xs[2][Cfg<KSEL>::BUF_ELEMS];
+  __attribute__((aligned(16))) __bf16 ot_s[2][kTile * kOtRow];
+  // target-side (cos, sin) blocks of a tile (tile-blocked table layout) for
+  // the epilogue, by tile index mod 3 (keys only)
+  __attribute__((aligned(16))) float2 ct_s[3][kTile * kHalf];
+};
+
+// One work item: target layer l, head h, keys (KEYS) or values, tokens of
+// chunk `chunk`.  Values have no rotation on either side, so their items
+// issue no table loads or copies at all.  PAGED: source and target rows
+// come from the per-token slot maps (a.src_row, a.dst_row; -1 = skip);
+// otherwise row = token.
+template <int KSEL, bool PAGED, bool KEYS>
+__device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l, int32_t h, int32_t chunk,
+                                              int32_t chunk_tokens, Smem<KSEL>& sm) {
   using C = Cfg<KSEL>;
   constexpr int D = kDepth;
+  constexpr bool keys = KEYS;
   // contiguous caches: the matrix waves store the output tiles; paged: the
   // data waves do (they hold the target slot maps)
   constexpr bool kMatrixStores = !PAGED;
-  // activation tiles and output tiles by tile parity
-  __shared__ __attribute__((aligned(16))) __bf16 xs[2][C::BUF_ELEMS];
-  __shared__ __attribute__((aligned(16))) __bf16 ot_s[2][kTile * kOtRow];
-  // target-side (cos, sin) blocks of a tile (tile-blocked table layout) for
-  // the epilogue, by tile index mod 3
-  __shared__ __attribute__((aligned(16))) float2 ct_s[3][kTile * kHalf];
+  auto& xs = sm.xs;
+  auto& ot_s = sm.ot_s;
+  auto& ct_s = sm.ct_s;
 
   const int tid = threadIdx.x;
   // role (0 = matrix waves, 1 = data waves) and wave within the role are
@@ -218,14 +231,7 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
   const uint32_t dst_bytes = (uint32_t)((a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes);
   const uint32_t tab_bytes = (uint32_t)((a.n_tok + kTile - 1) / kTile * kCsTileBytes);
   const u32x4 tab_tgt = rsrc_words(a.rope_tgt, tab_bytes);
-
-  for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int32_t pr = item % n_pairs;
-    const int32_t chunk = item / n_pairs;
-    const int32_t h = pr % a.H;
-    const int32_t rest = pr / a.H;
-    const bool keys = rest < a.L_t;        // pairs [0, L_t*H) are keys, the rest values
-    const int32_t l = keys ? rest : rest - a.L_t;
+  {
     const int32_t t_begin = chunk * chunk_tokens;   // a multiple of kTile
     const int32_t t_end = min(t_begin + chunk_tokens, n_tok);
     const int nt = (t_end - t_begin + kTile - 1) / kTile;
@@ -244,10 +250,8 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
                              (ok ? (int64_t)sj * a.src_layer + (int64_t)h * a.src_head : 0),
                          src_bytes);
     }
-    if (!active) continue;                 // uniform over the workgroup
-    // source-side tables (keys only: for values the descriptor is empty and
-    // its loads return zeros without touching memory)
-    const rsrc_t cs_rs = make_rsrc(a.rope_src, keys ? tab_bytes : 0u);
+    if (!active) return;                   // uniform over the workgroup
+    const rsrc_t cs_rs = make_rsrc(a.rope_src, tab_bytes);   // source-side tables (keys)
     const int32_t grp = l * a.H + h;
     const uint16_t* W = (const uint16_t*)(keys ? a.W_k : a.W_v) + (int64_t)grp * C::KD * kD;
     const float* bias = (keys ? a.b_k : a.b_v) + (int64_t)grp * kD;
@@ -281,10 +285,12 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
     };
     // tile-blocked table: piece e of (token pt, chunk pc) at e*4KB + pt*128 + pc*16
     auto load_tables = [&](Raw<KSEL>& r, int tile) __attribute__((always_inline)) {
-      const uint32_t toff = tile < nt ? (uint32_t)(blk0 + tile) * kCsTileBytes + 128 * pt + 16 * pc : kSkipRow;
+      if constexpr (KEYS) {
+        const uint32_t toff = tile < nt ? (uint32_t)(blk0 + tile) * kCsTileBytes + 128 * pt + 16 * pc : kSkipRow;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        r.cs[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cs_rs, toff + e * (kCsTileBytes / 4), 0, 0));
+        for (int e = 0; e < 4; ++e)
+          r.cs[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cs_rs, toff + e * (kCsTileBytes / 4), 0, 0));
+      }
     };
     auto load_raw = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
       const uint32_t off = raw_offset(tile, r);
@@ -339,7 +345,8 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
         const int32_t n = t_begin + tile * kTile + r;
         const int32_t row = PAGED ? drow[hh] : n;
         const uint32_t rowb = tile >= 0 && n < t_end && row >= 0 ? (uint32_t)row * dst_tok_b : kSkipRow;
-        __builtin_amdgcn_raw_buffer_store_b128(v[hh], dst, rowb + 16 * seg, 0, 0);
+        // non-temporal: the kernel never reads its output back
+        __builtin_amdgcn_raw_buffer_store_b128(v[hh], dst, rowb + 16 * seg, 0, kStoreNT);
       }
     };
     // ---- matrix-wave pieces
@@ -423,8 +430,8 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
       // The matrix waves' only other global accesses are their stores (two
       // per phase, after the copies): the previous phase's four copies are
       // complete once at most its stores and this phase's copies and stores
-      // remain.
-      wait_vmcnt<kMatrixStores ? 8 : 4>();
+      // remain.  (Values copy nothing and never wait.)
+      if constexpr (KEYS) wait_vmcnt<kMatrixStores ? 8 : 4>();
     };
 
     // ---- the tile pipeline.  Phase i (i = 0 .. nt+1): the matrix waves
@@ -483,7 +490,7 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) table_piece(tab_tgt, ct_s[0], 0, q);
-      wait_vmcnt<0>();
+      if constexpr (KEYS) wait_vmcnt<0>();
       lds_barrier();                                 // tile 0 un-rotated
       f32x16 acc[2] = {{}, {}};   // accumulators by tile parity
       auto phase = [&](int i, auto kk) __attribute__((always_inline)) {
@@ -494,7 +501,7 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
           // the data waves never store it)
           compute_tile(i, xs[P], acc[P], acc[P ^ 1], ct_s[Tp], ot_s[P ^ 1], ct_s[Tn], ot_s[P]);
         } else if (i == nt) {
-          wait_vmcnt<0>();
+          if constexpr (KEYS) wait_vmcnt<0>();
           float4 ec[4];
           epilogue_tables(ct_s[Tp], ec);
           epilogue_half(acc[P ^ 1], ec, ot_s[P ^ 1], 0);
@@ -564,6 +571,19 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
   }
 }
 
+// Persistent sweep over the keys (KEYS) or the values of every target
+// layer: workgroup b takes items b, b + grid, ...; an item is (token chunk,
+// target layer, head) with the head fastest.
+template <int KSEL, bool PAGED, bool KEYS>
+__global__ void __launch_bounds__(kThreads, 1)
+transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t n_items) {
+  __shared__ __attribute__((aligned(16))) Smem<KSEL> sm;
+  for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int32_t pr = item % n_pairs;
+    transfer_item<KSEL, PAGED, KEYS>(a, pr / a.H, pr % a.H, item / n_pairs, chunk_tokens, sm);
+  }
+}
+
 int g_cu_count = 0;
 
 int cu_count() {
@@ -596,7 +616,7 @@ bool mfma_supports(const XferArgs& a) {
 hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream) {
   if (!mfma_supports(a)) return hipErrorNotSupported;
   if (a.n_tok <= 0) return hipSuccess;
-  const int64_t n_pairs = (int64_t)a.L_t * a.H * 2;
+  const int64_t n_pairs = (int64_t)a.L_t * a.H;   // per launch: the keys, then the values
   const int64_t slots = cu_count();   // one 8-wave workgroup per CU
   // Split tokens into chunks only when there are fewer pairs than CUs.
   int64_t n_chunks = 1;
@@ -611,12 +631,15 @@ hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream) {
   const int32_t np = (int32_t)n_pairs, ct = (int32_t)chunk_tokens, ni = (int32_t)n_items;
   const bool paged = a.src_row != nullptr;
   if (paged != (a.dst_row != nullptr)) return hipErrorInvalidValue;
-#define HELM_LAUNCH(K)                                                                  \
-  do {                                                                                  \
-    if (paged)                                                                          \
-      hipLaunchKernelGGL((transfer_mfma_kernel<K, true>), g, b, 0, stream, a, np, ct, ni); \
-    else                                                                                \
-      hipLaunchKernelGGL((transfer_mfma_kernel<K, false>), g, b, 0, stream, a, np, ct, ni); \
+#define HELM_LAUNCH(K)                                                                          \
+  do {                                                                                          \
+    if (paged) {                                                                                \
+      hipLaunchKernelGGL((transfer_mfma_kernel<K, true, true>), g, b, 0, stream, a, np, ct, ni);  \
+      hipLaunchKernelGGL((transfer_mfma_kernel<K, true, false>), g, b, 0, stream, a, np, ct, ni); \
+    } else {                                                                                    \
+      hipLaunchKernelGGL((transfer_mfma_kernel<K, false, true>), g, b, 0, stream, a, np, ct, ni); \
+      hipLaunchKernelGGL((transfer_mfma_kernel<K, false, false>), g, b, 0, stream, a, np, ct, ni);\
+    }                                                                                           \
   } while (0)
   switch (a.k) {
     case 1: HELM_LAUNCH(1); break;
