@@ -120,6 +120,26 @@ def test_k1_negative_and_large_positions_distinct_thetas():
                    slab, "bf16", "k1_positions V")
 
 
+def test_positions_inside_and_outside_tile_windows():
+    """Position patterns within and across 32-token tiles: tiles 0-3
+    ascending, 4 holding a jump of 100,000, 5 constant, 6-7 scattered, 8-9
+    (the last one ragged) ascending again; target positions descending, with
+    one scattered tile."""
+    T = 300
+    t = np.arange(T)
+    src = np.where(t < 150, t + 7, t + 100000)
+    src[160:192] = 42
+    rng = np.random.default_rng(21)
+    src[192:256] = rng.integers(0, 200000, 64)
+    tgt = 5000 - t                              # descending: every tile is a window
+    tgt[200:232] = rng.integers(-70000, 70000, 32)
+    w = dataclasses.replace(SMALL_BF16, name="tile_windows", n_tokens=T, k=2, seed=22)
+    case = Case(w, src_pos=src.astype(np.int32), tgt_pos=tgt.astype(np.int32))
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    check_case(case, *out)
+
+
 def test_zero_tokens_writes_nothing():
     import cross_model_kv_helm_amd as hk
     w = dataclasses.replace(SMALL_BF16, n_tokens=0)
