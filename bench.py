@@ -43,8 +43,17 @@ KERNEL_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "transfer_mfm
 
 
 def kernel_source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 of the kernel source's code: comments (from // to the end of a
+    line) and blank lines removed, trailing spaces stripped, lines joined by
+    newlines.  Edits to comments keep recorded counters valid; edits to code
+    do not."""
+    lines = []
+    with open(KERNEL_SRC) as f:
+        for line in f:
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def recorded_traffic():

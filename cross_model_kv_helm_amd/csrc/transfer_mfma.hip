@@ -15,22 +15,22 @@
 //             always applied — and a nearest-even store to bf16.
 //
 // Design for MI355X:
-//   * Matrix instruction v_mfma_f32_32x32x16_bf16: it sustains its full rate
-//     from a single accumulator chain.  Each wave owns one 32-row block of
-//     Y^T: rows 0..15 are output columns 16q..16q+15 and rows 16..31 are
-//     columns 64+16q..64+16q+15 (q = wave within its group).  In the 32x32
-//     accumulator layout rows r and r+16 live in the same lane, so the RoPE
-//     partners n and n+64 meet in one lane and the rotation needs no
-//     exchange.  W stays in registers (128 VGPRs per wave for k = 4).
-//   * Ping-pong.  One workgroup of 8 waves per CU holds two groups: A (waves
-//     0-3) and B (waves 4-7); waves w and w+4 share a SIMD.  In every phase
-//     one group runs its matrix products and epilogue for a 32-token tile
-//     while the other group un-rotates the next tile into LDS, then they swap
-//     at a barrier.  So on each SIMD the matrix pipe of one wave overlaps the
-//     vector ALU work of the other.
-//   * Register prefetch.  Before its matrix products a wave issues the
-//     global loads of the source rows of its next un-rotation; they land
-//     during its products, epilogue and the other group's phase.
+//   * Matrix instruction v_mfma_f32_32x32x16_bf16.  A matrix wave owns one
+//     32-row block of Y^T: rows 0..15 are output columns 16q..16q+15 and rows
+//     16..31 are columns 64+16q..64+16q+15 (q = wave within its role).  In the
+//     32x32 accumulator layout rows r and r+16 live in the same lane, so the
+//     RoPE partners n and n+64 meet in one lane and the rotation needs no
+//     exchange.  W stays in registers (128 VGPRs per wave for k = 4) for the
+//     whole token sweep of an item.
+//   * Two roles per CU, one wave of each on every SIMD: four matrix waves
+//     (products, epilogue, target-table copies, output stores) and four data
+//     waves (source-row loads, un-rotation into LDS).  One LDS barrier ends
+//     each 32-token phase; the matrix pipe of one wave overlaps the vector ALU
+//     and memory work of the other.
+//   * Register prefetch.  The data waves load the source rows of a tile two
+//     phases ahead, layer by layer between the un-rotation arithmetic.
+//   * Keys and values are separate launches: values have no rotation, so
+//     their items issue no table loads or copies.
 //   * No hidden waits.  gfx9 counts outstanding global loads and stores in
 //     one in-order counter, so a wait for any one result also waits for
 //     everything issued before it.  Every global access of the tile loop is
@@ -39,20 +39,19 @@
 //     load or a dropped store), and the paged row maps are loaded one phase
 //     before they are used: the only waits left are for data that has had a
 //     whole phase to arrive.
-//   * Persistent sweep over tokens.  Work items are (token chunk, pair of
-//     target layers, head, K|V); a workgroup maps all tokens of its item, so W
-//     is read from HBM once per item.
+//   * Persistent sweep over tokens.  Work items are (token chunk, target
+//     layer, head); a workgroup maps all tokens of its item, so W is read
+//     from HBM once per item.
 //   * XCD-aware order.  Workgroups are dispatched round-robin over the 8
 //     XCDs (id mod 8); with the head as the fastest-varying coordinate of the
 //     item index and 8 heads, every workgroup of an XCD works on the same
-//     head.  All 64 target layers of that head sweep the same tokens at about
-//     the same time, so a source row is fetched from HBM once and then served
-//     from that XCD's L2 to the ~6 target layers that select it.
-//   * Stores through LDS: the epilogue writes its 32x32 block into the
-//     group's LDS output tile; in the group's next phase each wave stores
-//     whole 256-byte token rows (16 bytes per lane), so every store touches
-//     full cache lines.  The tile's (cos, sin) tables use a tile-blocked
-//     layout for the same reason: each 16-byte load of a wave is contiguous.
+//     head, so the ~3 target layers that select a source row read it from
+//     that XCD's L2 at about the same time.
+//   * Stores through LDS: the epilogue writes its 32x32 block into an LDS
+//     output tile; two phases later each wave stores whole 256-byte token
+//     rows (16 bytes per lane), so every store touches full cache lines.  The
+//     tile's (cos, sin) tables use a tile-blocked layout for the same reason:
+//     each 16-byte load of a wave is contiguous.
 //   * Buffer descriptors.  Source rows, cos/sin tables and output rows are
 //     addressed through 128-bit buffer descriptors whose bases are uniform
 //     (per layer and head) and live in scalar registers; a lane carries one
