@@ -18,6 +18,10 @@ enough, suffices", its fit/map listing and its strip/map/apply diagram):
 with R the rotate-half RoPE rotation.  In ``quantize_content`` mode x_k is
 rounded once to the storage dtype before the product.
 
+``kv_cosine`` is the KV-cosine diagnostic ("Helm Intelligent Routing", the
+retention / KL / KV-cosine table): per (layer, head) slab, the cosine of a
+mapped cache and a reference cache taken as flat vectors, in fp64.
+
 Pins: every function here is checked in tests/test_oracle_pins.py against
 closed forms, invariants, special cases that reduce to library routines,
 an independent complex-number / matrix-exponential formulation and a
@@ -282,3 +286,32 @@ def encode_keys(content, pos, theta: float, dtype: int, n_threads: int = 0) -> n
     if rc != 0:
         raise ValueError("oracle_encode_keys: invalid arguments")
     return out
+
+
+def kv_cosine(a, b, dtype: int, n_threads: int = 0) -> np.ndarray:
+    """Per-slab cosine of two caches [..., T, D] (storage dtype: uint16 bf16
+    bits or float32): for every index of the leading dimensions, the cosine
+    between the two [T, D] slabs taken as flat vectors, in fp64 (NaN for a
+    slab of zeros).  Returns the leading shape, fp64.  "Helm Intelligent
+    Routing", the retention / KL / KV-cosine table (KV cosine)."""
+    _check_data(a, dtype, "a")
+    _check_data(b, dtype, "b")
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    if a.shape != b.shape or a.ndim < 2:
+        raise ValueError("a and b must be caches of one shape [..., T, D]")
+    lead = a.shape[:-2]
+    n_slabs = int(np.prod(lead)) if lead else 1
+    n_elems = a.shape[-2] * a.shape[-1]
+    L = lib()
+    if not hasattr(L, "_cos_set"):
+        L.oracle_kv_cosine.restype = ctypes.c_int
+        L.oracle_kv_cosine.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.c_int32]
+        L._cos_set = True
+    out = np.empty(n_slabs, dtype=np.float64)
+    rc = L.oracle_kv_cosine(_ptr(a), _ptr(b), dtype, n_slabs, n_elems,
+                            out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), n_threads)
+    if rc != 0:
+        raise ValueError("oracle_kv_cosine: invalid arguments")
+    return out.reshape(lead)

@@ -440,3 +440,39 @@ int oracle_encode_keys(const void* in, void* out, int32_t dtype,
   }
   return bad;
 }
+
+/* ------------------------------------------------------------------ */
+/* KV-cosine diagnostic                                                 */
+/* ------------------------------------------------------------------ */
+
+/* "Helm Intelligent Routing", the retention / KL / KV-cosine table: the KV
+ * cosine measures how close a mapped cache is to the target model's own.
+ * Reading (the page gives no formula): for each slab s (one K or V cache of
+ * one target layer and head, n_elems = T*D values), the cosine between the
+ * two slabs taken as flat vectors,
+ *   out[s] = sum(a*b) / (sqrt(sum(a*a)) * sqrt(sum(b*b))),
+ * in fp64; a slab of zeros gives 0/0 = NaN.  a and b are n_slabs * n_elems
+ * values of dtype, slab-major.  Returns 0, or 1 on a bad argument. */
+int oracle_kv_cosine(const void* a, const void* b, int32_t dtype, int64_t n_slabs, int64_t n_elems,
+                     double* out, int32_t n_threads) {
+  if (!a || !b || !out || n_slabs < 0 || n_elems < 0) return 1;
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_F32) return 1;
+#ifdef _OPENMP
+  if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+  (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t s = 0; s < n_slabs; ++s) {
+    double ab = 0.0, aa = 0.0, bb = 0.0;
+    for (int64_t e = 0; e < n_elems; ++e) {
+      const double x = load_elem(a, dtype, s * n_elems + e);
+      const double y = load_elem(b, dtype, s * n_elems + e);
+      ab += x * y;
+      aa += x * x;
+      bb += y * y;
+    }
+    out[s] = ab / (sqrt(aa) * sqrt(bb));
+  }
+  return 0;
+}

@@ -495,3 +495,65 @@ def test_encode_keys_is_rounded_rotation(oracle_mod):
             for t in range(5):
                 exact = rope_complex(xf[l, h, t], pos[t], 1e6)
                 assert np.all(np.abs(enc[l, h, t] - exact) <= np.abs(exact) * 2.0 ** -8 * (1 + 1e-9))
+
+
+# ---------------------------------------------------------------- KV-cosine diagnostic
+# "Helm Intelligent Routing", the retention / KL / KV-cosine table: the KV
+# cosine says how close a mapped cache is to the target's own.  Reading: per
+# (layer, head) slab, the cosine of the two [T, D] slabs as flat vectors.
+def _bf16_bits(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_kv_cosine_closed_forms(oracle_mod):
+    """Hand-computed values: (3,4).(4,3) = 24 over 5*5; a slab against
+    itself, its negation and a positive multiple; disjoint supports give 0.
+    Catches a missing square root, a norm of only one side, a dropped sign."""
+    a = np.array([[[[3.0, 4.0]]]], np.float32)
+    b = np.array([[[[4.0, 3.0]]]], np.float32)
+    assert oracle_mod.kv_cosine(a, b, F32)[0, 0] == pytest.approx(24.0 / 25.0, abs=1e-15)
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 3, 17, 8)).astype(np.float32)
+    np.testing.assert_allclose(oracle_mod.kv_cosine(x, x, F32), 1.0, atol=1e-14)
+    np.testing.assert_allclose(oracle_mod.kv_cosine(x, -x, F32), -1.0, atol=1e-14)
+    np.testing.assert_allclose(oracle_mod.kv_cosine(x, 4.0 * x, F32), 1.0, atol=1e-14)
+    even, odd = x.copy(), x.copy()
+    even[..., 1::2] = 0
+    odd[..., 0::2] = 0
+    assert np.all(oracle_mod.kv_cosine(even, odd, F32) == 0.0)
+
+
+def test_kv_cosine_brute_force_and_slab_independence(oracle_mod):
+    """Pure-Python fsum brute force on a tiny case (each slab its own flat
+    vectors), and changing one slab changes that entry only.  Catches slabs
+    mixed up (a wrong stride or a reduction over the wrong axes)."""
+    rng = np.random.default_rng(2)
+    a = rng.standard_normal((3, 2, 5, 4)).astype(np.float32)
+    b = (a + 0.3 * rng.standard_normal(a.shape)).astype(np.float32)
+    got = oracle_mod.kv_cosine(a, b, F32)
+    assert got.shape == (3, 2)
+    for l in range(3):
+        for h in range(2):
+            x = [float(v) for v in a[l, h].ravel()]
+            y = [float(v) for v in b[l, h].ravel()]
+            dot = math.fsum(p * q for p, q in zip(x, y))
+            want = dot / (math.sqrt(math.fsum(p * p for p in x)) * math.sqrt(math.fsum(q * q for q in y)))
+            assert got[l, h] == pytest.approx(want, abs=1e-14)
+    b2 = b.copy()
+    b2[1, 0] = rng.standard_normal((5, 4))
+    got2 = oracle_mod.kv_cosine(a, b2, F32)
+    changed = np.abs(got2 - got) > 0
+    assert changed[1, 0] and changed.sum() == 1
+
+
+def test_kv_cosine_bf16_storage_and_zero_slab(oracle_mod):
+    """bf16 storage decodes to the same values as their fp32 spelling (so
+    the two dtypes agree exactly on bf16-representable data), and a slab of
+    zeros gives NaN (0/0), not a number that looks like a verdict."""
+    rng = np.random.default_rng(3)
+    x = oracle_mod.round_bf16(rng.standard_normal((2, 2, 6, 4))).astype(np.float32)
+    y = oracle_mod.round_bf16(rng.standard_normal((2, 2, 6, 4))).astype(np.float32)
+    np.testing.assert_array_equal(oracle_mod.kv_cosine(_bf16_bits(x), _bf16_bits(y), BF16),
+                                  oracle_mod.kv_cosine(x, y, F32))
+    z = np.zeros_like(x)
+    assert np.all(np.isnan(oracle_mod.kv_cosine(z, y, F32)))
