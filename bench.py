@@ -40,15 +40,17 @@ MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 matrix cores
 
 COUNTERS_MD = os.path.join(ROOT, "profiles", "transfer_mfma_qwen3_14b_32b_t32k_counters.md")
 KERNEL_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "transfer_mfma.hip")
+COSINE_MD = os.path.join(ROOT, "profiles", "kv_cosine_qwen3_14b_32b_t32k.md")
+COSINE_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "cosine.hip")
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(path: str = KERNEL_SRC) -> str:
     """sha256 of the kernel source's code: comments (from // to the end of a
     line) and blank lines removed, trailing spaces stripped, lines joined by
     newlines.  Edits to comments keep recorded counters valid; edits to code
     do not."""
     lines = []
-    with open(KERNEL_SRC) as f:
+    with open(path) as f:
         for line in f:
             code = line.split("//", 1)[0].rstrip()
             if code:
@@ -56,15 +58,15 @@ def kernel_source_digest() -> str:
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
-def recorded_traffic():
-    """(bytes per launch, note) from the committed counter summary, or
+def recorded_traffic(md: str = COUNTERS_MD, src: str = KERNEL_SRC):
+    """(bytes per launch, note) from a committed counter summary, or
     (None, reason) when it is missing or was taken on another kernel source."""
     try:
-        text = open(COUNTERS_MD).read()
+        text = open(md).read()
     except OSError:
         return None, "no counter summary"
     fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(("sha256:", "hbm_bytes_per_launch:")))
-    if fields.get("sha256", "").strip() != kernel_source_digest():
+    if fields.get("sha256", "").strip() != kernel_source_digest(src):
         return None, "counters were taken on another kernel source"
     return float(fields["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE x2 + WRITE_SIZE (copy-calibrated)"
 
@@ -245,6 +247,30 @@ def main():
     kms = float(kper.mean())
     log(f"transfer kernel: mean {kms:.4f} ms, median {np.median(kper):.4f}")
 
+    # the KV-cosine diagnostic on the mapped cache against a reference cache
+    # of the same shape (here a copy: the timing does not depend on values)
+    log(f"timing {args.steps} launches of the KV-cosine diagnostic")
+    ref_k, ref_v = out_k.clone(), out_v.clone()
+    cos_out = torch.empty((2, w.n_tgt_layers, w.n_kv_heads), dtype=torch.float32, device=dev)
+    hk.helm_kv_cosine(out_k, out_v, ref_k, ref_v, shape, out=cos_out)
+    cstarts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    cends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        cstarts[i].record(stream)
+        hk.helm_kv_cosine(out_k, out_v, ref_k, ref_v, shape, out=cos_out)
+        cends[i].record(stream)
+    torch.cuda.synchronize()
+    cms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(cstarts, cends)]))
+    cos_bytes = 4 * out_k.numel() * out_k.element_size()   # both caches, K and V, read once
+    log(f"KV cosine: mean {cms:.4f} ms, {cos_bytes / cms / 1e6:.1f} GB/s; min cosine {cos_out.min().item():.6f}")
+    del ref_k, ref_v
+    cos_traffic, cos_note = recorded_traffic(COSINE_MD, COSINE_SRC)
+    kv_cos = {"ms": cms, "kernel": "kv_cosine_kernel",
+              "roofline": {"bound": "hbm", "achieved": cos_bytes / (cms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
+                           "unit": "GB/s", "frac": cos_bytes / (cms * 1e-3) / HBM_PEAK, "traffic": cos_traffic,
+                           "algorithmic_bytes": cos_bytes, "traffic_source": cos_note}}
+
     B, F, parts = algorithmic_work(w, c["layer_sel"].cpu().numpy(), T)
     t_s = ms * 1e-3
     t_k = kms * 1e-3
@@ -292,6 +318,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "bytes_breakdown": parts,
+        "kv_cosine": kv_cos,
     }
     print(json.dumps(line), flush=True)
 

@@ -25,7 +25,8 @@ STATUS = {0: "HELM_OK", 1: "HELM_E_INVALID_ARG", 2: "HELM_E_PAIR_SHAPE", 3: "HEL
 
 HELM_STAGE_TABLES, HELM_STAGE_MAP, HELM_STAGE_ALL = 1, 2, 3
 
-EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_stage", "helm_kv_transfer_paged", "helm_kv_workspace_bytes",
+EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_stage", "helm_kv_transfer_paged", "helm_kv_cosine",
+            "helm_kv_workspace_bytes",
             "helm_kv_paged_workspace_bytes", "helm_mapper_check", "helm_paged_check",
             "helm_device_check", "helm_arch_supported", "helm_last_error", "helm_status_string",
             "helm_abi_version")
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.helm_kv_transfer.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
         L.helm_kv_transfer_stage.argtypes = [ctypes.c_int] + [vp] * 11 + [ctypes.POINTER(HelmShape)]
         L.helm_kv_transfer_stage.restype = ctypes.c_int
+        L.helm_kv_cosine.restype = ctypes.c_int
+        L.helm_kv_cosine.argtypes = [vp] * 5 + [ctypes.POINTER(HelmShape)]
         L.helm_kv_transfer_paged.restype = ctypes.c_int
         L.helm_kv_transfer_paged.argtypes = [vp] * 14 + [ctypes.POINTER(HelmPagedShape)]
         L.helm_kv_workspace_bytes.restype = ctypes.c_size_t
@@ -246,6 +249,24 @@ def helm_kv_transfer_stage(stages: int, src_k, src_v, src_pos, tgt_pos, layer_se
     shape.workspace = workspace.data_ptr()
     shape.workspace_bytes = workspace.numel()
     _raise(lib().helm_kv_transfer_stage(int(stages), *ptrs, ctypes.byref(shape)))
+
+
+def helm_kv_cosine(k_mapped, v_mapped, k_ref, v_ref, shape: HelmShape, out=None):
+    """KV-cosine diagnostic: [2, L_t, H] float32 on the caches' device, the
+    cosine of every (K|V, layer, head) slab of the mapped cache against the
+    reference cache (see include/helm_kv.h)."""
+    import torch
+    L_t, H, D, T = shape.n_tgt_layers, shape.n_kv_heads, shape.head_dim, shape.n_tokens
+    dt = torch.bfloat16 if shape.dtype == HELM_BF16 else torch.float32
+    ptrs = [_dev_ptr(k_mapped, "k_mapped", dt, (L_t, H, T, D)), _dev_ptr(v_mapped, "v_mapped", dt, (L_t, H, T, D)),
+            _dev_ptr(k_ref, "k_ref", dt, (L_t, H, T, D)), _dev_ptr(v_ref, "v_ref", dt, (L_t, H, T, D))]
+    if out is None:
+        out = torch.empty((2, L_t, H), dtype=torch.float32, device=k_mapped.device)
+    optr = _dev_ptr(out, "out", torch.float32, (2, L_t, H))
+    if not shape.stream:
+        shape.stream = current_stream_ptr(k_mapped.device)
+    _raise(lib().helm_kv_cosine(*ptrs, optr, ctypes.byref(shape)))
+    return out
 
 
 def make_paged_shape(src_k_pool, tgt_k_pool, W_k, layer_sel, src_block_table, tgt_block_table,

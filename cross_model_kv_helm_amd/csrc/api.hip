@@ -435,4 +435,34 @@ int helm_kv_transfer_paged(const void* src_k_pool, const void* src_v_pool, const
   return run_transfer(a, s->dtype, src_pos, tgt_pos, s->rope_theta_src, s->rope_theta_tgt, stream);
 }
 
+int helm_kv_cosine(const void* k_mapped, const void* v_mapped, const void* k_ref, const void* v_ref,
+                   float* cos_out, const helm_shape_t* s) {
+  clear_error();
+  if (!s) return fail(HELM_E_INVALID_ARG, "shape is NULL");
+  int rc = check_common(common_of(s));
+  if (rc != HELM_OK) return rc;
+  if (s->n_tokens < 0) return fail(HELM_E_INVALID_ARG, "n_tokens = %lld < 0", (long long)s->n_tokens);
+  if (s->n_tokens > 0x7fffffffLL) return fail(HELM_E_INVALID_ARG, "n_tokens exceeds 2^31-1");
+  if (!cos_out) return fail(HELM_E_INVALID_ARG, "cos_out is NULL");
+  if (s->n_tokens > 0 && (!k_mapped || !v_mapped || !k_ref || !v_ref))
+    return fail(HELM_E_INVALID_ARG, "a cache pointer is NULL");
+  const int64_t es = (int64_t)elem_bytes(s->dtype);
+  int64_t slab = s->n_tokens, cache_b = s->n_tgt_layers;
+  if (!mul_ok(slab, s->head_dim) || !mul_ok(cache_b, s->n_kv_heads) || !mul_ok(cache_b, slab) ||
+      !mul_ok(cache_b, es))
+    return fail(HELM_E_INVALID_ARG, "cache sizes overflow int64");
+  const int64_t n_slabs = (int64_t)s->n_tgt_layers * s->n_kv_heads;
+  const int64_t out_b = 2 * n_slabs * (int64_t)sizeof(float);
+  const struct { const void* p; const char* name; } ins[] = {
+      {k_mapped, "k_mapped"}, {v_mapped, "v_mapped"}, {k_ref, "k_ref"}, {v_ref, "v_ref"}};
+  for (const auto& in : ins)
+    if (overlaps(cos_out, out_b, in.p, cache_b)) return fail(HELM_E_ALIAS, "cos_out overlaps %s", in.name);
+  rc = device_gate(-1);
+  if (rc != HELM_OK) return rc;
+  return launch_status(helm::launch_kv_cosine(k_mapped, v_mapped, k_ref, v_ref, n_slabs, slab,
+                                              s->dtype == HELM_BF16 ? helm::Dtype::BF16 : helm::Dtype::F32,
+                                              cos_out, (hipStream_t)s->stream),
+                       "KV-cosine kernel launch");
+}
+
 }  // extern "C"

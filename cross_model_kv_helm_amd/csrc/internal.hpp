@@ -69,6 +69,12 @@ hipError_t launch_paged_rows(const int32_t* cu_seqlens, int32_t n_requests,
 // Portable transfer kernel: fp32 vector arithmetic, any supported D/k/dtype.
 hipError_t launch_transfer_generic(const XferArgs& a, Dtype dt, hipStream_t stream);
 
+// KV-cosine diagnostic: out[kv * n_slabs + s] = cosine of slab s of the
+// mapped and the reference cache (kv = 0 keys, 1 values), slabs of
+// slab_elems values each.
+hipError_t launch_kv_cosine(const void* k_a, const void* v_a, const void* k_b, const void* v_b, int64_t n_slabs,
+                            int64_t slab_elems, Dtype dt, float* out, hipStream_t stream);
+
 // Matrix-core transfer kernel for bf16 storage.  Returns hipErrorNotSupported
 // (and enqueues nothing) when the shape is outside what it handles.
 hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream);

@@ -197,6 +197,28 @@ int helm_kv_transfer_paged(const void* src_k_pool, const void* src_v_pool,
                            void* tgt_k_pool, void* tgt_v_pool,
                            const helm_paged_shape_t* shape);
 
+/* KV-cosine diagnostic ("Helm Intelligent Routing", the retention / KL /
+ * KV-cosine table: how close the mapped cache is to the target model's
+ * own; a low cosine with low retention means the map is wrong).  For every
+ * target layer l and head h, and for keys and for values, the cosine of the
+ * two [T, D] slabs taken as flat vectors:
+ *   cos_out[kv][l][h] = sum(a*b) / (sqrt(sum(a*a)) * sqrt(sum(b*b)))
+ * with a from the mapped cache (k_mapped / v_mapped, e.g. out_k / out_v of
+ * helm_kv_transfer) and b from the reference cache (k_ref / v_ref, e.g. the
+ * target model's own prefill), kv = 0 for keys and 1 for values.  A slab of
+ * zeros gives NaN (0/0); with n_tokens = 0 every entry is NaN.
+ *   caches : [L_t, H, T, D] contiguous, shape->dtype, device memory
+ *   cos_out: [2, L_t, H] float32, device memory, caller-owned; must not
+ *            overlap a cache
+ * Uses shape->n_tgt_layers, n_kv_heads, n_tokens, head_dim, dtype and stream
+ * (the other fields must still pass the transfer's checks; no workspace).
+ * Sums are accumulated in fp64 (fp32 within each 16-byte piece).  Enqueued
+ * asynchronously on shape->stream; same return convention as
+ * helm_kv_transfer (nothing enqueued on an error). */
+int helm_kv_cosine(const void* k_mapped, const void* v_mapped,
+                   const void* k_ref, const void* v_ref,
+                   float* cos_out, const helm_shape_t* shape);
+
 /* Workspace bytes the call with this shape needs (0 on an invalid shape;
  * helm_last_error() then says why).  Pure host arithmetic. */
 size_t helm_kv_workspace_bytes(const helm_shape_t* shape);

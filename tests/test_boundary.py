@@ -183,3 +183,23 @@ def _gpu_present():
 def test_no_device():
     assert hk.helm_device_check(-1) == 4
     assert hk.helm_device_check(0) == 4
+
+
+def test_kv_cosine_refusals_before_any_device_access():
+    """helm_kv_cosine: argument errors are reported without touching a
+    device: no shape, no output, a NULL cache with tokens, an output that
+    overlaps a cache, an invalid shape field."""
+    L = hk.lib()
+    s = shape(n_tokens=64)
+    caches = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(4)]
+    out = ctypes.c_void_p(0x70000000)
+    assert L.helm_kv_cosine(*caches, out, None) == 1
+    assert L.helm_kv_cosine(*caches, None, ctypes.byref(s)) == 1
+    assert "cos_out" in hk.helm_last_error()
+    assert L.helm_kv_cosine(caches[0], None, caches[2], caches[3], out, ctypes.byref(s)) == 1
+    # cache bytes: 64 layers * 8 heads * 64 tokens * 128 * 2 = 8 MiB; an output inside k_ref overlaps it
+    inside = ctypes.c_void_p(0x30000000 + 4096)
+    assert L.helm_kv_cosine(*caches, inside, ctypes.byref(s)) == 8
+    assert "overlaps k_ref" in hk.helm_last_error()
+    assert L.helm_kv_cosine(*caches, out, ctypes.byref(shape(n_tokens=64, head_dim=96))) == 2
+    assert L.helm_kv_cosine(*caches, out, ctypes.byref(shape(n_tokens=-1))) == 1
