@@ -18,6 +18,11 @@ enough, suffices", its fit/map listing and its strip/map/apply diagram):
 with R the rotate-half RoPE rotation.  In ``quantize_content`` mode x_k is
 rounded once to the storage dtype before the product.
 
+``transfer_wide_rows`` is the wide-input map (the Qwen3 write-up's full
+mapper): x concatenates the K (un-rotated) and V features of all heads of the
+k selected source layers, IN = k*2*H*D, one (IN, D) map per target head and
+K|V.
+
 ``kv_cosine`` is the KV-cosine diagnostic ("Helm Intelligent Routing", the
 retention / KL / KV-cosine table): per (layer, head) slab, the cosine of a
 mapped cache and a reference cache taken as flat vectors, in fp64.
@@ -315,3 +320,56 @@ def kv_cosine(a, b, dtype: int, n_threads: int = 0) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_kv_cosine: invalid arguments")
     return out.reshape(lead)
+
+
+def wide_in(k: int, H: int, D: int) -> int:
+    """Input width of the wide-input map: k layers x {K, V} x H heads x D."""
+    return k * 2 * H * D
+
+
+def transfer_wide_rows(pb: Problem, src_k, src_v, src_pos, tgt_pos, layer_sel,
+                       W_k, b_k, W_v, b_v, rows=None):
+    """Wide-input transfer (the Qwen3 write-up's full mapper: x concatenates
+    the K and V features of all heads of the k selected source layers) for
+    the given flat rows ((l*H + h)*T + t), or all.  W_k / W_v are
+    [L_t, H, k*2*H*D, D]; feature order (j, K|V, source head, d), keys
+    un-rotated.  Returns fp64 (out_k, out_v) like ``transfer_rows``."""
+    for a, n in ((src_k, "src_k"), (src_v, "src_v"), (W_k, "W_k"), (W_v, "W_v")):
+        _check_data(a, pb.dtype, n)
+    src_pos = np.ascontiguousarray(src_pos, dtype=np.int32)
+    tgt_pos = np.ascontiguousarray(tgt_pos, dtype=np.int32)
+    layer_sel = np.ascontiguousarray(layer_sel, dtype=np.int32)
+    b_k = np.ascontiguousarray(b_k, dtype=np.float32)
+    b_v = np.ascontiguousarray(b_v, dtype=np.float32)
+    D = pb.head_dim
+    IN = wide_in(pb.k, pb.n_kv_heads, D)
+    for a, n in ((W_k, "W_k"), (W_v, "W_v")):
+        if a.shape != (pb.n_tgt_layers, pb.n_kv_heads, IN, D):
+            raise ValueError(f"{n} must be [L_t, H, {IN}, D], got {a.shape}")
+    L = lib()
+    if not hasattr(L, "_wide_set"):
+        vp, i64p, dp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)
+        L.oracle_transfer_wide_rows.restype = ctypes.c_int
+        L.oracle_transfer_wide_rows.argtypes = [ctypes.POINTER(_Problem)] + [vp] * 9 + [ctypes.c_int64, i64p, dp, dp]
+        L._wide_set = True
+    if rows is None:
+        n = pb.n_tgt_layers * pb.n_kv_heads * pb.n_tokens
+        rows_p = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows.size
+        rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    out_k = np.empty((n, D), dtype=np.float64)
+    out_v = np.empty((n, D), dtype=np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    c = pb._c()
+    rc = L.oracle_transfer_wide_rows(
+        ctypes.byref(c), _ptr(src_k), _ptr(src_v), _ptr(src_pos), _ptr(tgt_pos),
+        _ptr(layer_sel), _ptr(np.ascontiguousarray(W_k)), _ptr(b_k), _ptr(np.ascontiguousarray(W_v)), _ptr(b_v),
+        n, rows_p, out_k.ctypes.data_as(dp), out_v.ctypes.data_as(dp))
+    if rc != 0:
+        raise ValueError("oracle_transfer_wide_rows: invalid arguments")
+    if rows is None:
+        shape = (pb.n_tgt_layers, pb.n_kv_heads, pb.n_tokens, D)
+        return out_k.reshape(shape), out_v.reshape(shape)
+    return out_k, out_v

@@ -266,6 +266,104 @@ int oracle_transfer_rows(const oracle_problem* pb,
 }
 
 /* ------------------------------------------------------------------ */
+/* Wide-input map                                                       */
+/* ------------------------------------------------------------------ */
+
+/* The Qwen3 cache-mapping write-up, section "A linear bridge, strangely
+ * enough, suffices": the full mapper's x concatenates the KV features of all
+ * selected source layers, and every target head has its own fits (one for
+ * keys, one for values); its parameter count (about 1.07 B for 14B -> 32B)
+ * is 64 layers x 8 heads x {K, V} x (IN*128 + 128) with IN = 8192 =
+ * k x {K, V} x H x D.  Readings (the text gives no order):
+ *   x[((j*2 + kv)*H + g)*D + d] = kv == 0 ? (R(-src_pos[t]) src_k[sel_j, g, t, :])[d]
+ *                                         : src_v[sel_j, g, t, d]
+ * with sel_j = layer_sel[l, j] in row order, keys before values, source head
+ * g, dimension d; keys are un-rotated (and, in quantize_content mode, rounded
+ * once to the storage dtype) exactly as in the per-head map.  Then
+ *   out_k[l, h, t, :] = R(+tgt_pos[t]) (x @ W_k[l, h] + b_k[l, h])
+ *   out_v[l, h, t, :] = x @ W_v[l, h] + b_v[l, h]
+ * with W_* [L_t, H, IN, D] in-major and b_* [L_t, H, D].
+ * rows: flat indices (l*H + h)*T + t (NULL = all, in order); out_k / out_v:
+ * [n_rows, D] fp64.  Returns 0, or 1 on a bad argument. */
+int oracle_transfer_wide_rows(const oracle_problem* pb,
+                              const void* src_k, const void* src_v,
+                              const int32_t* src_pos, const int32_t* tgt_pos,
+                              const int32_t* layer_sel,
+                              const void* W_k, const float* b_k,
+                              const void* W_v, const float* b_v,
+                              int64_t n_rows, const int64_t* rows,
+                              double* out_k, double* out_v) {
+  if (check_problem(pb) || pb->n_tokens <= 0) return 1;
+  const int64_t T = pb->n_tokens, H = pb->n_kv_heads, D = pb->head_dim;
+  const int32_t k = pb->k;
+  const int64_t IN = (int64_t)k * 2 * H * D;
+  const int64_t total = (int64_t)pb->n_tgt_layers * H * T;
+  if (!rows) n_rows = total;
+  for (int64_t j = 0; j < (int64_t)pb->n_tgt_layers * k; ++j)
+    if (layer_sel[j] < 0 || layer_sel[j] >= pb->n_src_layers) return 1;
+  if (rows)
+    for (int64_t r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= total) return 1;
+  const size_t wbytes = pb->dtype == ORACLE_BF16 ? 2 : 4;
+
+  set_threads(pb);
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)(IN + 3 * D));
+    if (!x) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+      double* u = x + IN;     /* [D] staging */
+      double* yk = u + D;     /* [D] */
+      double* yv = yk + D;    /* [D] */
+#pragma omp for schedule(static)
+      for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t flat = rows ? rows[r] : r;
+        const int64_t t = flat % T;
+        const int64_t h = (flat / T) % H;
+        const int64_t l = flat / (T * H);
+        /* gather: layer j, then keys (un-rotated) before values, then head g */
+        for (int32_t j = 0; j < k; ++j) {
+          const int64_t s = layer_sel[l * k + j];
+          for (int64_t g = 0; g < H; ++g) {
+            const int64_t src = ((s * H + g) * T + t) * D;
+            double* xk = x + ((int64_t)(j * 2 + 0) * H + g) * D;
+            double* xv = x + ((int64_t)(j * 2 + 1) * H + g) * D;
+            for (int64_t d = 0; d < D; ++d) {
+              u[d] = load_elem(src_k, pb->dtype, src + d);
+              xv[d] = load_elem(src_v, pb->dtype, src + d);
+            }
+            oracle_rope(u, xk, (int32_t)D, -(double)src_pos[t], pb->theta_src);
+            if (pb->quantize_content)
+              for (int64_t d = 0; d < D; ++d) xk[d] = round_to_dtype(xk[d], pb->dtype);
+          }
+        }
+        const int64_t grp = l * H + h;
+        const char* wk = (const char*)W_k + (size_t)grp * (size_t)(IN * D) * wbytes;
+        const char* wv = (const char*)W_v + (size_t)grp * (size_t)(IN * D) * wbytes;
+        for (int64_t n = 0; n < D; ++n) {
+          yk[n] = (double)b_k[grp * D + n];
+          yv[n] = (double)b_v[grp * D + n];
+        }
+        for (int64_t m = 0; m < IN; ++m) {
+          const double a = x[m];
+          for (int64_t n = 0; n < D; ++n) {
+            yk[n] += a * load_elem(wk, pb->dtype, m * D + n);
+            yv[n] += a * load_elem(wv, pb->dtype, m * D + n);
+          }
+        }
+        oracle_rope(yk, out_k + r * D, (int32_t)D, (double)tgt_pos[t], pb->theta_tgt);
+        for (int64_t n = 0; n < D; ++n) out_v[r * D + n] = yv[n];
+      }
+    }
+    free(x);
+  }
+  return bad;
+}
+
+/* ------------------------------------------------------------------ */
 /* Paged layout: pools [L, n_blocks, block_size, H, D]; block tables    */
 /* [R, max_blocks]; cu_seqlens [R+1]; positions [N] over packed tokens. */
 /* Token t of request r sits in slot t % block_size of logical page     */

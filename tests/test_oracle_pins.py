@@ -557,3 +557,113 @@ def test_kv_cosine_bf16_storage_and_zero_slab(oracle_mod):
                                   oracle_mod.kv_cosine(x, y, F32))
     z = np.zeros_like(x)
     assert np.all(np.isnan(oracle_mod.kv_cosine(z, y, F32)))
+
+
+# ---------------------------------------------------------------- wide-input map
+# The Qwen3 write-up's full mapper: x concatenates the K and V features of all
+# heads of the selected source layers; one fit per target head for keys and
+# one for values.  Reading of the feature order: (layer j in layer_sel row
+# order, keys then values, source head g, dimension d).
+def run_wide(oracle_mod, L_s, L_t, H, D, T, k, case, src_pos, tgt_pos, theta_s=1e4, theta_t=1e4,
+             dtype=F32, quantize=False):
+    pb = oracle_mod.Problem(L_s, L_t, H, D, k, n_tokens=T, theta_src=theta_s, theta_tgt=theta_t,
+                            dtype=dtype, quantize_content=quantize)
+    return oracle_mod.transfer_wide_rows(pb, case["src_k"], case["src_v"], src_pos, tgt_pos,
+                                         case["layer_sel"], case["W_k"], case["b_k"], case["W_v"], case["b_v"])
+
+
+@pytest.mark.parametrize("dtype,quantize", [(F32, False), (BF16, True)])
+def test_wide_map_reduces_to_per_head_map(oracle_mod, dtype, quantize):
+    """A wide W that is zero outside the target head's own keys (for W_k) and
+    own values (for W_v) gives exactly the per-head transfer: pins the key and
+    value blocks of the feature order, the per-head un-rotation (and its
+    rounding in quantize_content mode) and the re-rotation against the
+    (already pinned) per-head oracle."""
+    L_s, L_t, H, D, T, k = 5, 3, 3, 8, 7, 2
+    rng = np.random.default_rng(41)
+    case = random_case(rng, L_s, L_t, H, D, T, k, dtype=dtype)
+    IN = oracle_mod.wide_in(k, H, D)
+    Wk = np.zeros((L_t, H, IN, D), case["W_k"].dtype)
+    Wv = np.zeros((L_t, H, IN, D), case["W_v"].dtype)
+    for l in range(L_t):
+        for h in range(H):
+            for j in range(k):
+                Wk[l, h, ((j * 2 + 0) * H + h) * D:((j * 2 + 0) * H + h + 1) * D] = case["W_k"][l, h, j * D:(j + 1) * D]
+                Wv[l, h, ((j * 2 + 1) * H + h) * D:((j * 2 + 1) * H + h + 1) * D] = case["W_v"][l, h, j * D:(j + 1) * D]
+    wide = dict(case, W_k=Wk, W_v=Wv)
+    src = rng.integers(-500, 5000, T).astype(np.int32)
+    tgt = rng.integers(0, 90000, T).astype(np.int32)
+    nk, nv = run(oracle_mod, L_s, L_t, H, D, T, k, case, src, tgt, theta_s=1e4, theta_t=5e5, dtype=dtype,
+                 quantize=quantize)
+    wk, wv = run_wide(oracle_mod, L_s, L_t, H, D, T, k, wide, src, tgt, theta_s=1e4, theta_t=5e5, dtype=dtype,
+                      quantize=quantize)
+    np.testing.assert_allclose(wk, nk, atol=1e-12)
+    np.testing.assert_allclose(wv, nv, atol=1e-12)
+
+
+def test_wide_map_one_hot_features(oracle_mod):
+    """One-hot W columns pick single features: for target (l, h), output
+    column n of the value map equals feature m of x, which must be the key of
+    source head g of layer layer_sel[l, j] un-rotated at src_pos (kv = 0) or
+    that head's value as stored (kv = 1); the key map's output is the same
+    feature re-rotated at tgt_pos.  Catches a transposed (g, kv) order, a
+    rotated value, a missing un-rotation, features taken from the target head
+    instead of the source head."""
+    L_s, L_t, H, D, T, k = 4, 2, 2, 4, 5, 2
+    rng = np.random.default_rng(42)
+    case = random_case(rng, L_s, L_t, H, D, T, k)
+    case["layer_sel"] = np.array([[3, 1], [0, 2]], np.int32)
+    case["b_k"][:] = 0
+    case["b_v"][:] = 0
+    IN = oracle_mod.wide_in(k, H, D)
+    src = rng.integers(0, 300, T).astype(np.int32)
+    tgt = rng.integers(0, 300, T).astype(np.int32)
+    for (j, kv, g, d, n) in [(0, 0, 1, 2, 1), (1, 1, 0, 3, 0), (1, 0, 0, 0, 3), (0, 1, 1, 1, 2)]:
+        m = ((j * 2 + kv) * H + g) * D + d
+        W = np.zeros((L_t, H, IN, D), np.float32)
+        W[:, :, m, n] = 1.0
+        ok, ov = run_wide(oracle_mod, L_s, L_t, H, D, T, k, dict(case, W_k=W, W_v=W), src, tgt)
+        for l in range(L_t):
+            s = case["layer_sel"][l, j]
+            for t in range(T):
+                if kv == 0:
+                    feat = rope_complex(case["src_k"][s, g, t].astype(np.float64), -src[t], 1e4)[d]
+                else:
+                    feat = float(case["src_v"][s, g, t, d])
+                y = np.zeros(D)
+                y[n] = feat
+                for h in range(H):
+                    np.testing.assert_allclose(ov[l, h, t], y, atol=1e-12)
+                    np.testing.assert_allclose(ok[l, h, t], rope_complex(y, tgt[t], 1e4), atol=1e-12)
+
+
+def test_wide_map_brute_force(oracle_mod):
+    """Pure-Python loops (math.fsum dot products, complex-number RoPE) on a
+    tiny wide case with random W and bias."""
+    L_s, L_t, H, D, T, k = 3, 2, 2, 4, 3, 2
+    rng = np.random.default_rng(43)
+    case = random_case(rng, L_s, L_t, H, D, T, k)
+    IN = oracle_mod.wide_in(k, H, D)
+    case["W_k"] = (rng.standard_normal((L_t, H, IN, D)) / math.sqrt(IN)).astype(np.float32)
+    case["W_v"] = (rng.standard_normal((L_t, H, IN, D)) / math.sqrt(IN)).astype(np.float32)
+    src = rng.integers(0, 1000, T).astype(np.int32)
+    tgt = rng.integers(0, 1000, T).astype(np.int32)
+    ok, ov = run_wide(oracle_mod, L_s, L_t, H, D, T, k, case, src, tgt)
+    for l in range(L_t):
+        for t in range(T):
+            x = []
+            for j in range(k):
+                s = int(case["layer_sel"][l, j])
+                for kv in range(2):
+                    for g in range(H):
+                        if kv == 0:
+                            x += list(rope_complex(case["src_k"][s, g, t].astype(np.float64), -int(src[t]), 1e4))
+                        else:
+                            x += [float(v) for v in case["src_v"][s, g, t]]
+            for h in range(H):
+                yk = [math.fsum(x[m] * float(case["W_k"][l, h, m, n]) for m in range(IN)) + float(case["b_k"][l, h, n])
+                      for n in range(D)]
+                yv = [math.fsum(x[m] * float(case["W_v"][l, h, m, n]) for m in range(IN)) + float(case["b_v"][l, h, n])
+                      for n in range(D)]
+                np.testing.assert_allclose(ov[l, h, t], yv, atol=1e-12)
+                np.testing.assert_allclose(ok[l, h, t], rope_complex(np.array(yk), int(tgt[t]), 1e4), atol=1e-12)
