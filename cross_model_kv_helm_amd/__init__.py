@@ -26,7 +26,7 @@ STATUS = {0: "HELM_OK", 1: "HELM_E_INVALID_ARG", 2: "HELM_E_PAIR_SHAPE", 3: "HEL
 HELM_STAGE_TABLES, HELM_STAGE_MAP, HELM_STAGE_ALL = 1, 2, 3
 
 EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_stage", "helm_kv_transfer_paged", "helm_kv_cosine",
-            "helm_kv_workspace_bytes",
+            "helm_kv_transfer_wide", "helm_kv_wide_workspace_bytes", "helm_kv_workspace_bytes",
             "helm_kv_paged_workspace_bytes", "helm_mapper_check", "helm_paged_check",
             "helm_device_check", "helm_arch_supported", "helm_last_error", "helm_status_string",
             "helm_abi_version")
@@ -81,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.helm_kv_transfer.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
         L.helm_kv_transfer_stage.argtypes = [ctypes.c_int] + [vp] * 11 + [ctypes.POINTER(HelmShape)]
         L.helm_kv_transfer_stage.restype = ctypes.c_int
+        L.helm_kv_transfer_wide.restype = ctypes.c_int
+        L.helm_kv_transfer_wide.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
+        L.helm_kv_wide_workspace_bytes.restype = ctypes.c_size_t
+        L.helm_kv_wide_workspace_bytes.argtypes = [ctypes.POINTER(HelmShape)]
         L.helm_kv_cosine.restype = ctypes.c_int
         L.helm_kv_cosine.argtypes = [vp] * 5 + [ctypes.POINTER(HelmShape)]
         L.helm_kv_transfer_paged.restype = ctypes.c_int
@@ -249,6 +253,43 @@ def helm_kv_transfer_stage(stages: int, src_k, src_v, src_pos, tgt_pos, layer_se
     shape.workspace = workspace.data_ptr()
     shape.workspace_bytes = workspace.numel()
     _raise(lib().helm_kv_transfer_stage(int(stages), *ptrs, ctypes.byref(shape)))
+
+
+def helm_kv_wide_workspace_bytes(shape: HelmShape) -> int:
+    n = int(lib().helm_kv_wide_workspace_bytes(ctypes.byref(shape)))
+    if n == 0:
+        raise HelmError(1, helm_last_error())
+    return n
+
+
+def wide_in(k: int, H: int, D: int) -> int:
+    """Input width of the wide-input map: k layers x {K, V} x H heads x D."""
+    return k * 2 * H * D
+
+
+def helm_kv_transfer_wide(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v,
+                          shape: HelmShape, workspace=None) -> None:
+    """The wide-input map (see include/helm_kv.h): W_k, W_v [L_t, H, k*2*H*D, D] bf16."""
+    import torch
+    L_s, L_t, H, D, k, T = (shape.n_src_layers, shape.n_tgt_layers, shape.n_kv_heads,
+                            shape.head_dim, shape.k, shape.n_tokens)
+    IN = wide_in(k, H, D)
+    dt = torch.bfloat16
+    ptrs = [
+        _dev_ptr(src_k, "src_k", dt, (L_s, H, T, D)), _dev_ptr(src_v, "src_v", dt, (L_s, H, T, D)),
+        _dev_ptr(src_pos, "src_pos", torch.int32, (T,)), _dev_ptr(tgt_pos, "tgt_pos", torch.int32, (T,)),
+        _dev_ptr(layer_sel, "layer_sel", torch.int32, (L_t, k)),
+        _dev_ptr(W_k, "W_k", dt, (L_t, H, IN, D)), _dev_ptr(b_k, "b_k", torch.float32, (L_t, H, D)),
+        _dev_ptr(W_v, "W_v", dt, (L_t, H, IN, D)), _dev_ptr(b_v, "b_v", torch.float32, (L_t, H, D)),
+        _dev_ptr(out_k, "out_k", dt, (L_t, H, T, D)), _dev_ptr(out_v, "out_v", dt, (L_t, H, T, D)),
+    ]
+    if not shape.stream:
+        shape.stream = current_stream_ptr(src_k.device)
+    if workspace is None:
+        workspace = torch.empty(helm_kv_wide_workspace_bytes(shape), dtype=torch.uint8, device=src_k.device)
+    shape.workspace = workspace.data_ptr()
+    shape.workspace_bytes = workspace.numel()
+    _raise(lib().helm_kv_transfer_wide(*ptrs, ctypes.byref(shape)))
 
 
 def helm_kv_cosine(k_mapped, v_mapped, k_ref, v_ref, shape: HelmShape, out=None):

@@ -435,6 +435,111 @@ int helm_kv_transfer_paged(const void* src_k_pool, const void* src_v_pool, const
   return run_transfer(a, s->dtype, src_pos, tgt_pos, s->rope_theta_src, s->rope_theta_tgt, stream);
 }
 
+// Wide-input map workspace: [rope_src][rope_tgt] (K1 tables) [U: L_s*H*T*D bf16]
+// [WT_k: L_t*H*D*IN bf16][WT_v: same].
+struct WideWorkspace {
+  size_t rope_bytes = 0, u_bytes = 0, wt_bytes = 0, total = 0;
+};
+
+static bool wide_workspace_layout(const helm_shape_t* s, WideWorkspace& w) {
+  Workspace base;
+  if (!workspace_layout(s->n_tokens, s->head_dim, false, base)) return false;
+  int64_t u = s->n_src_layers, wt = s->n_tgt_layers;
+  const int64_t IN = helm::wide_in_features(s->k, s->n_kv_heads, s->head_dim);
+  if (!mul_ok(u, s->n_kv_heads) || !mul_ok(u, s->n_tokens) || !mul_ok(u, s->head_dim) || !mul_ok(u, 2) ||
+      !mul_ok(wt, s->n_kv_heads) || !mul_ok(wt, s->head_dim) || !mul_ok(wt, IN) || !mul_ok(wt, 2))
+    return false;
+  w.rope_bytes = base.rope_bytes;
+  w.u_bytes = align_up((size_t)u);
+  w.wt_bytes = align_up((size_t)wt);
+  w.total = 2 * w.rope_bytes + w.u_bytes + 2 * w.wt_bytes;
+  if (w.total == 0) w.total = kAlign;
+  return true;
+}
+
+static int check_wide_shape(const helm_shape_t* s) {
+  if (!s) return fail(HELM_E_INVALID_ARG, "shape is NULL");
+  int rc = check_common(common_of(s));
+  if (rc != HELM_OK) return rc;
+  if (s->dtype != HELM_BF16) return fail(HELM_E_DTYPE, "the wide-input map runs on bf16 caches and maps only");
+  if (s->head_dim != 128) return fail(HELM_E_PAIR_SHAPE, "the wide-input map needs head_dim 128 (got %d)", s->head_dim);
+  if (s->n_tokens < 0) return fail(HELM_E_INVALID_ARG, "n_tokens = %lld < 0", (long long)s->n_tokens);
+  if (s->n_tokens > 0x7fffffffLL) return fail(HELM_E_INVALID_ARG, "n_tokens exceeds 2^31-1");
+  return HELM_OK;
+}
+
+size_t helm_kv_wide_workspace_bytes(const helm_shape_t* s) {
+  clear_error();
+  if (check_wide_shape(s) != HELM_OK) return 0;
+  WideWorkspace w;
+  if (!wide_workspace_layout(s, w)) { fail(HELM_E_INVALID_ARG, "size overflow"); return 0; }
+  return w.total;
+}
+
+int helm_kv_transfer_wide(const void* src_k, const void* src_v, const int32_t* src_pos, const int32_t* tgt_pos,
+                          const int32_t* layer_sel, const void* W_k, const float* b_k, const void* W_v,
+                          const float* b_v, void* out_k, void* out_v, const helm_shape_t* s) {
+  clear_error();
+  int rc = check_wide_shape(s);
+  if (rc != HELM_OK) return rc;
+  if (s->n_tokens == 0) return HELM_OK;   // nothing to map; no pointer or device is touched
+  if (!src_k || !src_v || !src_pos || !tgt_pos || !layer_sel || !W_k || !b_k || !W_v || !b_v || !out_k ||
+      !out_v)
+    return fail(HELM_E_INVALID_ARG, "a tensor pointer is NULL");
+  const int64_t IN = helm::wide_in_features(s->k, s->n_kv_heads, s->head_dim);
+  int64_t src_b = s->n_src_layers, out_b = s->n_tgt_layers, w_b = s->n_tgt_layers, b_b = s->n_tgt_layers;
+  if (!mul_ok(src_b, s->n_kv_heads) || !mul_ok(src_b, s->n_tokens) || !mul_ok(src_b, s->head_dim * 2) ||
+      !mul_ok(out_b, s->n_kv_heads) || !mul_ok(out_b, s->n_tokens) || !mul_ok(out_b, s->head_dim * 2) ||
+      !mul_ok(w_b, s->n_kv_heads) || !mul_ok(w_b, IN) || !mul_ok(w_b, s->head_dim * 2) ||
+      !mul_ok(b_b, s->n_kv_heads) || !mul_ok(b_b, (int64_t)s->head_dim * 4))
+    return fail(HELM_E_INVALID_ARG, "tensor sizes overflow int64");
+  const int64_t pos_b = s->n_tokens * 4, sel_b = (int64_t)s->n_tgt_layers * s->k * 4;
+  const struct { const void* p; int64_t n; const char* name; } ins[] = {
+      {src_k, src_b, "src_k"}, {src_v, src_b, "src_v"}, {src_pos, pos_b, "src_pos"},
+      {tgt_pos, pos_b, "tgt_pos"}, {layer_sel, sel_b, "layer_sel"}, {W_k, w_b, "W_k"},
+      {b_k, b_b, "b_k"}, {W_v, w_b, "W_v"}, {b_v, b_b, "b_v"}};
+  for (const auto& in : ins) {
+    if (overlaps(out_k, out_b, in.p, in.n)) return fail(HELM_E_ALIAS, "out_k overlaps %s", in.name);
+    if (overlaps(out_v, out_b, in.p, in.n)) return fail(HELM_E_ALIAS, "out_v overlaps %s", in.name);
+  }
+  if (overlaps(out_k, out_b, out_v, out_b)) return fail(HELM_E_ALIAS, "out_k overlaps out_v");
+  WideWorkspace w;
+  if (!wide_workspace_layout(s, w)) return fail(HELM_E_INVALID_ARG, "size overflow");
+  if (!s->workspace || s->workspace_bytes < w.total)
+    return fail(HELM_E_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", s->workspace_bytes,
+                s->workspace, w.total);
+  if ((uintptr_t)s->workspace % kAlign)
+    return fail(HELM_E_WORKSPACE, "workspace %p is not %zu-byte aligned", s->workspace, kAlign);
+  for (const auto& in : ins)
+    if (overlaps(s->workspace, (int64_t)w.total, in.p, in.n))
+      return fail(HELM_E_ALIAS, "workspace overlaps %s", in.name);
+  if (overlaps(s->workspace, (int64_t)w.total, out_k, out_b) || overlaps(s->workspace, (int64_t)w.total, out_v, out_b))
+    return fail(HELM_E_ALIAS, "workspace overlaps an output");
+
+  char* ws = (char*)s->workspace;
+  helm::WideXfer x{};
+  x.src_k = src_k; x.src_v = src_v; x.layer_sel = layer_sel;
+  x.W_k = W_k; x.b_k = b_k; x.W_v = W_v; x.b_v = b_v; x.out_k = out_k; x.out_v = out_v;
+  x.rope_src = (const float2*)ws;
+  x.rope_tgt = (const float2*)(ws + w.rope_bytes);
+  x.U = (uint16_t*)(ws + 2 * w.rope_bytes);
+  x.WT_k = (uint16_t*)(ws + 2 * w.rope_bytes + w.u_bytes);
+  x.WT_v = (uint16_t*)(ws + 2 * w.rope_bytes + w.u_bytes + w.wt_bytes);
+  x.L_s = s->n_src_layers; x.L_t = s->n_tgt_layers; x.H = s->n_kv_heads; x.D = s->head_dim; x.k = s->k;
+  x.T = (int32_t)s->n_tokens;
+  if (!helm::wide_supports(x))
+    return fail(HELM_E_INVALID_ARG, "the wide-input map needs 16-byte aligned caches and a cache slab below 4 GB");
+  rc = device_gate(-1);
+  if (rc != HELM_OK) return rc;
+  const hipStream_t stream = (hipStream_t)s->stream;
+  rc = launch_status(helm::launch_rope_tables(src_pos, tgt_pos, s->n_tokens, s->head_dim, s->rope_theta_src,
+                                              s->rope_theta_tgt, const_cast<float2*>(x.rope_src),
+                                              const_cast<float2*>(x.rope_tgt), stream),
+                     "RoPE table kernel launch");
+  if (rc != HELM_OK) return rc;
+  return launch_status(helm::launch_wide(x, stream), "wide-input map launch");
+}
+
 int helm_kv_cosine(const void* k_mapped, const void* v_mapped, const void* k_ref, const void* v_ref,
                    float* cos_out, const helm_shape_t* s) {
   clear_error();

@@ -75,6 +75,31 @@ hipError_t launch_transfer_generic(const XferArgs& a, Dtype dt, hipStream_t stre
 hipError_t launch_kv_cosine(const void* k_a, const void* v_a, const void* k_b, const void* v_b, int64_t n_slabs,
                             int64_t slab_elems, Dtype dt, float* out, hipStream_t stream);
 
+// Wide-input map (bf16, head_dim 128): x = the K (un-rotated) and V features
+// of all heads of the k selected source layers, IN = k*2*H*D; one (IN, D) map
+// per target head and K|V.  U, WT_k, WT_v are workspace: the un-rotated keys
+// [L_s, H, T, D] and the transposed maps [L_t, H, D, IN].
+struct WideXfer {
+  const void* src_k;
+  const void* src_v;
+  const int32_t* layer_sel;   // [L_t, k]
+  const void* W_k;            // [L_t, H, IN, D]
+  const float* b_k;           // [L_t, H, D]
+  const void* W_v;
+  const float* b_v;
+  void* out_k;                // [L_t, H, T, D]
+  void* out_v;
+  const float2* rope_src;     // K1 tables (rope_index layout)
+  const float2* rope_tgt;
+  uint16_t* U;
+  uint16_t* WT_k;
+  uint16_t* WT_v;
+  int32_t L_s, L_t, H, D, k, T;
+};
+int64_t wide_in_features(int32_t k, int32_t H, int32_t D);
+bool wide_supports(const WideXfer& x);
+hipError_t launch_wide(const WideXfer& x, hipStream_t stream);
+
 // Matrix-core transfer kernel for bf16 storage.  Returns hipErrorNotSupported
 // (and enqueues nothing) when the shape is outside what it handles.
 hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream);

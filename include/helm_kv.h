@@ -197,6 +197,37 @@ int helm_kv_transfer_paged(const void* src_k_pool, const void* src_v_pool,
                            void* tgt_k_pool, void* tgt_v_pool,
                            const helm_paged_shape_t* shape);
 
+/* The wide-input map (the Qwen3 cache-mapping write-up, section "A linear
+ * bridge, strangely enough, suffices": the full mapper's x concatenates the
+ * KV features of all selected source layers, with one fit per target head
+ * for keys and one for values).  Per target layer l and token t:
+ *   x[((j*2 + kv)*H + g)*D + d] = kv == 0 ? (R(-src_pos[t]) src_k[sel_j, g, t, :])[d]
+ *                                         : src_v[sel_j, g, t, d]
+ * (j in layer_sel row order, keys before values, source head g; IN =
+ * k*2*H*D features), and for every target head h
+ *   out_k[l, h, t, :] = R(+tgt_pos[t]) (x W_k[l, h] + b_k[l, h])
+ *   out_v[l, h, t, :] = x W_v[l, h] + b_v[l, h].
+ * The un-rotated key is rounded once to bf16 (the map's operand type), as in
+ * helm_kv_transfer.  Same arguments and conventions as helm_kv_transfer,
+ * except:
+ *   W_k, W_v : [L_t, H, IN, D] bf16 (in-major)
+ *   dtype    : HELM_BF16 only (HELM_E_DTYPE otherwise); head_dim 128 only
+ *              (HELM_E_PAIR_SHAPE otherwise); every tensor and the workspace
+ *              16-byte aligned (HELM_E_INVALID_ARG otherwise)
+ *   workspace: helm_kv_wide_workspace_bytes(shape) bytes, 256-byte aligned;
+ *              it holds the RoPE tables, the un-rotated source keys
+ *              [L_s, H, T, D] and both maps transposed [L_t, H, D, IN]
+ *              (C3 with IN = 8192: 4.9 GB).
+ * n_tokens = 0 enqueues nothing. */
+size_t helm_kv_wide_workspace_bytes(const helm_shape_t* shape);
+int helm_kv_transfer_wide(const void* src_k, const void* src_v,
+                          const int32_t* src_pos, const int32_t* tgt_pos,
+                          const int32_t* layer_sel,
+                          const void* W_k, const float* b_k,
+                          const void* W_v, const float* b_v,
+                          void* out_k, void* out_v,
+                          const helm_shape_t* shape);
+
 /* KV-cosine diagnostic ("Helm Intelligent Routing", the retention / KL /
  * KV-cosine table: how close the mapped cache is to the target model's
  * own; a low cosine with low retention means the map is wrong).  For every

@@ -21,6 +21,8 @@ used on, per source layer, with torch's counter-based Philox generator):
 * values        v[l, h, t, d] = z' * s_V[l, h, d], drawn like the keys;
 * maps          W ~ N(0, 1/(k*D)) (the second parameter is a variance),
   biases b ~ N(0, 0.01) (variance; std 0.1), kept in fp32;
+* wide maps     (the wide-input map, IN = k*2*H*D input features)
+  W ~ N(0, 1/IN), biases as above;
 * layer_sel[l]  k distinct source layers by a partial Fisher-Yates shuffle,
   kept in draw order (not sorted);
 * positions     per workload (see CONFIGS);
@@ -72,6 +74,9 @@ CONFIGS = {
                                           "shift4096", 401),
     "qwen3_14b_32b_t128k_gap": Workload("qwen3_14b_32b_t128k_gap", 40, 64, 8, 128, 131072, 4, "bf16", 1e6,
                                         "gap1000", 402),
+    # the wide-input map at the 14B -> 32B shape (IN = 4 x 2 x 8 x 128 = 8192)
+    "qwen3_14b_32b_t32k_wide": Workload("qwen3_14b_32b_t32k_wide", 40, 64, 8, 128, 32768, 4, "bf16", 1e6,
+                                        "same", 311),
     "paged_32req": Workload("paged_32req", 28, 28, 8, 128, 0, 4, "bf16", 1e6, "same", 501, paged=True,
                             n_requests=32),
 }
@@ -146,6 +151,26 @@ def maps(w: Workload, device):
         W.append(Wt)
     b = [torch.randn((L, H, D), generator=_gen(device, w.seed, tid), device=device) * 0.1
          for tid in (22, 23)]
+    return W[0], b[0], W[1], b[1]
+
+
+def wide_maps(w: Workload, device):
+    """Wide-input maps: W_k, W_v [L_t, H, k*2*H*D, D] (storage dtype) with
+    W ~ N(0, 1/IN), b_k, b_v [L_t, H, D] fp32 ~ N(0, 0.01)."""
+    L, H, D, k = w.n_tgt_layers, w.n_kv_heads, w.head_dim, w.k
+    IN = k * 2 * H * D
+    dt = torch_dtype(w)
+    std = 1.0 / math.sqrt(IN)
+    W = []
+    for tid in (30, 31):
+        g = _gen(device, w.seed, tid)
+        Wt = torch.empty((L, H, IN, D), dtype=dt, device=device)
+        for l in range(L):
+            for h in range(H):
+                Wt[l, h] = (torch.randn((IN, D), generator=g, device=device) * std).to(dt)
+        W.append(Wt)
+    b = [torch.randn((L, H, D), generator=_gen(device, w.seed, tid), device=device) * 0.1
+         for tid in (32, 33)]
     return W[0], b[0], W[1], b[1]
 
 

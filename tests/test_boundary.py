@@ -203,3 +203,23 @@ def test_kv_cosine_refusals_before_any_device_access():
     assert "overlaps k_ref" in hk.helm_last_error()
     assert L.helm_kv_cosine(*caches, out, ctypes.byref(shape(n_tokens=64, head_dim=96))) == 2
     assert L.helm_kv_cosine(*caches, out, ctypes.byref(shape(n_tokens=-1))) == 1
+
+
+def test_wide_map_workspace_and_refusals():
+    """helm_kv_transfer_wide / helm_kv_wide_workspace_bytes: bf16 and
+    head_dim 128 only; the workspace holds the two RoPE tables, the
+    un-rotated source keys and both transposed maps."""
+    s = shape(n_tokens=32768)
+    IN = hk.wide_in(4, 8, 128)
+    assert IN == 8192
+    n = hk.helm_kv_wide_workspace_bytes(s)
+    assert n == 2 * 32768 * 64 * 8 + 40 * 8 * 32768 * 128 * 2 + 2 * 64 * 8 * 128 * IN * 2
+    L = hk.lib()
+    fake = [ctypes.c_void_p((1 << 34) * (i + 1)) for i in range(11)]      # far apart: no overlaps
+    assert L.helm_kv_transfer_wide(*fake, ctypes.byref(shape(dtype=hk.HELM_F32))) == 5
+    assert "bf16" in hk.helm_last_error()
+    assert L.helm_kv_transfer_wide(*fake, ctypes.byref(shape(head_dim=64))) == 2
+    assert L.helm_kv_wide_workspace_bytes(ctypes.byref(shape(head_dim=64))) == 0
+    assert L.helm_kv_transfer_wide(*fake, ctypes.byref(shape(n_tokens=0))) == 0      # nothing to do
+    s = shape(n_tokens=64)
+    assert L.helm_kv_transfer_wide(*fake, ctypes.byref(s)) == 7                       # no workspace

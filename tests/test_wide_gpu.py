@@ -1,0 +1,123 @@
+"""GPU parity of the wide-input map (helm_kv_transfer_wide) against the fp64
+oracle (oracle.transfer_wide_rows), through the C ABI.
+
+The Qwen3 cache-mapping write-up, section "A linear bridge, strangely enough,
+suffices": the full mapper's x concatenates the KV features of all selected
+source layers, with one fit per target head for keys and one for values.
+Tolerance: the bf16 rule of tests/parity.py (per slab, the excess over half
+an output ulp at most 1e-2 rms, cosine at least 0.9999), the oracle in DTYPE
+mode (the un-rotated key rounded once to bf16, the map's operand type).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import parity
+from tests.parity import log, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library():
+    import cross_model_kv_helm_amd as hk
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert hk.helm_device_check(-1) == 0, hk.helm_last_error()
+    yield
+
+
+class WideCase:
+    """Device tensors for the library, host copies for the oracle."""
+
+    def __init__(self, w: synth.Workload):
+        self.w = w
+        c = synth.contiguous_inputs(w, device="cuda")
+        c["W_k"], c["b_k"], c["W_v"], c["b_v"] = synth.wide_maps(w, "cuda")
+        self.T = c["k_content"].shape[2]
+        self.host = {k: parity.to_np_storage(v) for k, v in c.items() if k != "k_content"}
+        self.host["src_k"] = oracle.encode_keys(parity.to_np_storage(c.pop("k_content")), self.host["src_pos"],
+                                                w.theta, oracle.BF16)
+        c["src_k"] = parity.from_np_storage(self.host["src_k"], "cuda")
+        self.dev = c
+
+    def run_gpu(self):
+        import cross_model_kv_helm_amd as hk
+        d, w = self.dev, self.w
+        shape = (w.n_tgt_layers, w.n_kv_heads, self.T, w.head_dim)
+        out = (torch.empty(shape, dtype=torch.bfloat16, device="cuda"),
+               torch.empty(shape, dtype=torch.bfloat16, device="cuda"))
+        s = hk.make_shape(d["src_k"], d["W_k"], d["layer_sel"], w.theta, w.theta)
+        hk.helm_kv_transfer_wide(d["src_k"], d["src_v"], d["src_pos"], d["tgt_pos"], d["layer_sel"], d["W_k"],
+                                 d["b_k"], d["W_v"], d["b_v"], out[0], out[1], s)
+        return out
+
+    def check(self, out_k, out_v, rows=None, label=""):
+        w, h, D = self.w, self.host, self.w.head_dim
+        pb = oracle.Problem(w.n_src_layers, w.n_tgt_layers, w.n_kv_heads, D, w.k, n_tokens=self.T,
+                            theta_src=w.theta, theta_tgt=w.theta, dtype=oracle.BF16, quantize_content=True)
+        ref_k, ref_v = oracle.transfer_wide_rows(pb, h["src_k"], h["src_v"], h["src_pos"], h["tgt_pos"],
+                                                 h["layer_sel"], h["W_k"], h["b_k"], h["W_v"], h["b_v"], rows=rows)
+        gk = parity.storage_to_f64(parity.to_np_storage(out_k)).reshape(-1, D)
+        gv = parity.storage_to_f64(parity.to_np_storage(out_v)).reshape(-1, D)
+        if rows is None:
+            rows = np.arange(gk.shape[0])
+        else:
+            gk, gv = gk[rows], gv[rows]
+        slab = rows // self.T
+        sk = parity.compare(gk, ref_k.reshape(-1, D), slab, "bf16", f"{label}{w.name} K")
+        sv = parity.compare(gv, ref_v.reshape(-1, D), slab, "bf16", f"{label}{w.name} V")
+        log(f"{label}{w.name}: {len(rows)} rows; K {sk}; V {sv}")
+
+
+def W(name, *args, **kw):
+    return synth.Workload(name, *args, **kw)
+
+
+def test_wide_small_ragged_full():
+    """Two token tiles (the second ragged), two heads, k = 2 (IN = 1024)."""
+    case = WideCase(W("wide_small", 5, 3, 2, 128, 300, 2, "bf16", 1e6, "shift4096", 61))
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    case.check(*out)
+
+
+def test_wide_one_head_k1_short_full():
+    """H = 1 (one column tile: the key map and the value map of head 0),
+    k = 1 (IN = 256, four pipeline steps), 33 tokens."""
+    case = WideCase(W("wide_h1", 3, 2, 1, 128, 33, 1, "bf16", 1e4, "gap1000", 62))
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    case.check(*out)
+
+
+def test_wide_three_heads_mixed_tile_full():
+    """H = 3: column tile 1 holds the key map of head 2 and the value map of
+    head 0, so the two waves of a row-half take different kinds."""
+    case = WideCase(W("wide_h3", 4, 2, 3, 128, 257, 2, "bf16", 1e6, "same", 63))
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    case.check(*out)
+
+
+def test_wide_xcd_order_full():
+    """2,048 tokens = 8 token tiles: the XCD-aware tile order (the column
+    tiles of a token tile consecutive on one XCD)."""
+    case = WideCase(W("wide_xcd", 4, 2, 2, 128, 2048, 2, "bf16", 1e6, "shift4096", 64))
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    case.check(*out)
+
+
+def test_wide_qwen3_14b_32b_t32k_sampled():
+    """The benchmark's wide workload (40 -> 64 layers, 8 heads, k = 4, IN =
+    8192, 32,768 tokens) on sampled rows of every slab."""
+    w = synth.CONFIGS["qwen3_14b_32b_t32k_wide"]
+    case = WideCase(w)
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    rows = sample_rows(w.n_tgt_layers, w.n_kv_heads, case.T, 4, 2)
+    case.check(*out, rows=rows)
