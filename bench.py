@@ -42,6 +42,8 @@ COUNTERS_MD = os.path.join(ROOT, "profiles", "transfer_mfma_qwen3_14b_32b_t32k_c
 KERNEL_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "transfer_mfma.hip")
 COSINE_MD = os.path.join(ROOT, "profiles", "kv_cosine_qwen3_14b_32b_t32k.md")
 COSINE_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "cosine.hip")
+WIDE_MD = os.path.join(ROOT, "profiles", "wide_gemm_qwen3_14b_32b_t32k_wide.md")
+WIDE_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "wide.hip")
 
 
 def kernel_source_digest(path: str = KERNEL_SRC) -> str:
@@ -144,6 +146,55 @@ def cpu_baseline(w, budget_s: float):
                       f"first {T_s} tokens, fp64 C oracle with OpenMP, {elapsed:.2f} s"}
 
 
+def wide_leg(hk, synth, w, src_k, c, out_k, out_v, steps, stream):
+    """The wide-input map on the same caches, positions and selection: every
+    target head's key and value maps read the K and V features of all heads
+    of the k selected layers (IN = k*2*H*D), with maps drawn as
+    synth.wide_maps.  Times whole calls and the product kernel alone (the
+    HELM_STAGE_MAP stage, after one preparation), with HIP events on the
+    launch stream; the product's roofline is the matrix cores' bf16 peak."""
+    import numpy as np
+    import torch
+    log("wide-input map: drawing maps")
+    W_k, b_k, W_v, b_v = synth.wide_maps(w, src_k.device)
+    T = src_k.shape[2]
+    shape = hk.make_shape(src_k, W_k, c["layer_sel"], w.theta, w.theta)
+    shape.stream = hk.current_stream_ptr(src_k.device)
+    ws = torch.empty(hk.helm_kv_wide_workspace_bytes(shape), dtype=torch.uint8, device=src_k.device)
+
+    def call(stages):
+        hk.helm_kv_transfer_wide_stage(stages, src_k, c["src_v"], c["src_pos"], c["tgt_pos"], c["layer_sel"], W_k,
+                                       b_k, W_v, b_v, out_k, out_v, shape, workspace=ws)
+
+    n = max(2, steps // 4)          # ~72 ms per call at the 14B -> 32B shape
+    for _ in range(2):
+        call(hk.HELM_STAGE_ALL)
+    torch.cuda.synchronize()
+    res = {}
+    for name, stages in (("call", hk.HELM_STAGE_ALL), ("product", hk.HELM_STAGE_MAP)):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record(stream)
+            call(stages)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    IN = hk.wide_in(w.k, w.n_kv_heads, w.head_dim)
+    flops = 2.0 * w.n_tgt_layers * T * IN * 2 * w.n_kv_heads * w.head_dim
+    gms = res["product"]
+    log(f"wide-input map: call {res['call']:.3f} ms, product {gms:.3f} ms, "
+        f"{flops / (gms * 1e-3) / 1e12:.1f} TFLOP/s over {n} launches")
+    traffic, note = recorded_traffic(WIDE_MD, WIDE_SRC)
+    del ws, W_k, W_v
+    return {"ms_per_transfer": res["call"], "tokens_per_s": T / (res["call"] * 1e-3), "in_features": IN,
+            "launches": n, "kernel": "wide_gemm_kernel",
+            "roofline": {"bound": "mfma", "achieved": flops / (gms * 1e-3) / 1e12,
+                         "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": flops / (gms * 1e-3) / MFMA_BF16_PEAK, "traffic": traffic,
+                         "kernel_ms": gms, "algorithmic_flops": flops, "traffic_source": note}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +202,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_14b_32b_t32k")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--wide", type=int, default=1, help="also time the wide-input map (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (the reference "
                          "kernel that scales HBM byte counters) and exit")
@@ -271,6 +323,8 @@ def main():
                            "unit": "GB/s", "frac": cos_bytes / (cms * 1e-3) / HBM_PEAK, "traffic": cos_traffic,
                            "algorithmic_bytes": cos_bytes, "traffic_source": cos_note}}
 
+    wide = wide_leg(hk, synth, w, src_k, c, out_k, out_v, args.steps, stream) if args.wide else None
+
     B, F, parts = algorithmic_work(w, c["layer_sel"].cpu().numpy(), T)
     t_s = ms * 1e-3
     t_k = kms * 1e-3
@@ -319,6 +373,7 @@ def main():
         "cpu_baseline": cpu,
         "bytes_breakdown": parts,
         "kv_cosine": kv_cos,
+        "wide_map": wide,
     }
     print(json.dumps(line), flush=True)
 

@@ -26,7 +26,7 @@ STATUS = {0: "HELM_OK", 1: "HELM_E_INVALID_ARG", 2: "HELM_E_PAIR_SHAPE", 3: "HEL
 HELM_STAGE_TABLES, HELM_STAGE_MAP, HELM_STAGE_ALL = 1, 2, 3
 
 EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_stage", "helm_kv_transfer_paged", "helm_kv_cosine",
-            "helm_kv_transfer_wide", "helm_kv_wide_workspace_bytes", "helm_kv_workspace_bytes",
+            "helm_kv_transfer_wide", "helm_kv_transfer_wide_stage", "helm_kv_wide_workspace_bytes", "helm_kv_workspace_bytes",
             "helm_kv_paged_workspace_bytes", "helm_mapper_check", "helm_paged_check",
             "helm_device_check", "helm_arch_supported", "helm_last_error", "helm_status_string",
             "helm_abi_version")
@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.helm_kv_transfer_stage.restype = ctypes.c_int
         L.helm_kv_transfer_wide.restype = ctypes.c_int
         L.helm_kv_transfer_wide.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
+        L.helm_kv_transfer_wide_stage.restype = ctypes.c_int
+        L.helm_kv_transfer_wide_stage.argtypes = [ctypes.c_int] + [vp] * 11 + [ctypes.POINTER(HelmShape)]
         L.helm_kv_wide_workspace_bytes.restype = ctypes.c_size_t
         L.helm_kv_wide_workspace_bytes.argtypes = [ctypes.POINTER(HelmShape)]
         L.helm_kv_cosine.restype = ctypes.c_int
@@ -270,6 +272,15 @@ def wide_in(k: int, H: int, D: int) -> int:
 def helm_kv_transfer_wide(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v,
                           shape: HelmShape, workspace=None) -> None:
     """The wide-input map (see include/helm_kv.h): W_k, W_v [L_t, H, k*2*H*D, D] bf16."""
+    helm_kv_transfer_wide_stage(HELM_STAGE_ALL, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v,
+                                out_k, out_v, shape, workspace)
+
+
+def helm_kv_transfer_wide_stage(stages: int, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v,
+                                out_k, out_v, shape: HelmShape, workspace=None) -> None:
+    """helm_kv_transfer_wide in stages (HELM_STAGE_TABLES: tables, un-rotated
+    keys and transposed maps into the workspace; HELM_STAGE_MAP: the product
+    reading them)."""
     import torch
     L_s, L_t, H, D, k, T = (shape.n_src_layers, shape.n_tgt_layers, shape.n_kv_heads,
                             shape.head_dim, shape.k, shape.n_tokens)
@@ -289,7 +300,7 @@ def helm_kv_transfer_wide(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W
         workspace = torch.empty(helm_kv_wide_workspace_bytes(shape), dtype=torch.uint8, device=src_k.device)
     shape.workspace = workspace.data_ptr()
     shape.workspace_bytes = workspace.numel()
-    _raise(lib().helm_kv_transfer_wide(*ptrs, ctypes.byref(shape)))
+    _raise(lib().helm_kv_transfer_wide_stage(int(stages), *ptrs, ctypes.byref(shape)))
 
 
 def helm_kv_cosine(k_mapped, v_mapped, k_ref, v_ref, shape: HelmShape, out=None):

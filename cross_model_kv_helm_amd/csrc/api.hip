@@ -476,10 +476,12 @@ size_t helm_kv_wide_workspace_bytes(const helm_shape_t* s) {
   return w.total;
 }
 
-int helm_kv_transfer_wide(const void* src_k, const void* src_v, const int32_t* src_pos, const int32_t* tgt_pos,
-                          const int32_t* layer_sel, const void* W_k, const float* b_k, const void* W_v,
-                          const float* b_v, void* out_k, void* out_v, const helm_shape_t* s) {
+int helm_kv_transfer_wide_stage(int stages, const void* src_k, const void* src_v, const int32_t* src_pos,
+                                const int32_t* tgt_pos, const int32_t* layer_sel, const void* W_k, const float* b_k,
+                                const void* W_v, const float* b_v, void* out_k, void* out_v,
+                                const helm_shape_t* s) {
   clear_error();
+  if (stages < 1 || stages > HELM_STAGE_ALL) return fail(HELM_E_INVALID_ARG, "stages = %d is not 1, 2 or 3", stages);
   int rc = check_wide_shape(s);
   if (rc != HELM_OK) return rc;
   if (s->n_tokens == 0) return HELM_OK;   // nothing to map; no pointer or device is touched
@@ -532,12 +534,22 @@ int helm_kv_transfer_wide(const void* src_k, const void* src_v, const int32_t* s
   rc = device_gate(-1);
   if (rc != HELM_OK) return rc;
   const hipStream_t stream = (hipStream_t)s->stream;
-  rc = launch_status(helm::launch_rope_tables(src_pos, tgt_pos, s->n_tokens, s->head_dim, s->rope_theta_src,
-                                              s->rope_theta_tgt, const_cast<float2*>(x.rope_src),
-                                              const_cast<float2*>(x.rope_tgt), stream),
-                     "RoPE table kernel launch");
-  if (rc != HELM_OK) return rc;
-  return launch_status(helm::launch_wide(x, stream), "wide-input map launch");
+  if (stages & HELM_STAGE_TABLES) {
+    rc = launch_status(helm::launch_rope_tables(src_pos, tgt_pos, s->n_tokens, s->head_dim, s->rope_theta_src,
+                                                s->rope_theta_tgt, const_cast<float2*>(x.rope_src),
+                                                const_cast<float2*>(x.rope_tgt), stream),
+                       "RoPE table kernel launch");
+    if (rc != HELM_OK) return rc;
+  }
+  return launch_status(helm::launch_wide(x, stages & HELM_STAGE_TABLES, stages & HELM_STAGE_MAP, stream),
+                       "wide-input map launch");
+}
+
+int helm_kv_transfer_wide(const void* src_k, const void* src_v, const int32_t* src_pos, const int32_t* tgt_pos,
+                          const int32_t* layer_sel, const void* W_k, const float* b_k, const void* W_v,
+                          const float* b_v, void* out_k, void* out_v, const helm_shape_t* s) {
+  return helm_kv_transfer_wide_stage(HELM_STAGE_ALL, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v,
+                                     out_k, out_v, s);
 }
 
 int helm_kv_cosine(const void* k_mapped, const void* v_mapped, const void* k_ref, const void* v_ref,

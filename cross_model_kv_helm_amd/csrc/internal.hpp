@@ -98,7 +98,9 @@ struct WideXfer {
 };
 int64_t wide_in_features(int32_t k, int32_t H, int32_t D);
 bool wide_supports(const WideXfer& x);
-hipError_t launch_wide(const WideXfer& x, hipStream_t stream);
+// prep: the un-rotated keys and the transposed maps into the workspace
+// (reads rope_src); product: the map itself, reading them.
+hipError_t launch_wide(const WideXfer& x, bool prep, bool product, hipStream_t stream);
 
 // Matrix-core transfer kernel for bf16 storage.  Returns hipErrorNotSupported
 // (and enqueues nothing) when the shape is outside what it handles.

@@ -11,14 +11,15 @@
 //   out_k[l, h, t, :] = R(+tgt_pos[t]) (x W_k[l, h] + b_k[l, h]),
 //   out_v[l, h, t, :] = x W_v[l, h] + b_v[l, h].
 // So each target layer is one dense product [T, IN] x [IN, 2*H*D]: bound by
-// the matrix cores (C3 at IN = 8192: 70 TFLOP over ~60 GB of traffic).
+// the matrix cores (40 -> 64 layers, 8 heads, k = 4, IN = 8192, 32,768
+// tokens: 70 TFLOP over ~45 GB of compulsory HBM traffic).
 //
 // Design for MI355X:
 //   * Two streaming pre-passes put both operands in k-contiguous bf16, the
 //     form the matrix instruction reads: the source keys un-rotated once at
 //     src_pos (fp32 arithmetic, rounded once to bf16 — the map's operand
 //     type) and each map's W transposed to [D][IN].  Both are HBM-bound and
-//     small next to the product (~2 ms of ~40).
+//     small next to the product (~1 ms of ~72 at the shape above).
 //   * Product: v_mfma_f32_32x32x16_bf16, one 256-thread workgroup per
 //     256-token x 256-column tile (two (head, K|V) maps), four waves of
 //     128 x 128 each (4 x 4 accumulator blocks, 256 fp32 accumulators per
@@ -26,13 +27,19 @@
 //     d and d+64 sit in the same lane of blocks nb and nb+2.
 //   * Operand tiles of 64 k-values reach LDS by buffer->LDS DMA (16 bytes
 //     per lane, no registers in between), double-buffered: the copies of
-//     step s+1 fly while step s multiplies.  A lane chooses which 16-byte
-//     piece it copies, so the tiles are stored XOR-swizzled (piece c of row
-//     r at slot r*8 + (c ^ ((r/2) & 7))) and every 16-byte fragment read of
-//     the products is bank-conflict free.
+//     step s+1 are issued between the first 32 products of step s (one
+//     after every other product) and land while the rest run.  (The ring
+//     depth and step size are parameters; deeper rings of 32-value steps
+//     measured slower: one barrier per 32 products instead of 64.)  A lane
+//     chooses which 16-byte piece it copies, so the tiles are stored
+//     XOR-swizzled (piece c of row r at slot r*8 + (c ^ ((r/2) & 7))) and
+//     every 16-byte fragment read of the products is bank-conflict free.
 //   * XCD-aware tile order: the 8 column tiles of a token tile run on one
-//     XCD (workgroup id mod 8), so its activation tile is fetched into that
-//     XCD's L2 once and served to all 8.
+//     XCD (workgroup id mod 8), so its activation tile can be served to all
+//     8 from that XCD's L2.  The measured bound is the latency of the copies
+//     that miss L2 inside the one step of lookahead (vector memory returns
+//     in issue order, so neither deeper rings of smaller steps nor L2
+//     warm-up loads issued steps ahead shorten it), not HBM bytes.
 //   * Epilogue from registers: bias, the forward rotation at tgt_pos (keys;
 //     fp32 tables from the RoPE table kernel), round to bf16, store.
 #include "internal.hpp"
@@ -52,8 +59,15 @@ constexpr int kHalf = 64;
 constexpr int kTT = 256;          // tokens per tile
 constexpr int kCT = 256;          // output columns per tile (two maps)
 constexpr int kKB = 64;           // k-values per pipeline step
+constexpr int kBufs = 2;          // LDS ring of operand tiles: copies run kBufs-1 steps ahead
+constexpr int kMaxSel = 64;       // selected layers per target layer (the library's limit on k)
 constexpr int kThreads = 256;     // four waves, 2 x 2
-constexpr int kRowPieces = kKB * 2 / 16;   // 16-byte pieces per tile row and step (8)
+constexpr int kRowPieces = kKB * 2 / 16;   // 16-byte pieces per tile row and step
+constexpr int kSwz = 16 / kRowPieces;      // rows sharing one swizzle pattern
+constexpr int kRowsPerCopy = 64 / kRowPieces;   // tile rows per 1 KB copy instruction
+constexpr int kPer = kRowPieces;           // copy instructions per wave, operand and step
+constexpr int kCopyStride = 32 / (2 * kPer) > 0 ? 32 / (2 * kPer) : 1;   // products between two copies (spread over 32)
+static_assert(kKB % 16 == 0 && 16 % kRowPieces == 0 && kBufs >= 2 && kBufs <= 5 && (kBufs - 2) * 2 * kPer < 64, "pipeline shape");
 constexpr uint32_t kSkip = 0xffffff00u;    // offset past every descriptor: zero load
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -70,23 +84,28 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
 }
 
 // Buffer -> LDS copy of 16 bytes per lane: lane i reads the 16 bytes at
-// byte offset voff (per lane) of the buffer `rsrc` and they land at
-// lds_base + 16*i.  rsrc and lds_base are wave-uniform.  Inline assembly so
-// that the compiler does not make later LDS accesses wait for the copy; the
+// byte offset voff + soff of the buffer `rsrc` and they land at lds_base +
+// 16*i.  rsrc, soff and lds_base are wave-uniform.  Inline assembly so that
+// the compiler does not make later LDS accesses wait for the copy; the
 // kernel waits for its copies itself (wait_vmcnt) before the barrier that
 // publishes a tile.
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, const void* lds_base) {
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t soff, const void* lds_base) {
   const uint32_t m = (uint32_t)(uintptr_t)(lds_void_t)lds_base;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm("" : "+s"(soff));   // a constant offset above 64 is no inline operand: keep it in a register
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(m)
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(m)
                : "memory", "m0");
 }
 
-__device__ __forceinline__ void wait_vmcnt0() {
+// Waits until at most N of this wave's vector memory operations (here only
+// the copies) are outstanding; they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0); lgkm and exp untouched
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -96,8 +115,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// 16-byte slot of piece c of tile row r (XOR swizzle, see the header).
-__device__ __forceinline__ int slot(int r, int c) { return r * kRowPieces + (c ^ ((r >> 1) & 7)); }
+// 16-byte slot of piece c of tile row r (XOR swizzle, see the header): the
+// 16 rows that one pass of a 16-byte LDS read touches land in 16 different
+// bank groups.
+__device__ __forceinline__ int slot(int r, int c) { return r * kRowPieces + (c ^ ((r / kSwz) % kRowPieces)); }
 
 struct WideArgs {
   const uint16_t* U;          // un-rotated keys [L_s, H, T, D] bf16
@@ -114,15 +135,23 @@ struct WideArgs {
   int32_t n_tt, n_ct;         // token tiles, column tiles per target layer
 };
 
-__global__ void __launch_bounds__(kThreads, 1) wide_gemm_kernel(WideArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTT * kKB];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kCT * kKB];
+struct GemmSmem {
+  uint16_t As[kBufs][kTT * kKB] __attribute__((aligned(16)));
+  uint16_t Bs[kBufs][kCT * kKB] __attribute__((aligned(16)));
+  int32_t sel[kMaxSel];
+};
 
-  // ---- tile of this workgroup: with token tiles a multiple of 8, the
-  // column tiles of one token tile are consecutive on one XCD (id mod 8)
+// One 256 x 256 output tile m, computed by the whole workgroup.
+__device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem& sm) {
+  auto& As = sm.As;
+  auto& Bs = sm.Bs;
+  auto& sel_s = sm.sel;
+
+  // ---- tile m: with token tiles a multiple of 8, the column tiles of one
+  // token tile are consecutive on one XCD (m mod 8)
   const int64_t per_layer = (int64_t)a.n_tt * a.n_ct;
-  const int32_t l = (int32_t)(blockIdx.x / per_layer);
-  const int32_t i = (int32_t)(blockIdx.x % per_layer);
+  const int32_t l = (int32_t)(m / per_layer);
+  const int32_t i = (int32_t)(m % per_layer);
   int32_t tt, ct;
   if (a.n_tt % 8 == 0) {
     const int32_t q = i / 8;
@@ -132,13 +161,18 @@ __global__ void __launch_bounds__(kThreads, 1) wide_gemm_kernel(WideArgs a) {
     tt = i / a.n_ct;
     ct = i % a.n_ct;
   }
-  // an out-of-range selected layer leaves the target layer unwritten (and
-  // no address is ever formed from it)
-  for (int j = 0; j < a.k; ++j) {
-    const int32_t sj = a.layer_sel[l * a.k + j];
-    if (sj < 0 || sj >= a.L_s) return;   // uniform over the workgroup, before any barrier
-  }
+  // The selected layers of this target layer, read once into LDS: a global
+  // read inside the pipeline would be a vector load, and waiting for it
+  // would wait for every copy in flight.  An out-of-range selected layer
+  // leaves the target layer unwritten (and no address is ever formed from it).
+  if (a.k > kMaxSel) return;
   const int tid = threadIdx.x;
+  if (tid < a.k) sel_s[tid] = a.layer_sel[l * a.k + tid];
+  __syncthreads();
+  for (int j = 0; j < a.k; ++j) {
+    const int32_t sj = sel_s[j];
+    if (sj < 0 || sj >= a.L_s) return;   // uniform over the workgroup, before any later barrier
+  }
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
@@ -148,35 +182,51 @@ __global__ void __launch_bounds__(kThreads, 1) wide_gemm_kernel(WideArgs a) {
   const uint32_t map_bytes = (uint32_t)kD * IN * 2;
   const int n_steps = IN / kKB;
 
-  // ---- operand copies of step s into buffer p: wave w copies the A and
-  // B instructions i = w, w+4, ..., w+28; instruction i covers tile rows
-  // 8i .. 8i+7, lane q the row 8i + q/8 and slot (q % 8) of it, i.e. piece
-  // (q % 8) ^ ((row/2) & 7).
-  auto copy_step = [&](int s, int p) __attribute__((always_inline)) {
-    const int fb = s >> 1, half = s & 1;                 // feature block (j, kv, g) and its half
+  // ---- operand copies: wave w issues the A and B copy instructions i =
+  // w, w+4, w+8, ...; instruction i covers kRowsPerCopy tile rows from
+  // kRowsPerCopy*i on, lane q the row kRowsPerCopy*i + q/kRowPieces and slot
+  // q % kRowPieces of it (so the piece that swizzles to that slot).  The
+  // per-lane byte offsets do not depend on the step; the step's part (which
+  // part of a feature block, which k range of W^T) is the uniform scalar
+  // offset, and the A descriptor names the step's source slab.  Instruction
+  // n of a wave is 4*kRowsPerCopy rows below instruction n-1 and its lanes
+  // take the same pieces (the swizzle term repeats every 16*kSwz rows), so
+  // one per-lane offset per operand serves all: A adds the row step (and
+  // skips rows past T), B folds it, modulo one map, into the scalar offset.
+  constexpr int kRowStep = 4 * kRowsPerCopy;                     // rows between a wave's instructions
+  constexpr int kMapWraps = kD / kRowStep;                       // instructions per map (B)
+  static_assert((16 * kSwz) % kRowStep == 0 || kRowStep % (16 * kSwz) == 0, "swizzle period");
+  const int r0 = kRowsPerCopy * w + lane / kRowPieces;
+  const int c0 = (lane % kRowPieces) ^ ((r0 / kSwz) % kRowPieces);
+  const uint32_t voff_a0 = (uint32_t)(t0 + r0) * (kD * 2) + 16 * c0;
+  const uint32_t a_lim = (uint32_t)T * (kD * 2);                 // first byte past the last token
+  const uint32_t voff_b0 = (uint32_t)r0 * IN * 2 + 16 * c0;
+  u32x4 rs_b[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int mi = 2 * ct + q;                            // map: kind * H + head
+    rs_b[q] = rsrc_words((mi / H ? a.WT_v : a.WT_k) + ((int64_t)l * H + mi % H) * kD * IN, map_bytes);
+  }
+  constexpr int kStepsPerBlock = kD / kKB;                // steps per (j, kv, g) feature block
+  auto a_rsrc = [&](int s) __attribute__((always_inline)) {
+    const int fb = s / kStepsPerBlock;                    // feature block (j, kv, g)
     const int j = fb / (2 * H), kv = (fb / H) & 1, g = fb % H;
-    const int32_t sl = a.layer_sel[l * a.k + j];
-    const uint16_t* slab = (kv ? a.V : a.U) + ((int64_t)sl * H + g) * T * kD;
-    const u32x4 ra = rsrc_words(slab, slab_bytes);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int ins = w + 4 * n;
-      const int r = 8 * ins + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      const int32_t t = t0 + r;
-      const uint32_t off = t < T ? (uint32_t)t * (kD * 2) + half * (kKB * 2) + 16 * c : kSkip;
-      dma16(ra, off, (const char*)As[p] + 1024 * ins);
-    }
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int ins = w + 4 * n;
-      const int r = 8 * ins + (lane >> 3);
-      const int mi = 2 * ct + (r >> 7);                  // map: kind * H + head (uniform per instruction)
-      const int kind = mi / H, h = mi % H;
-      const uint16_t* map = (kind ? a.WT_v : a.WT_k) + ((int64_t)l * H + h) * kD * IN;
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      const uint32_t off = (uint32_t)(r & (kD - 1)) * IN * 2 + (uint32_t)s * (kKB * 2) + 16 * c;
-      dma16(rsrc_words(map, map_bytes), off, (const char*)Bs[p] + 1024 * ins);
+    const int32_t sl = __builtin_amdgcn_readfirstlane(sel_s[j]);
+    return rsrc_words((kv ? a.V : a.U) + ((int64_t)sl * H + g) * T * kD, slab_bytes);
+  };
+  // copy q (0 .. 2*kPer-1) of step s into ring slot p: q < kPer this wave's
+  // A instruction q, else its B instruction q-kPer (the first half of the B
+  // instructions covers map 0, the second map 1)
+  auto copy_one = [&](int s, int p, int q, const u32x4& ra) __attribute__((always_inline)) {
+    if (q < kPer) {
+      const uint32_t va = voff_a0 + (uint32_t)(q * kRowStep * kD * 2);
+      dma16(ra, va < a_lim ? va : kSkip, (uint32_t)(s % kStepsPerBlock) * (kKB * 2),   // (kSkip + 192 stays past every range)
+            (const char*)As[p] + 1024 * (w + 4 * q));
+    } else {
+      const int n = q - kPer;
+      dma16(rs_b[n >= kPer / 2 ? 1 : 0], voff_b0,
+            (uint32_t)s * (kKB * 2) + (uint32_t)((n % kMapWraps) * kRowStep) * (uint32_t)IN * 2,
+            (const char*)Bs[p] + 1024 * (w + 4 * n));
     }
   };
 
@@ -186,32 +236,82 @@ __global__ void __launch_bounds__(kThreads, 1) wide_gemm_kernel(WideArgs a) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
 
-  copy_step(0, 0);
-  wait_vmcnt0();
+  // steps 0 .. kBufs-2 in flight before the loop (n_steps >= kBufs - 1:
+  // at least 256 features, the host checks)
+#pragma unroll
+  for (int s0 = 0; s0 < kBufs - 1; ++s0) {
+    const u32x4 ra = a_rsrc(s0);
+#pragma unroll
+    for (int q = 0; q < 2 * kPer; ++q) copy_one(s0, s0, q, ra);
+  }
+  wait_vmcnt<(kBufs - 2) * 2 * kPer>();   // step 0 landed
   lds_barrier();
-  for (int s = 0; s < n_steps; ++s) {
-    const int p = s & 1;
-    if (s + 1 < n_steps) copy_step(s + 1, p ^ 1);
+  // fragment bases: row 128*wm + 32*mb + lane%32 (resp. 128*wn + ...), piece
+  // 2*ks + lane/32; the swizzle term depends on lane%32 only, so the four
+  // 32-row blocks are 32 rows apart
+  const int fr = lane & 31;
+  auto frag_off = [&](int base_row, int ks) __attribute__((always_inline)) {
+    return slot(base_row + fr, 2 * ks + (lane >> 5)) * 8;
+  };
+  constexpr int kBlockElems = 32 * kRowPieces * 8;        // one 32-row block of a tile (elements)
+  // one pipeline step: the products of step s from ring slot s % kBufs and,
+  // with ISSUE, the copies of step s+kBufs-1 into the slot step s-1 used
+  auto step = [&](int s, auto issue) __attribute__((always_inline)) {
+    constexpr bool kIssue = decltype(issue)::value;
+    const int p = s % kBufs;
+    const int ahead = s + kBufs - 1;
+    u32x4 ra;
+    if constexpr (kIssue) ra = a_rsrc(ahead);
     const uint16_t* A = As[p];
     const uint16_t* B = Bs[p];
+    bf16x8 af[2][4], bfr[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) af[0][mb] = *(const bf16x8*)&A[frag_off(128 * wm, 0) + mb * kBlockElems];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) bfr[0][nb] = *(const bf16x8*)&B[frag_off(128 * wn, 0) + nb * kBlockElems];
 #pragma unroll
     for (int ks = 0; ks < kKB / 16; ++ks) {
-      const int c = 2 * ks + (lane >> 5);
-      bf16x8 af[4], bfr[4];
+      const int cur = ks & 1, nxt = cur ^ 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < kKB / 16) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        af[mb] = *(const bf16x8*)&A[slot(128 * wm + 32 * mb + (lane & 31), c) * 8];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        bfr[nb] = *(const bf16x8*)&B[slot(128 * wn + 32 * nb + (lane & 31), c) * 8];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 4; ++mb)
+          af[nxt][mb] = *(const bf16x8*)&A[frag_off(128 * wm, ks + 1) + mb * kBlockElems];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+          bfr[nxt][nb] = *(const bf16x8*)&B[frag_off(128 * wn, ks + 1) + nb * kBlockElems];
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][mb], bfr[cur][nb], acc[mb][nb], 0, 0, 0);
+          // the copies of the step ahead, one after every kCopyStride-th product
+          const int m = 16 * ks + 4 * mb + nb;
+          if constexpr (kIssue)
+            if (m % kCopyStride == kCopyStride - 1 && m / kCopyStride < 2 * kPer)
+              copy_one(ahead, ahead % kBufs, m / kCopyStride, ra);
+        }
     }
-    wait_vmcnt0();        // this wave's copies of step s+1
-    lds_barrier();        // everyone's copies landed; everyone is done with buffer p
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // steady state: step s+1 must have landed at the end of step s, the copies
+  // of steps s+2 .. s+kBufs-1 may still fly
+  int s = 0;
+  for (; s + kBufs - 1 < n_steps; ++s) {
+    step(s, std::true_type{});
+    wait_vmcnt<(kBufs - 2) * 2 * kPer>();
+    lds_barrier();        // everyone's copies of step s+1 landed; everyone is done with slot s % kBufs
+  }
+  // the last kBufs-1 steps issue nothing; after step s the copies of steps
+  // s+2 .. n_steps-1 (at most two steps' worth) may still fly
+  for (; s < n_steps; ++s) {
+    step(s, std::false_type{});
+    const int rem = n_steps - s - 2;
+    if (rem >= 2) wait_vmcnt<2 * 2 * kPer < 64 ? 2 * 2 * kPer : 0>();
+    else if (rem == 1) wait_vmcnt<2 * kPer>();
+    else wait_vmcnt<0>();
+    lds_barrier();
   }
 
   // ---- epilogue: this wave's map, bias, forward rotation (keys), store.
@@ -246,6 +346,15 @@ __global__ void __launch_bounds__(kThreads, 1) wide_gemm_kernel(WideArgs a) {
       }
     }
   }
+}
+
+// One workgroup per output tile.  (A persistent grid, one workgroup per CU
+// looping over tiles in lockstep rounds, halves the L2 misses but runs
+// slower: every workgroup then waits on the same misses, where drifting
+// start times let followers hit what leaders fetched.)
+__global__ void __launch_bounds__(kThreads, 1) wide_gemm_kernel(WideArgs a) {
+  __shared__ GemmSmem sm;
+  gemm_tile(a, blockIdx.x, sm);
 }
 
 // Keys un-rotated at src_pos and rounded once to bf16: one thread per
@@ -304,25 +413,28 @@ int64_t wide_in_features(int32_t k, int32_t H, int32_t D) { return (int64_t)k * 
 bool wide_supports(const WideXfer& x) {
   auto al = [](const void* p) { return ((uintptr_t)p % 16) == 0; };
   const int64_t IN = wide_in_features(x.k, x.H, x.D);
-  return x.D == kD && IN % kKB == 0 && (int64_t)x.T * kD * 2 <= 0xffffff00LL && (int64_t)kD * IN * 2 <= 0xffffff00LL &&
+  return x.D == kD && IN % kKB == 0 && IN / kKB >= kBufs - 1 && (int64_t)x.T * kD * 2 <= 0xffffff00LL && (int64_t)kD * IN * 2 <= 0xffffff00LL &&
          al(x.src_k) && al(x.src_v) && al(x.U) && al(x.WT_k) && al(x.WT_v);
 }
 
-hipError_t launch_wide(const WideXfer& x, hipStream_t stream) {
+hipError_t launch_wide(const WideXfer& x, bool prep, bool product, hipStream_t stream) {
   if (!wide_supports(x)) return hipErrorNotSupported;
   if (x.T <= 0) return hipSuccess;
   const int32_t IN = (int32_t)wide_in_features(x.k, x.H, x.D);
-  // pre-pass 1: un-rotated keys of every source layer
-  const int64_t rows = (int64_t)x.L_s * x.H * x.T;
-  hipLaunchKernelGGL(unrotate_keys_kernel, dim3(grid_for(rows * 8)), dim3(256), 0, stream,
-                     (const uint16_t*)x.src_k, x.rope_src, rows, x.T, x.U);
-  // pre-pass 2: every map's W transposed to [D, IN]
   const int64_t G = (int64_t)x.L_t * x.H;
   if (G > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_w_kernel, dim3(IN / 64, kD / 64, (unsigned)G), dim3(256), 0, stream,
-                     (const uint16_t*)x.W_k, IN, x.WT_k);
-  hipLaunchKernelGGL(transpose_w_kernel, dim3(IN / 64, kD / 64, (unsigned)G), dim3(256), 0, stream,
-                     (const uint16_t*)x.W_v, IN, x.WT_v);
+  if (prep) {
+    // pre-pass 1: un-rotated keys of every source layer
+    const int64_t rows = (int64_t)x.L_s * x.H * x.T;
+    hipLaunchKernelGGL(unrotate_keys_kernel, dim3(grid_for(rows * 8)), dim3(256), 0, stream,
+                       (const uint16_t*)x.src_k, x.rope_src, rows, x.T, x.U);
+    // pre-pass 2: every map's W transposed to [D, IN]
+    hipLaunchKernelGGL(transpose_w_kernel, dim3(IN / 64, kD / 64, (unsigned)G), dim3(256), 0, stream,
+                       (const uint16_t*)x.W_k, IN, x.WT_k);
+    hipLaunchKernelGGL(transpose_w_kernel, dim3(IN / 64, kD / 64, (unsigned)G), dim3(256), 0, stream,
+                       (const uint16_t*)x.W_v, IN, x.WT_v);
+  }
+  if (!product) return hipGetLastError();
   // the product with its epilogue
   WideArgs a{};
   a.U = x.U;
@@ -343,9 +455,9 @@ hipError_t launch_wide(const WideXfer& x, hipStream_t stream) {
   a.IN = IN;
   a.n_tt = (x.T + kTT - 1) / kTT;
   a.n_ct = (2 * x.H * kD) / kCT;   // = H
-  const int64_t grid = (int64_t)x.L_t * a.n_tt * a.n_ct;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(wide_gemm_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  const int64_t n_tiles = (int64_t)x.L_t * a.n_tt * a.n_ct;
+  if (n_tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(wide_gemm_kernel, dim3((unsigned)n_tiles), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -217,7 +217,7 @@ int helm_kv_transfer_paged(const void* src_k_pool, const void* src_v_pool,
  *   workspace: helm_kv_wide_workspace_bytes(shape) bytes, 256-byte aligned;
  *              it holds the RoPE tables, the un-rotated source keys
  *              [L_s, H, T, D] and both maps transposed [L_t, H, D, IN]
- *              (C3 with IN = 8192: 4.9 GB).
+ *              (40 -> 64 layers, 8 heads, IN = 8192, 32,768 tokens: 4.9 GB).
  * n_tokens = 0 enqueues nothing. */
 size_t helm_kv_wide_workspace_bytes(const helm_shape_t* shape);
 int helm_kv_transfer_wide(const void* src_k, const void* src_v,
@@ -227,6 +227,29 @@ int helm_kv_transfer_wide(const void* src_k, const void* src_v,
                           const void* W_v, const float* b_v,
                           void* out_k, void* out_v,
                           const helm_shape_t* shape);
+
+/* helm_kv_transfer_wide in two separately enqueued stages (for mapping
+ * several caches with the same maps and positions, and for timing the
+ * product alone).  stages is a bit mask:
+ *   HELM_STAGE_TABLES (1)  the preparation: the RoPE tables, the un-rotated
+ *                          source keys and both transposed maps, all into
+ *                          shape->workspace;
+ *   HELM_STAGE_MAP    (2)  the product and its bias / RoPE epilogue, reading
+ *                          the workspace: it must hold the preparation of
+ *                          the same src_k, positions, thetas, maps and shape,
+ *                          ordered before this call (not checked; a stale
+ *                          workspace gives wrong outputs);
+ *   HELM_STAGE_ALL    (3)  both, exactly helm_kv_transfer_wide.
+ * Every check of helm_kv_transfer_wide applies in every stage; stages
+ * outside 1..3 give HELM_E_INVALID_ARG. */
+int helm_kv_transfer_wide_stage(int stages,
+                                const void* src_k, const void* src_v,
+                                const int32_t* src_pos, const int32_t* tgt_pos,
+                                const int32_t* layer_sel,
+                                const void* W_k, const float* b_k,
+                                const void* W_v, const float* b_v,
+                                void* out_k, void* out_v,
+                                const helm_shape_t* shape);
 
 /* KV-cosine diagnostic ("Helm Intelligent Routing", the retention / KL /
  * KV-cosine table: how close the mapped cache is to the target model's

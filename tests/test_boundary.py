@@ -223,3 +223,7 @@ def test_wide_map_workspace_and_refusals():
     assert L.helm_kv_transfer_wide(*fake, ctypes.byref(shape(n_tokens=0))) == 0      # nothing to do
     s = shape(n_tokens=64)
     assert L.helm_kv_transfer_wide(*fake, ctypes.byref(s)) == 7                       # no workspace
+    for stages in (1, 2, 3):
+        assert L.helm_kv_transfer_wide_stage(stages, *fake, ctypes.byref(s)) == 7
+    for stages in (0, 4, -1):
+        assert L.helm_kv_transfer_wide_stage(stages, *fake, ctypes.byref(s)) == 1

@@ -121,3 +121,24 @@ def test_wide_qwen3_14b_32b_t32k_sampled():
     torch.cuda.synchronize()
     rows = sample_rows(w.n_tgt_layers, w.n_kv_heads, case.T, 4, 2)
     case.check(*out, rows=rows)
+
+
+def test_wide_stages_equal_one_call():
+    """The preparation and the product enqueued separately
+    (helm_kv_transfer_wide_stage) write exactly what one call writes, and a
+    second product from the same workspace does too."""
+    import cross_model_kv_helm_amd as hk
+    case = WideCase(W("wide_stages", 5, 3, 2, 128, 300, 2, "bf16", 1e6, "shift4096", 65))
+    d, w = case.dev, case.w
+    whole = case.run_gpu()
+    s = hk.make_shape(d["src_k"], d["W_k"], d["layer_sel"], w.theta, w.theta)
+    ws = torch.empty(hk.helm_kv_wide_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        out = (torch.full_like(whole[0], float("nan")), torch.full_like(whole[1], float("nan")))
+        stages = (hk.HELM_STAGE_TABLES, hk.HELM_STAGE_MAP) if rep == 0 else (hk.HELM_STAGE_MAP,)
+        for st in stages:
+            hk.helm_kv_transfer_wide_stage(st, d["src_k"], d["src_v"], d["src_pos"], d["tgt_pos"], d["layer_sel"],
+                                           d["W_k"], d["b_k"], d["W_v"], d["b_v"], out[0], out[1], s, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out[0], whole[0]) and torch.equal(out[1], whole[1]), f"pass {rep}"
+    case.check(*whole)
