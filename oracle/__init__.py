@@ -27,6 +27,10 @@ K|V.
 retention / KL / KV-cosine table): per (layer, head) slab, the cosine of a
 mapped cache and a reference cache taken as flat vectors, in fp64.
 
+``ridge_fit`` is the calibration's ridge fit of the maps (the Qwen3
+write-up's closed-form fit: centred data, lambda = 0.01, the bias from the
+means), in numpy fp64 with LAPACK's solve as one step.
+
 Pins: every function here is checked in tests/test_oracle_pins.py against
 closed forms, invariants, special cases that reduce to library routines,
 an independent complex-number / matrix-exponential formulation and a
@@ -373,3 +377,50 @@ def transfer_wide_rows(pb: Problem, src_k, src_v, src_pos, tgt_pos, layer_sel,
         shape = (pb.n_tgt_layers, pb.n_kv_heads, pb.n_tokens, D)
         return out_k.reshape(shape), out_v.reshape(shape)
     return out_k, out_v
+
+
+def _decode(a, dtype):
+    """Storage -> fp64: bf16 bits (uint16) are the upper half of an fp32;
+    float arrays are taken as they are."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        if dtype != BF16:
+            raise TypeError("uint16 storage is bf16")
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def ridge_fit(x, y, lam: float = 0.01, dtype: int = BF16):
+    """The ridge fit of the per-(target layer, head, K|V) maps, fp64 (the
+    Qwen3 cache-mapping write-up, section "A linear bridge, strangely enough,
+    suffices": each target head's key map and value map are fitted
+    separately by ridge regression with centred data and lambda = 0.01).
+
+    x: [G, N, IN] observations of the map's input per group (bf16 storage as
+    uint16, or float); y: [G, N, D] the targets.  For every group g, with the
+    column means mx = mean_n x[g], my = mean_n y[g] and the centred data
+    xc = x[g] - mx, yc = y[g] - my, the map W[g] [IN, D] solves
+        (xc^T xc + lam * I) W = xc^T yc
+    and the bias is b[g] = my - mx @ W (so x @ W + b reproduces y's mean).
+    Returns (W [G, IN, D], b [G, D]) in fp64.  The products are numpy
+    matmuls and the solve is LAPACK's (numpy.linalg.solve), in fp64."""
+    X = _decode(x, dtype)
+    Y = _decode(y, dtype)
+    if X.ndim != 3 or Y.ndim != 3 or X.shape[:2] != Y.shape[:2]:
+        raise ValueError("x [G, N, IN] and y [G, N, D] must share G and N")
+    G, N, IN = X.shape
+    D = Y.shape[2]
+    if N < 1:
+        raise ValueError("the fit needs at least one observation")
+    W = np.empty((G, IN, D))
+    b = np.empty((G, D))
+    for g in range(G):
+        mx = X[g].sum(axis=0) / N
+        my = Y[g].sum(axis=0) / N
+        xc = X[g] - mx
+        yc = Y[g] - my
+        normal = xc.T @ xc
+        normal[np.diag_indices(IN)] += lam
+        W[g] = np.linalg.solve(normal, xc.T @ yc)
+        b[g] = my - mx @ W[g]
+    return W, b

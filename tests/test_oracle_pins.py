@@ -667,3 +667,123 @@ def test_wide_map_brute_force(oracle_mod):
                       for n in range(D)]
                 np.testing.assert_allclose(ov[l, h, t], yv, atol=1e-12)
                 np.testing.assert_allclose(ok[l, h, t], rope_complex(np.array(yk), int(tgt[t]), 1e4), atol=1e-12)
+
+
+# ------------------------------------------------------------- ridge fit
+# The Qwen3 write-up, section "A linear bridge, strangely enough, suffices":
+# every target head's K and V maps are fitted separately by ridge regression
+# on centred data with lambda = 0.01; the bias comes from the means.
+
+def _planted(rng, G, N, IN, D, x_shift=3.0):
+    X = rng.standard_normal((G, N, IN)) + x_shift * rng.standard_normal((G, 1, IN))
+    Wt = rng.standard_normal((G, IN, D))
+    bt = rng.standard_normal((G, D))
+    Y = X @ Wt + bt[:, None, :]
+    return X, Y, Wt, bt
+
+
+def test_ridge_recovers_planted_map_and_bias(oracle_mod):
+    """Noiseless data y = x W* + b* (x with non-zero means, IN != D): a
+    vanishing lambda recovers W* and b*.  Catches a dropped centring, a
+    wrong bias sign or formula, and a transposed W."""
+    rng = np.random.default_rng(11)
+    X, Y, Wt, bt = _planted(rng, 3, 400, 7, 5)
+    W, b = oracle_mod.ridge_fit(X, Y, lam=1e-12, dtype=F32)
+    assert W.shape == (3, 7, 5) and b.shape == (3, 5)
+    np.testing.assert_allclose(W, Wt, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(b, bt, rtol=0, atol=1e-9)
+
+
+def test_ridge_zero_lambda_is_least_squares_with_intercept(oracle_mod):
+    """lambda = 0 is ordinary least squares with an intercept column:
+    numpy's lstsq (an SVD route) on [x, 1] gives the same map and bias."""
+    rng = np.random.default_rng(12)
+    X = rng.standard_normal((2, 300, 6)) + 2.0
+    Y = rng.standard_normal((2, 300, 4))
+    W, b = oracle_mod.ridge_fit(X, Y, lam=0.0, dtype=F32)
+    for g in range(2):
+        A = np.hstack([X[g], np.ones((300, 1))])
+        sol = np.linalg.lstsq(A, Y[g], rcond=None)[0]
+        np.testing.assert_allclose(W[g], sol[:6], rtol=0, atol=1e-11)
+        np.testing.assert_allclose(b[g], sol[6], rtol=0, atol=1e-11)
+
+
+def test_ridge_large_lambda_asymptote(oracle_mod):
+    """lambda -> infinity: lambda * W -> xc^T yc (the penalty dominates the
+    normal matrix), the closed-form limit; pins lambda on the diagonal,
+    unscaled."""
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((1, 200, 5)) + 1.0
+    Y = rng.standard_normal((1, 200, 3))
+    lam = 1e10
+    W, _ = oracle_mod.ridge_fit(X, Y, lam=lam, dtype=F32)
+    xc = X[0] - X[0].mean(axis=0)
+    yc = Y[0] - Y[0].mean(axis=0)
+    np.testing.assert_allclose(lam * W[0], xc.T @ yc, rtol=1e-6, atol=0)
+
+
+def test_ridge_scalar_closed_form_brute_force(oracle_mod):
+    """IN = D = 1 in pure Python: w = Sxy / (Sxx + lambda), b = ybar - xbar w,
+    with lambda = 0.01 on a small sample (where lambda is not negligible)."""
+    xs = [0.3, -1.2, 2.5, 0.7, 1.1]
+    ys = [1.0, -0.4, 3.3, 0.2, 2.0]
+    n = len(xs)
+    xb, yb = math.fsum(xs) / n, math.fsum(ys) / n
+    sxy = math.fsum((a - xb) * (c - yb) for a, c in zip(xs, ys))
+    sxx = math.fsum((a - xb) ** 2 for a in xs)
+    w = sxy / (sxx + 0.01)
+    bb = yb - xb * w
+    W, b = oracle_mod.ridge_fit(np.array(xs).reshape(1, n, 1), np.array(ys).reshape(1, n, 1), lam=0.01, dtype=F32)
+    assert W[0, 0, 0] == pytest.approx(w, rel=1e-13)
+    assert b[0, 0] == pytest.approx(bb, rel=1e-13)
+
+
+def test_ridge_optimality_conditions(oracle_mod):
+    """The fitted (W, b) is the minimiser of |y - x W - b|^2 + lambda |W|^2:
+    the gradient in W, xc^T (xc W - yc) + lambda W, vanishes and the mean
+    residual is zero."""
+    rng = np.random.default_rng(14)
+    X = rng.standard_normal((2, 150, 8)) * np.linspace(0.5, 4, 8) + 1.5
+    Y = rng.standard_normal((2, 150, 3)) + X[:, :, :3] * 0.7
+    lam = 0.5
+    W, b = oracle_mod.ridge_fit(X, Y, lam=lam, dtype=F32)
+    for g in range(2):
+        xc = X[g] - X[g].mean(axis=0)
+        yc = Y[g] - Y[g].mean(axis=0)
+        grad = xc.T @ (xc @ W[g] - yc) + lam * W[g]
+        assert np.abs(grad).max() < 1e-10
+        assert np.abs((Y[g] - X[g] @ W[g] - b[g]).mean(axis=0)).max() < 1e-12
+
+
+def test_ridge_shift_invariances(oracle_mod):
+    """Shifting x by a constant vector c leaves W and moves b by -c W;
+    shifting y by d moves only b, by d (centring at work)."""
+    rng = np.random.default_rng(15)
+    X = rng.standard_normal((1, 120, 4))
+    Y = rng.standard_normal((1, 120, 2))
+    c = np.array([5.0, -3.0, 0.5, 10.0])
+    d = np.array([-7.0, 2.0])
+    W0, b0 = oracle_mod.ridge_fit(X, Y, dtype=F32)
+    W1, b1 = oracle_mod.ridge_fit(X + c, Y, dtype=F32)
+    W2, b2 = oracle_mod.ridge_fit(X, Y + d, dtype=F32)
+    np.testing.assert_allclose(W1, W0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(b1[0], b0[0] - c @ W0[0], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(W2, W0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(b2[0], b0[0] + d, rtol=0, atol=1e-12)
+
+
+def test_ridge_bf16_storage_and_group_independence(oracle_mod):
+    """bf16 storage (uint16 bits) fits the same as its fp32 spelling, and
+    each group's fit depends on that group's data only."""
+    rng = np.random.default_rng(16)
+    X = torch.from_numpy(rng.standard_normal((3, 90, 6)).astype(np.float32)).to(torch.bfloat16)
+    Y = torch.from_numpy(rng.standard_normal((3, 90, 4)).astype(np.float32)).to(torch.bfloat16)
+    xb = X.view(torch.int16).numpy().view(np.uint16)
+    yb = Y.view(torch.int16).numpy().view(np.uint16)
+    Wb, bb = oracle_mod.ridge_fit(xb, yb, dtype=BF16)
+    Wf, bf = oracle_mod.ridge_fit(X.float().numpy(), Y.float().numpy(), dtype=F32)
+    np.testing.assert_array_equal(Wb, Wf)
+    np.testing.assert_array_equal(bb, bf)
+    W1, b1 = oracle_mod.ridge_fit(X[1:2].float().numpy(), Y[1:2].float().numpy(), dtype=F32)
+    np.testing.assert_array_equal(W1[0], Wf[1])
+    np.testing.assert_array_equal(b1[0], bf[1])
