@@ -49,14 +49,22 @@ WIDE_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "wide.hip")
 def kernel_source_digest(path: str = KERNEL_SRC) -> str:
     """sha256 of the kernel source's code: comments (from // to the end of a
     line) and blank lines removed, trailing spaces stripped, lines joined by
-    newlines.  Edits to comments keep recorded counters valid; edits to code
-    do not."""
-    lines = []
-    with open(path) as f:
-        for line in f:
-            code = line.split("//", 1)[0].rstrip()
-            if code:
-                lines.append(code)
+    newlines, followed by the code of the local headers it includes that
+    hold device code (every one but internal.hpp, the library's host-side
+    declarations).  Edits to comments keep recorded counters valid; edits to
+    code do not."""
+    def code_lines(p):
+        out = []
+        with open(p) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    out.append(code)
+        return out
+    lines = code_lines(path)
+    for line in list(lines):
+        if line.startswith('#include "') and line != '#include "internal.hpp"':
+            lines += code_lines(os.path.join(os.path.dirname(path), line.split('"')[1]))
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 

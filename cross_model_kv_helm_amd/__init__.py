@@ -26,7 +26,8 @@ STATUS = {0: "HELM_OK", 1: "HELM_E_INVALID_ARG", 2: "HELM_E_PAIR_SHAPE", 3: "HEL
 HELM_STAGE_TABLES, HELM_STAGE_MAP, HELM_STAGE_ALL = 1, 2, 3
 
 EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_stage", "helm_kv_transfer_paged", "helm_kv_cosine",
-            "helm_kv_transfer_wide", "helm_kv_transfer_wide_stage", "helm_kv_wide_workspace_bytes", "helm_kv_workspace_bytes",
+            "helm_kv_transfer_wide", "helm_kv_transfer_wide_stage", "helm_kv_wide_workspace_bytes",
+            "helm_ridge_fit", "helm_ridge_fit_stage", "helm_ridge_workspace_bytes", "helm_kv_workspace_bytes",
             "helm_kv_paged_workspace_bytes", "helm_mapper_check", "helm_paged_check",
             "helm_device_check", "helm_arch_supported", "helm_last_error", "helm_status_string",
             "helm_abi_version")
@@ -45,6 +46,16 @@ class HelmShape(ctypes.Structure):
         ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("n_tokens", ctypes.c_int64),
         ("rope_theta_src", ctypes.c_double), ("rope_theta_tgt", ctypes.c_double),
+        ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class HelmRidgeShape(ctypes.Structure):
+    _fields_ = [
+        ("n_groups", ctypes.c_int64), ("n_obs", ctypes.c_int64),
+        ("in_features", ctypes.c_int32), ("out_features", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("lambda_", ctypes.c_double),
         ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -83,6 +94,12 @@ def lib() -> ctypes.CDLL:
         L.helm_kv_transfer_stage.restype = ctypes.c_int
         L.helm_kv_transfer_wide.restype = ctypes.c_int
         L.helm_kv_transfer_wide.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
+        L.helm_ridge_workspace_bytes.restype = ctypes.c_size_t
+        L.helm_ridge_workspace_bytes.argtypes = [ctypes.POINTER(HelmRidgeShape)]
+        L.helm_ridge_fit.restype = ctypes.c_int
+        L.helm_ridge_fit.argtypes = [vp] * 4 + [ctypes.POINTER(HelmRidgeShape)]
+        L.helm_ridge_fit_stage.restype = ctypes.c_int
+        L.helm_ridge_fit_stage.argtypes = [ctypes.c_int] + [vp] * 4 + [ctypes.POINTER(HelmRidgeShape)]
         L.helm_kv_transfer_wide_stage.restype = ctypes.c_int
         L.helm_kv_transfer_wide_stage.argtypes = [ctypes.c_int] + [vp] * 11 + [ctypes.POINTER(HelmShape)]
         L.helm_kv_wide_workspace_bytes.restype = ctypes.c_size_t
@@ -367,3 +384,41 @@ def helm_kv_transfer_paged(src_k_pool, src_v_pool, src_block_table, tgt_block_ta
     s.workspace = workspace.data_ptr()
     s.workspace_bytes = workspace.numel()
     _raise(lib().helm_kv_transfer_paged(*ptrs, ctypes.byref(s)))
+
+
+def ridge_shape(n_groups: int, n_obs: int, in_features: int, out_features: int = 128, lam: float = 0.01,
+                dtype: int = HELM_BF16) -> HelmRidgeShape:
+    s = HelmRidgeShape()
+    s.n_groups, s.n_obs, s.in_features, s.out_features = n_groups, n_obs, in_features, out_features
+    s.dtype, s.lambda_ = dtype, lam
+    return s
+
+
+def helm_ridge_workspace_bytes(shape: HelmRidgeShape) -> int:
+    n = int(lib().helm_ridge_workspace_bytes(ctypes.byref(shape)))
+    if n == 0:
+        raise HelmError(1, helm_last_error())
+    return n
+
+
+def helm_ridge_fit(X, Y, lam: float = 0.01, W=None, b=None, workspace=None, stages: int = HELM_STAGE_ALL):
+    """Ridge fit of G maps (see include/helm_kv.h): X [G, N, IN] and Y
+    [G, N, 128] bf16 on the GPU.  Returns (W [G, IN, 128], b [G, 128]) fp32,
+    enqueued on torch's current stream."""
+    import torch
+    G, N, IN = X.shape
+    D = Y.shape[2]
+    shape = ridge_shape(G, N, IN, D, lam)
+    if W is None:
+        W = torch.empty((G, IN, D), dtype=torch.float32, device=X.device)
+    if b is None:
+        b = torch.empty((G, D), dtype=torch.float32, device=X.device)
+    ptrs = [_dev_ptr(X, "X", torch.bfloat16, (G, N, IN)), _dev_ptr(Y, "Y", torch.bfloat16, (G, N, D)),
+            _dev_ptr(W, "W", torch.float32, (G, IN, D)), _dev_ptr(b, "b", torch.float32, (G, D))]
+    shape.stream = current_stream_ptr(X.device)
+    if workspace is None:
+        workspace = torch.empty(helm_ridge_workspace_bytes(shape), dtype=torch.uint8, device=X.device)
+    shape.workspace = workspace.data_ptr()
+    shape.workspace_bytes = workspace.numel()
+    _raise(lib().helm_ridge_fit_stage(int(stages), *ptrs, ctypes.byref(shape)))
+    return W, b

@@ -156,6 +156,46 @@ int run_transfer(helm::XferArgs& a, int32_t dtype, const int32_t* src_pos, const
   return rc;
 }
 
+
+// ---- ridge fit ---------------------------------------------------------
+struct RidgeWorkspace {
+  size_t gram, cross, sums, M, total;   // byte offsets of each part, total size
+};
+
+int check_ridge_shape(const helm_ridge_shape_t* s) {
+  if (!s) return fail(HELM_E_INVALID_ARG, "shape is NULL");
+  if (s->dtype != HELM_BF16 && s->dtype != HELM_F32)
+    return fail(HELM_E_DTYPE, "unknown dtype code %d (HELM_BF16=0, HELM_F32=1)", s->dtype);
+  if (s->dtype != HELM_BF16) return fail(HELM_E_DTYPE, "the ridge fit takes bf16 observations only");
+  if (s->out_features != 128)
+    return fail(HELM_E_PAIR_SHAPE, "the ridge fit takes out_features = 128 (got %d)", s->out_features);
+  if (s->in_features < 128 || s->in_features > 1024 || s->in_features % 128)
+    return fail(HELM_E_PAIR_SHAPE, "in_features must be a multiple of 128 in [128, 1024] (got %d)",
+                s->in_features);
+  if (s->n_groups < 1 || s->n_obs < 1)
+    return fail(HELM_E_INVALID_ARG, "n_groups = %lld and n_obs = %lld must be >= 1", (long long)s->n_groups,
+                (long long)s->n_obs);
+  if (s->n_obs > 0xffffff00LL / (2LL * s->in_features))
+    return fail(HELM_E_INVALID_ARG, "one group's observations exceed 4 GB (n_obs = %lld)", (long long)s->n_obs);
+  if (!(s->lambda >= 0.0) || std::isinf(s->lambda))
+    return fail(HELM_E_INVALID_ARG, "lambda must be finite and >= 0");
+  if (s->n_groups > 0x7fffffffLL / helm::ridge_tiles_per_group(s->in_features))
+    return fail(HELM_E_INVALID_ARG, "too many groups (%lld)", (long long)s->n_groups);
+  return HELM_OK;
+}
+
+bool ridge_workspace_layout(const helm_ridge_shape_t* s, RidgeWorkspace& w) {
+  const int64_t G = s->n_groups, IN = s->in_features, D = s->out_features;
+  int64_t g = G, c = G, u = G, m = G;
+  if (!mul_ok(g, IN * IN * 4) || !mul_ok(c, IN * D * 4) || !mul_ok(u, (IN + D) * 4) || !mul_ok(m, IN * (IN + D) * 8))
+    return false;
+  w.gram = 0;
+  w.cross = align_up((size_t)g);
+  w.sums = w.cross + align_up((size_t)c);
+  w.M = w.sums + align_up((size_t)u);
+  w.total = w.M + align_up((size_t)m);
+  return true;
+}
 }  // namespace
 
 extern "C" {
@@ -580,6 +620,71 @@ int helm_kv_cosine(const void* k_mapped, const void* v_mapped, const void* k_ref
                                               s->dtype == HELM_BF16 ? helm::Dtype::BF16 : helm::Dtype::F32,
                                               cos_out, (hipStream_t)s->stream),
                        "KV-cosine kernel launch");
+}
+
+size_t helm_ridge_workspace_bytes(const helm_ridge_shape_t* s) {
+  clear_error();
+  if (check_ridge_shape(s) != HELM_OK) return 0;
+  RidgeWorkspace w;
+  if (!ridge_workspace_layout(s, w)) { fail(HELM_E_INVALID_ARG, "size overflow"); return 0; }
+  return w.total;
+}
+
+int helm_ridge_fit_stage(int stages, const void* X, const void* Y, float* W, float* b,
+                         const helm_ridge_shape_t* s) {
+  clear_error();
+  if (stages < 1 || stages > HELM_STAGE_ALL) return fail(HELM_E_INVALID_ARG, "stages = %d is not 1, 2 or 3", stages);
+  int rc = check_ridge_shape(s);
+  if (rc != HELM_OK) return rc;
+  if (!X || !Y || !W || !b) return fail(HELM_E_INVALID_ARG, "a tensor pointer is NULL");
+  if ((uintptr_t)X % 16 || (uintptr_t)Y % 16) return fail(HELM_E_INVALID_ARG, "X and Y must be 16-byte aligned");
+  const int64_t G = s->n_groups, N = s->n_obs, IN = s->in_features, D = s->out_features;
+  int64_t x_b = G, y_b = G, w_b = G, b_b = G;
+  if (!mul_ok(x_b, N) || !mul_ok(x_b, IN * 2) || !mul_ok(y_b, N) || !mul_ok(y_b, D * 2) || !mul_ok(w_b, IN * D * 4) ||
+      !mul_ok(b_b, D * 4))
+    return fail(HELM_E_INVALID_ARG, "tensor sizes overflow int64");
+  RidgeWorkspace w;
+  if (!ridge_workspace_layout(s, w)) return fail(HELM_E_INVALID_ARG, "size overflow");
+  if (!s->workspace || s->workspace_bytes < w.total)
+    return fail(HELM_E_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", s->workspace_bytes,
+                s->workspace, w.total);
+  if ((uintptr_t)s->workspace % kAlign)
+    return fail(HELM_E_WORKSPACE, "workspace %p is not %zu-byte aligned", s->workspace, kAlign);
+  const struct { const void* p; int64_t n; const char* name; } outs[] = {
+      {W, w_b, "W"}, {b, b_b, "b"}, {s->workspace, (int64_t)w.total, "the workspace"}};
+  const struct { const void* p; int64_t n; const char* name; } ins[] = {{X, x_b, "X"}, {Y, y_b, "Y"}};
+  for (int i = 0; i < 3; ++i) {
+    for (const auto& in : ins)
+      if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return fail(HELM_E_ALIAS, "%s overlaps %s", outs[i].name, in.name);
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(HELM_E_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  char* ws = (char*)s->workspace;
+  helm::RidgeFit f{};
+  f.X = X;
+  f.Y = Y;
+  f.gram = (float*)(ws + w.gram);
+  f.cross = (float*)(ws + w.cross);
+  f.sums = (float*)(ws + w.sums);
+  f.M = (double*)(ws + w.M);
+  f.W = W;
+  f.b = b;
+  f.G = G;
+  f.N = N;
+  f.IN = (int32_t)IN;
+  f.D = (int32_t)D;
+  f.lambda = s->lambda;
+  if (!helm::ridge_supports(f)) return fail(HELM_E_INVALID_ARG, "shape outside the ridge kernels' limits");
+  rc = device_gate(-1);
+  if (rc != HELM_OK) return rc;
+  return launch_status(helm::launch_ridge(f, stages & HELM_STAGE_TABLES, stages & HELM_STAGE_MAP,
+                                          (hipStream_t)s->stream),
+                       "ridge fit launch");
+}
+
+int helm_ridge_fit(const void* X, const void* Y, float* W, float* b, const helm_ridge_shape_t* s) {
+  return helm_ridge_fit_stage(HELM_STAGE_ALL, X, Y, W, b, s);
 }
 
 }  // extern "C"

@@ -102,6 +102,27 @@ bool wide_supports(const WideXfer& x);
 // (reads rope_src); product: the map itself, reading them.
 hipError_t launch_wide(const WideXfer& x, bool prep, bool product, hipStream_t stream);
 
+// Ridge fit of G maps (bf16 observations, D = 128 targets, IN a multiple of
+// 128 up to 1024): gram/cross/sums/M are workspace, W [G, IN, D] and
+// b [G, D] the fp32 results.
+struct RidgeFit {
+  const void* X;     // [G, N, IN] bf16
+  const void* Y;     // [G, N, D] bf16
+  float* gram;       // [G, IN, IN]
+  float* cross;      // [G, IN, D]
+  float* sums;       // [G, IN + D]
+  double* M;         // [G, IN, IN + D]
+  float* W;
+  float* b;
+  int64_t G, N;
+  int32_t IN, D;
+  double lambda;
+};
+int64_t ridge_tiles_per_group(int32_t IN);
+bool ridge_supports(const RidgeFit& f);
+// gram: the products and sums into the workspace; solve: the fit from them.
+hipError_t launch_ridge(const RidgeFit& f, bool gram, bool solve, hipStream_t stream);
+
 // Matrix-core transfer kernel for bf16 storage.  Returns hipErrorNotSupported
 // (and enqueues nothing) when the shape is outside what it handles.
 hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream);

@@ -1,0 +1,519 @@
+// ridge.hip — the ridge fit of the maps (the Qwen3 cache-mapping write-up,
+// section "A linear bridge, strangely enough, suffices": every target head's
+// key map and value map are fitted separately, by ridge regression on
+// centred data with lambda = 0.01, the bias from the means).
+//
+// Per group g (one (target layer, head, K|V) map) with observations
+// X [N, IN] and targets Y [N, D]:
+//   W = (Xc^T Xc + lambda I)^-1 Xc^T Yc,   b = mean(Y) - mean(X) W
+// (Xc, Yc the centred data).  The centred products follow from one pass
+// over the raw data: Xc^T Xc = X^T X - sx sx^T / N and Xc^T Yc = X^T Y -
+// sx sy^T / N with the column sums sx, sy.
+//
+// Design for MI355X:
+//   * Gram kernel (matrix cores, the hot loop: 2 N IN (IN + D) flop per
+//     group): X^T X and X^T Y contract over the observations, but X is
+//     stored observation-major, so a fragment (8 observations of one
+//     feature per lane) is not contiguous in memory.  Operand tiles of 64
+//     observations x 256 features are copied to LDS as they are stored
+//     (buffer -> LDS DMA, double-buffered) and every fragment is read with
+//     two ds_read_b64_tr_b16: within each 16-lane group, lane 4e+q names 4
+//     consecutive features of observation e and receives feature q' = lane/4
+//     ... of the 4 observations named by lanes q', 4+q', 8+q', 12+q'
+//     (measured lane layout), i.e. the transpose a fragment needs.  Tile rows
+//     are XOR-swizzled in 16-byte pieces (slot = piece ^ 4*((t%4) + 4*((t/8)%2)))
+//     so the 8 observation rows one read touches fall in 8 different bank
+//     groups.  Tiles: 256 x 256 outputs, four waves of 128 x 128 (fp32
+//     accumulators), one group's tiles on one XCD.  Only the upper tiles of
+//     the symmetric X^T X are formed; the X^T Y tiles have 128 spare columns,
+//     whose waves form the column sums as products with a constant fragment
+//     of ones (a contraction the matrix cores do anyway, the data read once).
+//   * Solve kernel (fp64, one workgroup per group): the centred normal
+//     matrix plus lambda I in upper storage, a blocked Cholesky A = U^T U in
+//     16-wide panels with the forward substitution of the right-hand sides
+//     folded into the panel updates, then the back substitution, W in fp32
+//     and b from the means.
+#include "internal.hpp"
+#include "lds_dma.hpp"
+
+namespace helm {
+namespace {
+
+using lds::dma16;
+using lds::kSkip;
+using lds::lds_barrier;
+using lds::rsrc_words;
+using lds::wait_vmcnt;
+typedef lds::u32x4 u32x4;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kD = 128;            // target features per map
+constexpr int kFT = 256;           // features per tile side
+constexpr int kKB = 64;            // observations per pipeline step
+constexpr int kRowBytes = kFT * 2; // one observation row of a tile (512 B, 32 pieces)
+constexpr int kThreads = 256;
+constexpr int kPer = 8;            // copy instructions per wave, operand and step (32 KB tile / 4 waves / 1 KB)
+constexpr int kMaxIn = 1024;       // largest input width the solve kernel holds
+
+enum Role { kProducts = 0, kSums = 1, kIdle = 2 };
+
+struct GramArgs {
+  const uint16_t* X;     // [G, N, IN] bf16
+  const uint16_t* Y;     // [G, N, D] bf16
+  float* gram;           // [G, IN, IN] fp32 (upper 256-tiles written)
+  float* cross;          // [G, IN, D] fp32
+  float* sums;           // [G, IN + D] fp32: column sums of X, then of Y
+  int64_t N;
+  int32_t G, IN, nX;     // nX = column tiles of X (IN / 256 rounded up)
+  int32_t tiles;         // per group: nX (nX + 1) / 2 upper tiles + nX cross tiles
+};
+
+// Swizzle of observation row t (multiples of 4 in 0..28: XOR on piece bits 2..4).
+__device__ __forceinline__ int row_swz(int t) { return 4 * ((t & 3) + 4 * ((t >> 3) & 1)); }
+
+__device__ __forceinline__ bf16x8 read_frag(const char* tile, uint32_t lane_off, int ks) {
+  // rows 16ks + 4r + (lane's e and k-group): the uniform part of the address
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + lane_off + (16 * ks) * kRowBytes));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + lane_off + (16 * ks + 4) * kRowBytes));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+struct GramSmem {
+  char A[2][kKB * kRowBytes] __attribute__((aligned(16)));
+  char B[2][kKB * kRowBytes] __attribute__((aligned(16)));
+};
+
+template <int ROLE>
+__device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int64_t g, int rt, int ct, int w,
+                                           int lane, f32x16 (&acc)[4][4]) {
+  const int wm = w >> 1, wn = w & 1;
+  const bool cross_tile = ct == a.nX;
+  const int64_t N = a.N;
+  const int IN = a.IN;
+  const int n_steps = (int)((N + kKB - 1) / kKB);
+  const uint16_t* Xg = a.X + g * N * IN;
+  const uint16_t* Yg = a.Y + g * N * kD;
+
+  // ---- copies: wave w issues instructions n = w + 4jj (jj < 8) of each
+  // operand; instruction n fills tile rows 2n, 2n+1, lane i row 2n + i/32,
+  // slot i % 32, i.e. the piece (i % 32) ^ row_swz(row).  A: X features
+  // 256 rt + 8 piece; B: X features 256 ct + 8 piece, or Y features 8 piece
+  // (pieces past 15 of Y, and features past IN, read zeros).
+  const int slot_i = lane & 31;
+  auto piece_of = [&](int jj) __attribute__((always_inline)) {
+    const int r = 2 * (w + 4 * jj) + (lane >> 5);
+    return slot_i ^ row_swz(r);
+  };
+  auto a_voff = [&](int jj) __attribute__((always_inline)) {
+    const int r = 2 * (w + 4 * jj) + (lane >> 5);
+    const int f = kFT * rt + 8 * piece_of(jj);
+    return f < IN ? (uint32_t)r * IN * 2 + 2 * f : kSkip;
+  };
+  auto b_voff = [&](int jj) __attribute__((always_inline)) {
+    const int r = 2 * (w + 4 * jj) + (lane >> 5);
+    if (cross_tile) {
+      const int p = piece_of(jj);
+      return p < kD / 8 ? (uint32_t)r * kD * 2 + 16 * p : kSkip;
+    }
+    const int f = kFT * ct + 8 * piece_of(jj);
+    return f < IN ? (uint32_t)r * IN * 2 + 2 * f : kSkip;
+  };
+  // descriptors of step s: the observations from 64 s on (rows past N read zeros)
+  auto a_rsrc = [&](int s) __attribute__((always_inline)) {
+    const int64_t t0 = (int64_t)s * kKB;
+    return rsrc_words(Xg + t0 * IN, (uint32_t)((N - t0) * IN * 2));
+  };
+  auto b_rsrc = [&](int s) __attribute__((always_inline)) {
+    const int64_t t0 = (int64_t)s * kKB;
+    return cross_tile ? rsrc_words(Yg + t0 * kD, (uint32_t)((N - t0) * kD * 2))
+                      : rsrc_words(Xg + t0 * IN, (uint32_t)((N - t0) * IN * 2));
+  };
+  auto copy_one = [&](int p, int q, const u32x4& ra, const u32x4& rb) __attribute__((always_inline)) {
+    if (q < kPer)
+      dma16(ra, a_voff(q), 0, sm.A[p] + 1024 * (w + 4 * q));
+    else
+      dma16(rb, b_voff(q - kPer), 0, sm.B[p] + 1024 * (w + 4 * (q - kPer)));
+  };
+
+  // ---- fragment reads: lane l (16-lane group gg = l/16: feature half fb =
+  // gg%2, k-group kg = gg/2; in the group e = (l%16)/4, q = l%4) names
+  // observation row 8kg + e (+ 16ks + 4r) and features 32mb + 16fb + 4q ..
+  // +3 of its wave's 128; it receives feature 32mb + 16fb + l%16 of 4 rows.
+  const int gg = lane >> 4, fb = gg & 1, kg = gg >> 1, e = (lane >> 2) & 3, q4 = lane & 3;
+  const int trow = 8 * kg + e;
+  const uint32_t row_base = (uint32_t)trow * kRowBytes + 8 * (q4 & 1);
+  // A rows: the wave's 128 X features (the sums waves read the same rows as
+  // the products waves of their row half); B columns likewise
+  const int a_half = wm, b_half = (ROLE == kSums) ? 0 : wn;
+  uint32_t a_off[4], b_off[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int pa = 16 * a_half + 4 * mb + 2 * fb + (q4 >> 1);
+    const int pb = 16 * b_half + 4 * mb + 2 * fb + (q4 >> 1);
+    a_off[mb] = row_base + 16 * (pa ^ row_swz(trow));
+    b_off[mb] = row_base + 16 * (pb ^ row_swz(trow));
+  }
+  // constant fragment: 1.0 in row (column) 0 of its 32, 0 elsewhere
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (lane & 31) == 0 ? (__bf16)1.0f : (__bf16)0.0f;
+
+  // step 0 in flight, then the pipeline: the copies of step s+1 go out
+  // between the first 32 products of step s
+  {
+    const u32x4 ra = a_rsrc(0), rb = b_rsrc(0);
+#pragma unroll
+    for (int q = 0; q < 2 * kPer; ++q) copy_one(0, q, ra, rb);
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+  for (int s = 0; s < n_steps; ++s) {
+    const int p = s & 1;
+    const bool more = s + 1 < n_steps;
+    const u32x4 ra = a_rsrc(more ? s + 1 : s), rb = b_rsrc(more ? s + 1 : s);
+    const char* At = sm.A[p];
+    const char* Bt = sm.B[p];
+#pragma unroll
+    for (int ks = 0; ks < kKB / 16; ++ks) {
+      bf16x8 af[4], bfr[4];
+      if constexpr (ROLE != kIdle) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          af[i] = read_frag(At, a_off[i], ks);
+          bfr[i] = read_frag(Bt, b_off[i], ks);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          if constexpr (ROLE == kProducts) {
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+          } else if constexpr (ROLE == kSums) {
+            // acc[0][mb]: sums of the wave's X features (times a ones column);
+            // acc[1][nb]: sums of the Y features (a ones row times Y)
+            if (nb == 0) acc[0][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], ones, acc[0][mb], 0, 0, 0);
+            if (mb == 0) acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, bfr[nb], acc[1][nb], 0, 0, 0);
+          }
+          const int m = 16 * ks + 4 * mb + nb;
+          if (more && (m & 1) && m / 2 < 2 * kPer) copy_one(p ^ 1, m / 2, ra, rb);
+        }
+    }
+    wait_vmcnt<0>();
+    lds_barrier();   // step s+1 landed everywhere; everyone is done with buffer p
+  }
+}
+
+__global__ void __launch_bounds__(kThreads, 1) ridge_gram_kernel(GramArgs a) {
+  __shared__ GramSmem sm;
+  // tile of this workgroup: with groups a multiple of 8, all tiles of group
+  // g run on XCD g % 8 (workgroup id mod 8) and share its L2
+  const int64_t b = blockIdx.x;
+  int64_t g;
+  int t;
+  if (a.G % 8 == 0) {
+    const int64_t q = b / 8;
+    g = b % 8 + 8 * (q / a.tiles);
+    t = (int)(q % a.tiles);
+  } else {
+    g = b / a.tiles;
+    t = (int)(b % a.tiles);
+  }
+  // tile t: the upper X^T X tiles (rt <= ct) in row order, then X^T Y for
+  // every row tile (ct = nX)
+  int rt = 0, ct;
+  const int n_upper = a.nX * (a.nX + 1) / 2;
+  if (t < n_upper) {
+    int left = t;
+    while (left >= a.nX - rt) {
+      left -= a.nX - rt;
+      ++rt;
+    }
+    ct = rt + left;
+  } else {
+    rt = t - n_upper;
+    ct = a.nX;
+  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const bool cross_tile = ct == a.nX;
+  const int IN = a.IN;
+  // role of this wave: products where its rows and columns are real
+  // features (the lower half of a diagonal tile is the mirror of the upper:
+  // skipped), column sums in the spare half of a cross tile
+  int role;
+  const bool rows_ok = kFT * rt + 128 * wm < IN;
+  if (cross_tile)
+    role = !rows_ok ? kIdle : wn == 0 ? kProducts : kSums;
+  else
+    role = (rows_ok && kFT * ct + 128 * wn < IN && !(rt == ct && wm > wn)) ? kProducts : kIdle;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  if (role == kProducts)
+    gram_steps<kProducts>(a, sm, g, rt, ct, w, lane, acc);
+  else if (role == kSums)
+    gram_steps<kSums>(a, sm, g, rt, ct, w, lane, acc);
+  else
+    gram_steps<kIdle>(a, sm, g, rt, ct, w, lane, acc);
+
+  // ---- epilogue: accumulator register r of a 32 x 32 block holds row
+  // 8(r/4) + 4(lane/32) + r%4, column lane%32
+  const int col = lane & 31, rgrp = 4 * (lane >> 5);
+  if (role == kProducts) {
+    float* out;
+    int64_t ld;
+    int c0;
+    if (cross_tile) {
+      out = a.cross + g * (int64_t)IN * kD;
+      ld = kD;
+      c0 = 0;
+    } else {
+      out = a.gram + g * (int64_t)IN * IN;
+      ld = IN;
+      c0 = kFT * ct + 128 * wn;
+    }
+    const int r0 = kFT * rt + 128 * wm;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = r0 + 32 * mb + 8 * (r >> 2) + rgrp + (r & 3);
+          out[(int64_t)row * ld + c0 + 32 * nb + col] = acc[mb][nb][r];
+        }
+  } else if (role == kSums) {
+    float* sums = a.sums + g * (int64_t)(IN + kD);
+    // X sums: column 0 of acc[0][mb] (lanes 0 and 32), rows of the wave's half
+    if (col == 0) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sums[kFT * rt + 128 * wm + 32 * mb + 8 * (r >> 2) + rgrp + (r & 3)] = acc[0][mb][r];
+    }
+    // Y sums: row 0 of acc[1][nb] (register 0, lanes 0..31), once per group
+    if (rt == 0 && wm == 0 && lane < 32) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) sums[IN + 32 * nb + col] = acc[1][nb][0];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- solve
+constexpr int kP = 16;   // panel width of the Cholesky
+
+struct SolveArgs {
+  const float* gram;     // [G, IN, IN] (upper tiles)
+  const float* cross;    // [G, IN, D]
+  const float* sums;     // [G, IN + D]
+  double* M;             // [G, IN, IN + D] fp64 workspace: upper A | right-hand sides
+  float* W;              // [G, IN, D]
+  float* b;              // [G, D]
+  int64_t N;
+  int32_t IN;
+  double lambda;
+};
+
+struct SolveSmem {
+  double Dg[kP][kP + 1];
+  double Pn[kP][kMaxIn + kD - kP];
+};
+
+__global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
+  __shared__ SolveSmem sm;
+  const int64_t g = blockIdx.x;
+  const int n = a.IN, ld = n + kD, tid = threadIdx.x;
+  const double invN = 1.0 / (double)a.N;
+  const float* G = a.gram + g * (int64_t)n * n;
+  const float* C = a.cross + g * (int64_t)n * kD;
+  const float* sx = a.sums + g * (int64_t)(n + kD);
+  const float* sy = sx + n;
+  double* M = a.M + g * (int64_t)n * ld;
+
+  // centred normal matrix + lambda I (upper: row j, columns i >= j) and
+  // centred right-hand sides X^T Y - sx sy^T / N
+  for (int j = 0; j < n; ++j) {
+    const double sj = sx[j];
+    for (int i = j + tid; i < ld; i += kThreads) {
+      double v;
+      if (i < n)
+        v = (double)G[(int64_t)j * n + i] - sj * (double)sx[i] * invN + (i == j ? a.lambda : 0.0);
+      else
+        v = (double)C[(int64_t)j * kD + (i - n)] - sj * (double)sy[i - n] * invN;
+      M[(int64_t)j * ld + i] = v;
+    }
+  }
+  __syncthreads();
+
+  // ---- A = U^T U, forward substitution U^T Z = B folded in: panel k0
+  for (int k0 = 0; k0 < n; k0 += kP) {
+    // diagonal block, factored in LDS
+    for (int e = tid; e < kP * kP; e += kThreads) {
+      const int r = e / kP, c = e % kP;
+      if (c >= r) sm.Dg[r][c] = M[(int64_t)(k0 + r) * ld + k0 + c];
+    }
+    __syncthreads();
+    for (int r = 0; r < kP; ++r) {
+      if (tid == 0) sm.Dg[r][r] = sqrt(sm.Dg[r][r]);   // a non-positive pivot gives NaN
+      __syncthreads();
+      if (tid > r && tid < kP) sm.Dg[r][tid] /= sm.Dg[r][r];
+      __syncthreads();
+      for (int e = tid; e < kP * kP; e += kThreads) {
+        const int s = e / kP, c = e % kP;
+        if (s > r && c >= s) sm.Dg[s][c] -= sm.Dg[r][s] * sm.Dg[r][c];
+      }
+      __syncthreads();
+    }
+    for (int e = tid; e < kP * kP; e += kThreads) {
+      const int r = e / kP, c = e % kP;
+      if (c >= r) M[(int64_t)(k0 + r) * ld + k0 + c] = sm.Dg[r][c];
+    }
+    // panel rows k0 .. k0+15, columns past the block (the rest of U's rows
+    // and the right-hand sides): solve U_kk^T X = panel, one column a thread
+    const int m0 = k0 + kP, width = ld - m0;
+    for (int c = tid; c < width; c += kThreads) {
+      double x[kP];
+#pragma unroll
+      for (int r = 0; r < kP; ++r) {
+        double v = M[(int64_t)(k0 + r) * ld + m0 + c];
+#pragma unroll
+        for (int p = 0; p < r; ++p) v -= sm.Dg[p][r] * x[p];
+        x[r] = v / sm.Dg[r][r];
+      }
+#pragma unroll
+      for (int r = 0; r < kP; ++r) {
+        sm.Pn[r][c] = x[r];
+        M[(int64_t)(k0 + r) * ld + m0 + c] = x[r];
+      }
+    }
+    __syncthreads();
+    // trailing update: row s >= m0, column j >= s (A part) or any column of
+    // the right-hand sides: M[s][j] -= sum_r Pn[r][s - m0] Pn[r][j - m0]
+    for (int c = tid; c < width; c += kThreads) {
+      const int j = m0 + c;
+      double col[kP];
+#pragma unroll
+      for (int r = 0; r < kP; ++r) col[r] = sm.Pn[r][c];
+      const int s_end = j < n ? j : n - 1;
+      for (int s = m0; s <= s_end; ++s) {
+        double v = 0.0;
+#pragma unroll
+        for (int r = 0; r < kP; ++r) v += sm.Pn[r][s - m0] * col[r];
+        M[(int64_t)s * ld + j] -= v;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- back substitution U W = Z, panels from the last: W_K from the
+  // diagonal block, then Z rows above it lose U[j][K] W_K
+  for (int k0 = ((n - 1) / kP) * kP; k0 >= 0; k0 -= kP) {
+    for (int e = tid; e < kP * kP; e += kThreads) {
+      const int r = e / kP, c = e % kP;
+      if (c >= r) sm.Dg[r][c] = M[(int64_t)(k0 + r) * ld + k0 + c];
+    }
+    __syncthreads();
+    if (tid < kD) {
+      double wv[kP];
+#pragma unroll
+      for (int r = kP - 1; r >= 0; --r) {
+        double v = M[(int64_t)(k0 + r) * ld + n + tid];
+#pragma unroll
+        for (int p = r + 1; p < kP; ++p) v -= sm.Dg[r][p] * wv[p];
+        wv[r] = v / sm.Dg[r][r];
+      }
+#pragma unroll
+      for (int r = 0; r < kP; ++r) {
+        M[(int64_t)(k0 + r) * ld + n + tid] = wv[r];
+        sm.Pn[r][tid] = wv[r];
+      }
+    }
+    __syncthreads();
+    // rows j < k0: two threads per right-hand column, rows split in halves
+    {
+      const int d = tid % kD, half = tid / kD;
+      double wv[kP];
+#pragma unroll
+      for (int r = 0; r < kP; ++r) wv[r] = sm.Pn[r][d];
+      for (int j = half; j < k0; j += 2) {
+        const double* urow = M + (int64_t)j * ld + k0;
+        double v = 0.0;
+#pragma unroll
+        for (int r = 0; r < kP; ++r) v += urow[r] * wv[r];
+        M[(int64_t)j * ld + n + d] -= v;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- outputs: W in fp32; b = mean(Y) - mean(X) W in fp64
+  float* Wg = a.W + g * (int64_t)n * kD;
+  for (int e = tid; e < n * kD; e += kThreads) {
+    const int i = e / kD, d = e % kD;
+    Wg[e] = (float)M[(int64_t)i * ld + n + d];
+  }
+  if (tid < kD) {
+    double v = (double)sy[tid] * invN;
+    for (int i = 0; i < n; ++i) v -= (double)sx[i] * invN * M[(int64_t)i * ld + n + tid];
+    a.b[g * kD + tid] = (float)v;
+  }
+}
+
+}  // namespace
+
+int64_t ridge_tiles_per_group(int32_t IN) {
+  const int64_t nX = (IN + kFT - 1) / kFT;
+  return nX * (nX + 1) / 2 + nX;
+}
+
+bool ridge_supports(const RidgeFit& f) {
+  auto al = [](const void* p) { return ((uintptr_t)p % 16) == 0; };
+  return f.D == kD && f.IN >= 128 && f.IN <= kMaxIn && f.IN % 128 == 0 && f.N >= 1 &&
+         f.N * f.IN * 2 <= (int64_t)kSkip && f.G >= 1 && f.G <= 0x7fffffffLL / ridge_tiles_per_group(f.IN) &&
+         al(f.X) && al(f.Y);
+}
+
+hipError_t launch_ridge(const RidgeFit& f, bool gram, bool solve, hipStream_t stream) {
+  if (!ridge_supports(f)) return hipErrorNotSupported;
+  if (gram) {
+    GramArgs a{};
+    a.X = (const uint16_t*)f.X;
+    a.Y = (const uint16_t*)f.Y;
+    a.gram = f.gram;
+    a.cross = f.cross;
+    a.sums = f.sums;
+    a.N = f.N;
+    a.G = (int32_t)f.G;
+    a.IN = f.IN;
+    a.nX = (f.IN + kFT - 1) / kFT;
+    a.tiles = (int32_t)ridge_tiles_per_group(f.IN);
+    hipLaunchKernelGGL(ridge_gram_kernel, dim3((unsigned)(f.G * a.tiles)), dim3(kThreads), 0, stream, a);
+  }
+  if (solve) {
+    SolveArgs s{};
+    s.gram = f.gram;
+    s.cross = f.cross;
+    s.sums = f.sums;
+    s.M = f.M;
+    s.W = f.W;
+    s.b = f.b;
+    s.N = f.N;
+    s.IN = f.IN;
+    s.lambda = f.lambda;
+    hipLaunchKernelGGL(ridge_solve_kernel, dim3((unsigned)f.G), dim3(kThreads), 0, stream, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace helm

@@ -43,16 +43,22 @@
 //   * Epilogue from registers: bias, the forward rotation at tgt_pos (keys;
 //     fp32 tables from the RoPE table kernel), round to bf16, store.
 #include "internal.hpp"
+#include "lds_dma.hpp"
 
 namespace helm {
 namespace {
 
+using lds::dma16;
+using lds::kSkip;
+using lds::lds_barrier;
+using lds::rsrc_words;
+using lds::wait_vmcnt;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef lds::u32x4 u32x4;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef __attribute__((address_space(3))) void* lds_void_t;
 
 constexpr int kD = 128;
 constexpr int kHalf = 64;
@@ -68,7 +74,6 @@ constexpr int kRowsPerCopy = 64 / kRowPieces;   // tile rows per 1 KB copy instr
 constexpr int kPer = kRowPieces;           // copy instructions per wave, operand and step
 constexpr int kCopyStride = 32 / (2 * kPer) > 0 ? 32 / (2 * kPer) : 1;   // products between two copies (spread over 32)
 static_assert(kKB % 16 == 0 && 16 % kRowPieces == 0 && kBufs >= 2 && kBufs <= 5 && (kBufs - 2) * 2 * kPer < 64, "pipeline shape");
-constexpr uint32_t kSkip = 0xffffff00u;    // offset past every descriptor: zero load
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -76,43 +81,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   v[0] = (__bf16)a;
   v[1] = (__bf16)b;
   return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t p = (uint64_t)(uintptr_t)base;
-  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
-}
-
-// Buffer -> LDS copy of 16 bytes per lane: lane i reads the 16 bytes at
-// byte offset voff + soff of the buffer `rsrc` and they land at lds_base +
-// 16*i.  rsrc, soff and lds_base are wave-uniform.  Inline assembly so that
-// the compiler does not make later LDS accesses wait for the copy; the
-// kernel waits for its copies itself (wait_vmcnt) before the barrier that
-// publishes a tile.
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t soff, const void* lds_base) {
-  const uint32_t m = (uint32_t)(uintptr_t)(lds_void_t)lds_base;
-  asm("" : "+s"(soff));   // a constant offset above 64 is no inline operand: keep it in a register
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(soff), "s"(m)
-               : "memory", "m0");
-}
-
-// Waits until at most N of this wave's vector memory operations (here only
-// the copies) are outstanding; they complete in issue order.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // 16-byte slot of piece c of tile row r (XOR swizzle, see the header): the

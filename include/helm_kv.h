@@ -273,6 +273,53 @@ int helm_kv_cosine(const void* k_mapped, const void* v_mapped,
                    const void* k_ref, const void* v_ref,
                    float* cos_out, const helm_shape_t* shape);
 
+/* Ridge fit of the maps (the Qwen3 cache-mapping write-up, section "A
+ * linear bridge, strangely enough, suffices": each target head's key map
+ * and value map are fitted separately by ridge regression on centred data,
+ * lambda = 0.01, the bias from the means).  For each of n_groups
+ * independent groups g (one (target layer, head, K|V) map each), with
+ * observations X[g] [N, IN] and targets Y[g] [N, D]:
+ *   W[g] = (Xc^T Xc + lambda I)^-1 Xc^T Yc,   b[g] = mean(Y[g]) - mean(X[g]) W[g]
+ * (Xc, Yc = the data minus its column means).  X^T X, X^T Y and the column
+ * sums are accumulated in fp32 on the matrix cores (bf16 products are
+ * exact); the centring, lambda, the Cholesky solve and b are fp64; W and b
+ * are stored as fp32.
+ *   X : [n_groups, n_obs, in_features] bf16, device, 16-byte aligned
+ *   Y : [n_groups, n_obs, out_features] bf16, device, 16-byte aligned
+ *   W : [n_groups, in_features, out_features] fp32 (in-major, the layout of
+ *       the transfer's maps), caller-owned
+ *   b : [n_groups, out_features] fp32, caller-owned
+ * Limits: dtype HELM_BF16 (HELM_E_DTYPE otherwise); out_features 128 and
+ * in_features a multiple of 128 up to 1024 (HELM_E_PAIR_SHAPE otherwise);
+ * n_obs >= 1 with n_obs * in_features * 2 below 4 GB; lambda >= 0.  A group
+ * whose normal matrix is not positive definite (possible only with
+ * lambda = 0) gets NaN in its W and b.  Enqueued on shape->stream; nothing
+ * is enqueued on an error; W, b and the workspace must not overlap X, Y or
+ * each other (HELM_E_ALIAS). */
+typedef struct {
+  int64_t n_groups;        /* G >= 1 */
+  int64_t n_obs;           /* N >= 1 observations per group */
+  int32_t in_features;     /* IN */
+  int32_t out_features;    /* D */
+  int32_t dtype;           /* helm_dtype_t of X and Y */
+  double lambda;           /* ridge penalty, >= 0 (0.01 on the pages) */
+  void* stream;            /* hipStream_t */
+  void* workspace;         /* device scratch, 256-byte aligned */
+  size_t workspace_bytes;
+} helm_ridge_shape_t;
+/* Workspace bytes of a fit (0 on an invalid shape): the fp32 products
+ * [G, IN, IN] and [G, IN, D], the sums [G, IN + D] and the fp64 solve
+ * matrix [G, IN, IN + D] (1,024 groups of IN = 512: 4.2 GB). */
+size_t helm_ridge_workspace_bytes(const helm_ridge_shape_t* shape);
+int helm_ridge_fit(const void* X, const void* Y, float* W, float* b, const helm_ridge_shape_t* shape);
+/* The fit in two separately enqueued stages: HELM_STAGE_TABLES (1) the
+ * products and sums into the workspace, HELM_STAGE_MAP (2) the solve
+ * reading them (the workspace must hold the first stage's results of the
+ * same X, Y and shape, ordered before; not checked), HELM_STAGE_ALL (3)
+ * both.  For timing the stages alone; same checks and return convention. */
+int helm_ridge_fit_stage(int stages, const void* X, const void* Y, float* W, float* b,
+                         const helm_ridge_shape_t* shape);
+
 /* Workspace bytes the call with this shape needs (0 on an invalid shape;
  * helm_last_error() then says why).  Pure host arithmetic. */
 size_t helm_kv_workspace_bytes(const helm_shape_t* shape);

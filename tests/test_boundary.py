@@ -227,3 +227,38 @@ def test_wide_map_workspace_and_refusals():
         assert L.helm_kv_transfer_wide_stage(stages, *fake, ctypes.byref(s)) == 7
     for stages in (0, 4, -1):
         assert L.helm_kv_transfer_wide_stage(stages, *fake, ctypes.byref(s)) == 1
+
+
+def test_ridge_workspace_and_refusals():
+    """helm_ridge_fit / helm_ridge_workspace_bytes: bf16, out_features 128,
+    in_features a multiple of 128 up to 1024; the workspace holds the fp32
+    products and sums and the fp64 solve matrix; every refusal comes before
+    any device access."""
+    L = hk.lib()
+    s = hk.ridge_shape(1024, 131072, 512)
+    n = hk.helm_ridge_workspace_bytes(s)
+    assert n == 1024 * (512 * 512 * 4 + 512 * 128 * 4 + 640 * 4 + 512 * 640 * 8)
+    fake = [ctypes.c_void_p((1 << 40) * (i + 1)) for i in range(4)]     # far apart: no overlaps
+    assert L.helm_ridge_fit(*fake, ctypes.byref(hk.ridge_shape(2, 100, 256, dtype=hk.HELM_F32))) == 5
+    assert "bf16" in hk.helm_last_error()
+    assert L.helm_ridge_fit(*fake, ctypes.byref(hk.ridge_shape(2, 100, 256, out_features=64))) == 2
+    for IN in (64, 200, 1152):
+        assert L.helm_ridge_fit(*fake, ctypes.byref(hk.ridge_shape(2, 100, IN))) == 2
+        assert L.helm_ridge_workspace_bytes(ctypes.byref(hk.ridge_shape(2, 100, IN))) == 0
+    assert L.helm_ridge_fit(*fake, ctypes.byref(hk.ridge_shape(2, 0, 256))) == 1
+    assert L.helm_ridge_fit(*fake, ctypes.byref(hk.ridge_shape(0, 10, 256))) == 1
+    assert L.helm_ridge_fit(*fake, ctypes.byref(hk.ridge_shape(2, 10, 256, lam=-1.0))) == 1
+    assert L.helm_ridge_fit(*fake, ctypes.byref(hk.ridge_shape(2, 10, 256, lam=float("nan")))) == 1
+    assert L.helm_ridge_fit(*fake, ctypes.byref(hk.ridge_shape(1, 1 << 22, 1024))) == 1   # one group over 4 GB
+    s = hk.ridge_shape(2, 100, 256)
+    assert L.helm_ridge_fit(*fake, ctypes.byref(s)) == 7                                   # no workspace
+    s.workspace, s.workspace_bytes = (1 << 40) * 8, hk.helm_ridge_workspace_bytes(s)
+    assert L.helm_ridge_fit(fake[0], fake[1], fake[0], fake[3], ctypes.byref(s)) == 8      # W overlaps X
+    assert L.helm_ridge_fit(fake[0], fake[1], fake[2], fake[2], ctypes.byref(s)) == 8      # b overlaps W
+    s.workspace = fake[1].value
+    assert L.helm_ridge_fit(*fake, ctypes.byref(s)) == 8                                   # workspace overlaps Y
+    s.workspace = (1 << 40) * 8 + 16
+    assert L.helm_ridge_fit(*fake, ctypes.byref(s)) == 7                                   # misaligned
+    for stages in (0, 4):
+        assert L.helm_ridge_fit_stage(stages, *fake, ctypes.byref(s)) == 1
+    assert L.helm_ridge_fit(None, *fake[1:], ctypes.byref(s)) == 1

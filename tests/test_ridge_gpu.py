@@ -1,0 +1,145 @@
+"""GPU parity of the ridge fit (helm_ridge_fit) against the fp64 oracle
+(oracle.ridge_fit), through the C ABI.
+
+The Qwen3 cache-mapping write-up, section "A linear bridge, strangely enough,
+suffices": each map is fitted by ridge regression on centred data with
+lambda = 0.01, the bias from the means.
+
+Tolerance, derived from the arithmetic.  The library accumulates X^T X,
+X^T Y and the column sums in fp32 from exact bf16 products, 16 products per
+matrix instruction, so an entry carries at most (N/16) * 2^-24 * sum|x_i x_j|
+of rounding error; the centring subtracts sx sx^T / N (in fp64), so relative
+to the centred matrix A the error is bounded by
+    eps_A = (N/16) * 2^-24 * (1 + max mean^2 / min variance) * (a small factor).
+A solve turns that into at most cond(A) * eps_A relative error in W, and the
+result is rounded to fp32.  Each test computes cond(A) from the oracle's own
+centred data and checks  max|W - W_ref| <= 4 * cond(A) * eps_A * max|W_ref| +
+2^-23 * max|W_ref|, and b through b = mean(Y) - mean(X) W.  The inputs are
+well conditioned (N >> IN) and have non-zero means, so the centring is
+exercised; the bound is loose by a large factor on random data, and the
+achieved error is logged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import parity
+from tests.parity import log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library():
+    import cross_model_kv_helm_amd as hk
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert hk.helm_device_check(-1) == 0, hk.helm_last_error()
+    yield
+
+
+def draw(G, N, IN, seed, mean=2.0, noise=0.05):
+    """X with per-feature means ~ N(0, mean^2) and unit-variance noise;
+    Y = X W* + b* + noise (a planted map), both rounded to bf16."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    mu = torch.randn((G, 1, IN), generator=g, device="cuda") * mean
+    X = (torch.randn((G, N, IN), generator=g, device="cuda") + mu).to(torch.bfloat16)
+    Wt = torch.randn((G, IN, 128), generator=g, device="cuda") / IN ** 0.5
+    bt = torch.randn((G, 1, 128), generator=g, device="cuda")
+    Y = (torch.bmm(X.float(), Wt) + bt + noise * torch.randn((G, N, 128), generator=g, device="cuda"))
+    return X, Y.to(torch.bfloat16)
+
+
+def check(X, Y, W, b, lam, label, groups=None):
+    G, N, IN = X.shape
+    groups = range(G) if groups is None else groups
+    xs = parity.to_np_storage(X)
+    ys = parity.to_np_storage(Y)
+    Wg = W.double().cpu().numpy()
+    bg = b.double().cpu().numpy()
+    worst_w = worst_b = 0.0
+    for gi in groups:
+        Wr, br = oracle.ridge_fit(xs[gi:gi + 1], ys[gi:gi + 1], lam=lam, dtype=oracle.BF16)
+        Wr, br = Wr[0], br[0]
+        x = parity.storage_to_f64(xs[gi])
+        mx = x.mean(axis=0)
+        xc = x - mx
+        A = xc.T @ xc + lam * np.eye(IN)
+        cond = np.linalg.cond(A)
+        ratio = 1.0 + (mx ** 2).max() / max(xc.var(axis=0).min(), 1e-30)
+        eps_a = (N / 16) * 2.0 ** -24 * ratio
+        scale = np.abs(Wr).max()
+        tol_w = 4 * cond * eps_a * scale + 2.0 ** -23 * scale
+        err_w = np.abs(Wg[gi] - Wr).max()
+        # b = mean(Y) - mean(X) W: the W error moves b by at most |mean(X)|_1 tol_w
+        tol_b = np.abs(mx).sum() * tol_w + 2.0 ** -23 * (np.abs(br).max() + 1.0) + 1e-6
+        err_b = np.abs(bg[gi] - br).max()
+        worst_w, worst_b = max(worst_w, err_w / scale), max(worst_b, err_b)
+        assert np.isfinite(Wg[gi]).all() and np.isfinite(bg[gi]).all(), f"{label} group {gi}: non-finite"
+        assert err_w <= tol_w, f"{label} group {gi}: max|dW| {err_w:.3e} > {tol_w:.3e} (cond {cond:.1f})"
+        assert err_b <= tol_b, f"{label} group {gi}: max|db| {err_b:.3e} > {tol_b:.3e}"
+    log(f"{label}: {len(groups)} groups, worst max|dW|/max|W| {worst_w:.2e}, worst max|db| {worst_b:.2e}")
+
+
+def fit(X, Y, lam):
+    import cross_model_kv_helm_amd as hk
+    W, b = hk.helm_ridge_fit(X, Y, lam=lam)
+    torch.cuda.synchronize()
+    return W, b
+
+
+def test_ridge_small_ragged_three_groups():
+    """3 groups (not a multiple of 8: plain tile order), N = 1000 (the last
+    64-observation step ragged), IN = 256 (one X tile)."""
+    X, Y = draw(3, 1000, 256, 1)
+    check(X, Y, *fit(X, Y, 0.01), 0.01, "ridge G3 N1000 IN256")
+
+
+def test_ridge_in128_single_step():
+    """IN = 128 (half of the one X tile idle), N = 64 (one step)."""
+    X, Y = draw(2, 64 * 9, 128, 2)
+    X, Y = X[:, :64].contiguous(), Y[:, :64].contiguous()
+    check(X, Y, *fit(X, Y, 0.01), 0.01, "ridge G2 N64 IN128")
+
+
+def test_ridge_in384_xcd_order_strong_penalty():
+    """IN = 384 (two X tiles, the second half idle; three upper tiles), 8
+    groups (the XCD tile order), N = 4097, lambda = 50."""
+    X, Y = draw(8, 4097, 384, 3)
+    check(X, Y, *fit(X, Y, 50.0), 50.0, "ridge G8 N4097 IN384 lam50")
+
+
+def test_ridge_zero_penalty():
+    """lambda = 0: plain least squares with an intercept."""
+    X, Y = draw(2, 3000, 512, 4)
+    check(X, Y, *fit(X, Y, 0.0), 0.0, "ridge G2 N3000 IN512 lam0")
+
+
+def test_ridge_in1024():
+    """IN = 1024 (the largest width: four X tiles, ten upper tiles), N = 2500."""
+    X, Y = draw(1, 2500, 1024, 5, mean=0.5)
+    check(X, Y, *fit(X, Y, 0.01), 0.01, "ridge G1 N2500 IN1024")
+
+
+def test_ridge_stages_equal_one_call():
+    """The products stage and the solve stage enqueued separately write
+    exactly what one call writes."""
+    import cross_model_kv_helm_amd as hk
+    X, Y = draw(3, 777, 256, 6)
+    W1, b1 = fit(X, Y, 0.01)
+    ws = torch.empty(hk.helm_ridge_workspace_bytes(hk.ridge_shape(3, 777, 256)), dtype=torch.uint8, device="cuda")
+    W2 = torch.full_like(W1, float("nan"))
+    b2 = torch.full_like(b1, float("nan"))
+    hk.helm_ridge_fit(X, Y, W=W2, b=b2, workspace=ws, stages=hk.HELM_STAGE_TABLES)
+    hk.helm_ridge_fit(X, Y, W=W2, b=b2, workspace=ws, stages=hk.HELM_STAGE_MAP)
+    torch.cuda.synchronize()
+    assert torch.equal(W1, W2) and torch.equal(b1, b2)
+
+
+def test_ridge_calibration_shape_sampled():
+    """The calibration's shape per group (about 128K observations, IN = k*D =
+    512 at k = 4): 16 groups (two rounds of the XCD order), 3 checked
+    against the oracle."""
+    X, Y = draw(16, 131072, 512, 7, mean=1.0, noise=0.1)
+    W, b = fit(X, Y, 0.01)
+    check(X, Y, W, b, 0.01, "ridge G16 N131072 IN512", groups=[0, 7, 15])
