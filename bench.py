@@ -44,6 +44,8 @@ COSINE_MD = os.path.join(ROOT, "profiles", "kv_cosine_qwen3_14b_32b_t32k.md")
 COSINE_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "cosine.hip")
 WIDE_MD = os.path.join(ROOT, "profiles", "wide_gemm_qwen3_14b_32b_t32k_wide.md")
 WIDE_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "wide.hip")
+RIDGE_MD = os.path.join(ROOT, "profiles", "ridge_gram_qwen3_14b_32b_calibration.md")
+RIDGE_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "ridge.hip")
 
 
 def kernel_source_digest(path: str = KERNEL_SRC) -> str:
@@ -68,17 +70,26 @@ def kernel_source_digest(path: str = KERNEL_SRC) -> str:
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
-def recorded_traffic(md: str = COUNTERS_MD, src: str = KERNEL_SRC):
+def recorded_traffic(md: str = COUNTERS_MD, src: str = KERNEL_SRC, units: float | None = None):
     """(bytes per launch, note) from a committed counter summary, or
-    (None, reason) when it is missing or was taken on another kernel source."""
+    (None, reason) when it is missing or was taken on another kernel source.
+    A summary may record bytes per independent unit of work
+    (hbm_bytes_per_group) instead of per launch; then `units` (the launch's
+    count) scales it."""
     try:
         text = open(md).read()
     except OSError:
         return None, "no counter summary"
-    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(("sha256:", "hbm_bytes_per_launch:")))
+    keys = ("sha256:", "hbm_bytes_per_launch:", "hbm_bytes_per_group:")
+    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(keys))
     if fields.get("sha256", "").strip() != kernel_source_digest(src):
         return None, "counters were taken on another kernel source"
-    return float(fields["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE x2 + WRITE_SIZE (copy-calibrated)"
+    note = "rocprofv3 FETCH_SIZE x2 + WRITE_SIZE (copy-calibrated)"
+    if "hbm_bytes_per_launch" in fields:
+        return float(fields["hbm_bytes_per_launch"]), note
+    if "hbm_bytes_per_group" in fields and units is not None:
+        return float(fields["hbm_bytes_per_group"]) * units, note + ", per group x groups"
+    return None, "no per-launch figure for this launch"
 
 
 def log(msg):
@@ -195,11 +206,70 @@ def wide_leg(hk, synth, w, src_k, c, out_k, out_v, steps, stream):
         f"{flops / (gms * 1e-3) / 1e12:.1f} TFLOP/s over {n} launches")
     traffic, note = recorded_traffic(WIDE_MD, WIDE_SRC)
     del ws, W_k, W_v
+    torch.cuda.empty_cache()
     return {"ms_per_transfer": res["call"], "tokens_per_s": T / (res["call"] * 1e-3), "in_features": IN,
             "launches": n, "kernel": "wide_gemm_kernel",
             "roofline": {"bound": "mfma", "achieved": flops / (gms * 1e-3) / 1e12,
                          "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
                          "frac": flops / (gms * 1e-3) / MFMA_BF16_PEAK, "traffic": traffic,
+                         "kernel_ms": gms, "algorithmic_flops": flops, "traffic_source": note}}
+
+
+def ridge_leg(hk, synth, w, groups, steps, stream):
+    """The ridge fit of the maps at the calibration's shape: one group per
+    (target layer, head, K|V) map of the 40 -> 64-layer pair (64 x 8 x 2 =
+    1,024 groups), ~128K observations each (131,072), IN = k*D = 512 inputs
+    and D = 128 targets per observation; synthetic observations
+    (synth.ridge_inputs).  Fewer groups (a multiple of 8) when device memory
+    is short; the line says how many.  Times whole fits and the two stages
+    alone with HIP events on the launch stream; the roofline of the Gram
+    kernel counts the symmetric half of X^T X, X^T Y and the sums."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    N, IN, D = 131072, w.k * w.head_dim, w.head_dim
+    per_group = N * (IN + D) * 2 + IN * IN * 4 + IN * D * 4 + (IN + D) * 4 + IN * (IN + D) * 8 + IN * D * 4 + D * 4
+    free, _ = torch.cuda.mem_get_info(dev)
+    fit_groups = min(groups, int((free - (8 << 30)) // per_group) // 8 * 8)
+    if fit_groups < 8:
+        log(f"ridge fit: skipped ({free / 2**30:.1f} GiB free)")
+        return {"skipped": f"{free / 2**30:.1f} GiB of device memory free"}
+    log(f"ridge fit: drawing {fit_groups} groups of {N} x {IN} observations")
+    X, Y = synth.ridge_inputs(fit_groups, N, IN, D, 511, dev)
+    shape = hk.ridge_shape(fit_groups, N, IN, D, 0.01)
+    ws = torch.empty(hk.helm_ridge_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    W = torch.empty((fit_groups, IN, D), dtype=torch.float32, device=dev)
+    b = torch.empty((fit_groups, D), dtype=torch.float32, device=dev)
+
+    def call(stages):
+        hk.helm_ridge_fit(X, Y, lam=0.01, W=W, b=b, workspace=ws, stages=stages)
+
+    call(hk.HELM_STAGE_ALL)
+    torch.cuda.synchronize()
+    n = max(2, steps // 4)
+    res = {}
+    for name, stages in (("fit", hk.HELM_STAGE_ALL), ("gram", hk.HELM_STAGE_TABLES), ("solve", hk.HELM_STAGE_MAP)):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record(stream)
+            call(stages)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    flops = float(fit_groups) * (N * IN * (IN + 1) + 2.0 * N * IN * D)
+    gms = res["gram"]
+    log(f"ridge fit: {fit_groups} groups, fit {res['fit']:.3f} ms (gram {gms:.3f}, solve {res['solve']:.3f}), "
+        f"{flops / (gms * 1e-3) / 1e12:.1f} TFLOP/s in the Gram kernel")
+    traffic, note = recorded_traffic(RIDGE_MD, RIDGE_SRC, units=fit_groups)
+    finite = bool(torch.isfinite(W).all().item() and torch.isfinite(b).all().item())
+    del X, Y, ws, W, b
+    torch.cuda.empty_cache()
+    return {"groups": fit_groups, "observations": N, "in_features": IN, "out_features": D, "lambda": 0.01,
+            "ms_per_fit": res["fit"], "gram_ms": gms, "solve_ms": res["solve"], "launches": n,
+            "groups_per_s": fit_groups / (res["fit"] * 1e-3), "finite": finite, "kernel": "ridge_gram_kernel",
+            "roofline": {"bound": "mfma", "achieved": flops / (gms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+                         "unit": "TFLOP/s", "frac": flops / (gms * 1e-3) / MFMA_BF16_PEAK, "traffic": traffic,
                          "kernel_ms": gms, "algorithmic_flops": flops, "traffic_source": note}}
 
 
@@ -211,6 +281,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_14b_32b_t32k")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--wide", type=int, default=1, help="also time the wide-input map (0 = skip)")
+    ap.add_argument("--ridge-groups", type=int, default=1024,
+                    help="groups of the ridge-fit leg (0 = skip); fewer when device memory is short")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (the reference "
                          "kernel that scales HBM byte counters) and exit")
@@ -332,6 +404,7 @@ def main():
                            "algorithmic_bytes": cos_bytes, "traffic_source": cos_note}}
 
     wide = wide_leg(hk, synth, w, src_k, c, out_k, out_v, args.steps, stream) if args.wide else None
+    ridge = ridge_leg(hk, synth, w, args.ridge_groups, args.steps, stream) if args.ridge_groups > 0 else None
 
     B, F, parts = algorithmic_work(w, c["layer_sel"].cpu().numpy(), T)
     t_s = ms * 1e-3
@@ -382,6 +455,7 @@ def main():
         "bytes_breakdown": parts,
         "kv_cosine": kv_cos,
         "wide_map": wide,
+        "ridge_fit": ridge,
     }
     print(json.dumps(line), flush=True)
 

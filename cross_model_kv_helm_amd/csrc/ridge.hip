@@ -17,10 +17,11 @@
 //     feature per lane) is not contiguous in memory.  Operand tiles of 64
 //     observations x 256 features are copied to LDS as they are stored
 //     (buffer -> LDS DMA, double-buffered) and every fragment is read with
-//     two ds_read_b64_tr_b16: within each 16-lane group, lane 4e+q names 4
-//     consecutive features of observation e and receives feature q' = lane/4
-//     ... of the 4 observations named by lanes q', 4+q', 8+q', 12+q'
-//     (measured lane layout), i.e. the transpose a fragment needs.  Tile rows
+//     two ds_read_b64_tr_b16.  Within each 16-lane group, lane 4e+q gives
+//     the address of 4 consecutive features (4q .. 4q+3) of observation e,
+//     and lane i receives element i%4 of the 4-feature chunks named by lanes
+//     i/4, 4+i/4, 8+i/4, 12+i/4 (a measured lane layout): feature i of
+//     observations 0..3, the transpose a fragment needs.  Tile rows
 //     are XOR-swizzled in 16-byte pieces (slot = piece ^ 4*((t%4) + 4*((t/8)%2)))
 //     so the 8 observation rows one read touches fall in 8 different bank
 //     groups.  Tiles: 256 x 256 outputs, four waves of 128 x 128 (fp32
@@ -312,6 +313,7 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_gram_kernel(GramArgs a) {
 
 // ---------------------------------------------------------------- solve
 constexpr int kP = 16;   // panel width of the Cholesky
+constexpr int kRB = 8;   // rows whose memory accesses are issued together
 
 struct SolveArgs {
   const float* gram;     // [G, IN, IN] (upper tiles)
@@ -325,6 +327,12 @@ struct SolveArgs {
   double lambda;
 };
 
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 struct SolveSmem {
   double Dg[kP][kP + 1];
   double Pn[kP][kMaxIn + kD - kP];
@@ -335,23 +343,32 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
   const int64_t g = blockIdx.x;
   const int n = a.IN, ld = n + kD, tid = threadIdx.x;
   const double invN = 1.0 / (double)a.N;
-  const float* G = a.gram + g * (int64_t)n * n;
-  const float* C = a.cross + g * (int64_t)n * kD;
-  const float* sx = a.sums + g * (int64_t)(n + kD);
-  const float* sy = sx + n;
-  double* M = a.M + g * (int64_t)n * ld;
+  const float* __restrict__ G = a.gram + g * (int64_t)n * n;
+  const float* __restrict__ C = a.cross + g * (int64_t)n * kD;
+  const float* __restrict__ sx = a.sums + g * (int64_t)(n + kD);
+  const float* __restrict__ sy = sx + n;
+  double* __restrict__ M = a.M + g * (int64_t)n * ld;
 
   // centred normal matrix + lambda I (upper: row j, columns i >= j) and
   // centred right-hand sides X^T Y - sx sy^T / N
-  for (int j = 0; j < n; ++j) {
-    const double sj = sx[j];
-    for (int i = j + tid; i < ld; i += kThreads) {
-      double v;
-      if (i < n)
-        v = (double)G[(int64_t)j * n + i] - sj * (double)sx[i] * invN + (i == j ? a.lambda : 0.0);
-      else
-        v = (double)C[(int64_t)j * kD + (i - n)] - sj * (double)sy[i - n] * invN;
-      M[(int64_t)j * ld + i] = v;
+  // (rows in batches of kRB, their loads issued together)
+  for (int j0 = 0; j0 < n; j0 += kRB) {
+    double sj[kRB];
+#pragma unroll
+    for (int u = 0; u < kRB; ++u) sj[u] = sx[j0 + u];
+    for (int i = j0 + tid; i < ld; i += kThreads) {
+      const bool a_part = i < n;
+      const double si = a_part ? (double)sx[i] : (double)sy[i - n];
+      double raw[kRB];
+#pragma unroll
+      for (int u = 0; u < kRB; ++u)
+        raw[u] = a_part ? (i >= j0 + u ? (double)G[(int64_t)(j0 + u) * n + i] : 0.0)
+                        : (double)C[(int64_t)(j0 + u) * kD + (i - n)];
+#pragma unroll
+      for (int u = 0; u < kRB; ++u) {
+        const int j = j0 + u;
+        if (!a_part || i >= j) M[(int64_t)j * ld + i] = raw[u] - sj[u] * si * invN + (i == j ? a.lambda : 0.0);
+      }
     }
   }
   __syncthreads();
@@ -364,17 +381,25 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
       if (c >= r) sm.Dg[r][c] = M[(int64_t)(k0 + r) * ld + k0 + c];
     }
     __syncthreads();
-    for (int r = 0; r < kP; ++r) {
-      if (tid == 0) sm.Dg[r][r] = sqrt(sm.Dg[r][r]);   // a non-positive pivot gives NaN
-      __syncthreads();
-      if (tid > r && tid < kP) sm.Dg[r][tid] /= sm.Dg[r][r];
-      __syncthreads();
-      for (int e = tid; e < kP * kP; e += kThreads) {
-        const int s = e / kP, c = e % kP;
-        if (s > r && c >= s) sm.Dg[s][c] -= sm.Dg[r][s] * sm.Dg[r][c];
+    // (by wave 0 alone: one wave's LDS accesses take effect in issue order,
+    // so a compiler barrier orders its lanes' steps)
+    if (tid < 64) {
+      for (int r = 0; r < kP; ++r) {
+        const double piv = sqrt(sm.Dg[r][r]);   // a non-positive pivot gives NaN
+        wave_sync();
+        if (tid == r)
+          sm.Dg[r][r] = piv;
+        else if (tid > r && tid < kP)
+          sm.Dg[r][tid] /= piv;
+        wave_sync();
+        for (int e = tid; e < kP * kP; e += 64) {
+          const int s = e / kP, c = e % kP;
+          if (s > r && c >= s) sm.Dg[s][c] -= sm.Dg[r][s] * sm.Dg[r][c];
+        }
+        wave_sync();
       }
-      __syncthreads();
     }
+    __syncthreads();
     for (int e = tid; e < kP * kP; e += kThreads) {
       const int r = e / kP, c = e % kP;
       if (c >= r) M[(int64_t)(k0 + r) * ld + k0 + c] = sm.Dg[r][c];
@@ -400,13 +425,27 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
     __syncthreads();
     // trailing update: row s >= m0, column j >= s (A part) or any column of
     // the right-hand sides: M[s][j] -= sum_r Pn[r][s - m0] Pn[r][j - m0]
+    // (rows in batches of kRB, their loads issued together)
     for (int c = tid; c < width; c += kThreads) {
       const int j = m0 + c;
       double col[kP];
 #pragma unroll
       for (int r = 0; r < kP; ++r) col[r] = sm.Pn[r][c];
-      const int s_end = j < n ? j : n - 1;
-      for (int s = m0; s <= s_end; ++s) {
+      const int s_stop = (j < n ? j : n - 1) + 1;
+      int s = m0;
+      for (; s + kRB <= s_stop; s += kRB) {
+        double mv[kRB];
+#pragma unroll
+        for (int u = 0; u < kRB; ++u) mv[u] = M[(int64_t)(s + u) * ld + j];
+#pragma unroll
+        for (int u = 0; u < kRB; ++u) {
+          double v = 0.0;
+#pragma unroll
+          for (int r = 0; r < kP; ++r) v += sm.Pn[r][s + u - m0] * col[r];
+          M[(int64_t)(s + u) * ld + j] = mv[u] - v;
+        }
+      }
+      for (; s < s_stop; ++s) {
         double v = 0.0;
 #pragma unroll
         for (int r = 0; r < kP; ++r) v += sm.Pn[r][s - m0] * col[r];
@@ -446,12 +485,21 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
       double wv[kP];
 #pragma unroll
       for (int r = 0; r < kP; ++r) wv[r] = sm.Pn[r][d];
-      for (int j = half; j < k0; j += 2) {
-        const double* urow = M + (int64_t)j * ld + k0;
-        double v = 0.0;
+      // (rows in batches of kRB, their loads issued together; k0 is a
+      // multiple of 16, so each half has whole batches)
+      for (int j0 = half * (k0 / 2); j0 < (half + 1) * (k0 / 2); j0 += kRB) {
+        double mv[kRB], v[kRB];
 #pragma unroll
-        for (int r = 0; r < kP; ++r) v += urow[r] * wv[r];
-        M[(int64_t)j * ld + n + d] -= v;
+        for (int u = 0; u < kRB; ++u) {
+          mv[u] = M[(int64_t)(j0 + u) * ld + n + d];
+          v[u] = 0.0;
+        }
+#pragma unroll
+        for (int r = 0; r < kP; ++r)
+#pragma unroll
+          for (int u = 0; u < kRB; ++u) v[u] += M[(int64_t)(j0 + u) * ld + k0 + r] * wv[r];
+#pragma unroll
+        for (int u = 0; u < kRB; ++u) M[(int64_t)(j0 + u) * ld + n + d] = mv[u] - v[u];
       }
     }
     __syncthreads();

@@ -23,6 +23,10 @@ used on, per source layer, with torch's counter-based Philox generator):
   biases b ~ N(0, 0.01) (variance; std 0.1), kept in fp32;
 * wide maps     (the wide-input map, IN = k*2*H*D input features)
   W ~ N(0, 1/IN), biases as above;
+* ridge data    (calibration observations of the ridge fit) X[g, n, i] =
+  (z + m[g, i]) * s[g, i] and Y[g, n, d] drawn the same way, independently
+  of X: z ~ N(0, 1), per-feature means m ~ N(0, 1) and scales
+  s = exp(0.5 * N(0, 1)), rounded to bf16;
 * layer_sel[l]  k distinct source layers by a partial Fisher-Yates shuffle,
   kept in draw order (not sorted);
 * positions     per workload (see CONFIGS);
@@ -285,3 +289,22 @@ def empty_target_pool(w: Workload, lay: PagedLayout, device="cpu") -> torch.Tens
                        dtype=torch_dtype(w), device=device)
     pool.view(torch.int16).fill_(np.int16(np.uint16(CANARY_BITS).view(np.int16)))
     return pool
+
+
+def ridge_inputs(n_groups: int, n_obs: int, in_features: int, out_features: int, seed: int, device):
+    """Observations X [G, N, IN] and targets Y [G, N, D] (bf16) for the ridge
+    fit, drawn per group on ``device``: every feature has its own mean and
+    scale (see the module docstring); Y is independent of X."""
+    out = []
+    for tid, F in ((40, in_features), (41, out_features)):
+        g = _gen(device, seed, tid)
+        m = torch.randn((n_groups, 1, F), generator=g, device=device)
+        sc = torch.exp(0.5 * torch.randn((n_groups, 1, F), generator=g, device=device))
+        t = torch.empty((n_groups, n_obs, F), dtype=torch.bfloat16, device=device)
+        step = max(1, (1 << 30) // max(1, n_obs * F * 4))     # about 1 GiB of fp32 per draw
+        for i in range(0, n_groups, step):
+            j = min(n_groups, i + step)
+            z = torch.randn((j - i, n_obs, F), generator=g, device=device)
+            t[i:j] = ((z + m[i:j]) * sc[i:j]).to(torch.bfloat16)
+        out.append(t)
+    return out[0], out[1]
