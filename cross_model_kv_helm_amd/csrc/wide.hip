@@ -20,11 +20,12 @@
 //     src_pos (fp32 arithmetic, rounded once to bf16 — the map's operand
 //     type) and each map's W transposed to [D][IN].  Both are HBM-bound and
 //     small next to the product (~1 ms of ~72 at the shape above).
-//   * Product: v_mfma_f32_32x32x16_bf16, one 256-thread workgroup per
-//     256-token x 256-column tile (two (head, K|V) maps), four waves of
-//     128 x 128 each (4 x 4 accumulator blocks, 256 fp32 accumulators per
-//     lane).  A wave's 128 columns are one whole map, so the RoPE partners
-//     d and d+64 sit in the same lane of blocks nb and nb+2.
+//   * Product: v_mfma_f32_32x32x16_bf16, one workgroup per 256-token x
+//     256-column tile (two (head, K|V) maps), eight waves of 128 x 64 (two
+//     per SIMD, 4 x 2 accumulator blocks, 128 fp32 accumulators per lane).
+//     A wave's two 32-column blocks are 64 columns apart in one map, so the
+//     RoPE partners d and d+64 sit in the same lane of blocks 0 and 1.  (Four
+//     waves of 128 x 128 run at the same speed with twice the registers.)
 //   * Operand tiles of 64 k-values reach LDS by buffer->LDS DMA (16 bytes
 //     per lane, no registers in between), double-buffered: the copies of
 //     step s+1 are issued between the first 32 products of step s (one
@@ -36,10 +37,15 @@
 //     every 16-byte fragment read of the products is bank-conflict free.
 //   * XCD-aware tile order: the 8 column tiles of a token tile run on one
 //     XCD (workgroup id mod 8), so its activation tile can be served to all
-//     8 from that XCD's L2.  The measured bound is the latency of the copies
-//     that miss L2 inside the one step of lookahead (vector memory returns
-//     in issue order, so neither deeper rings of smaller steps nor L2
-//     warm-up loads issued steps ahead shorten it), not HBM bytes.
+//     8 from that XCD's L2.  What bounds it (timed with the copies or the
+//     products taken out): the products, LDS reads and barriers alone run at
+//     ~59% of the matrix peak; the copies alone move ~9x the compulsory bytes
+//     across L2 at ~6 TB/s, because tiles that share operands drift apart in
+//     time; together they overlap only partly.  Lockstep (persistent) tiles
+//     halve the bytes but every tile then waits on the same misses, and
+//     neither deeper rings, L2 warm-up loads nor loads staged through
+//     registers two steps ahead shortened the wait (vector memory returns in
+//     issue order).
 //   * Epilogue from registers: bias, the forward rotation at tgt_pos (keys;
 //     fp32 tables from the RoPE table kernel), round to bf16, store.
 #include "internal.hpp"
@@ -58,7 +64,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef lds::u32x4 u32x4;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kD = 128;
 constexpr int kHalf = 64;
@@ -67,12 +72,15 @@ constexpr int kCT = 256;          // output columns per tile (two maps)
 constexpr int kKB = 64;           // k-values per pipeline step
 constexpr int kBufs = 2;          // LDS ring of operand tiles: copies run kBufs-1 steps ahead
 constexpr int kMaxSel = 64;       // selected layers per target layer (the library's limit on k)
-constexpr int kThreads = 256;     // four waves, 2 x 2
+constexpr int kWaves = 8;         // 4: 2 x 2 waves of 128 x 128 outputs; 8: 2 x 4 waves of 128 x 64 (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kNB = 16 / kWaves;  // 32-column accumulator blocks per wave
 constexpr int kRowPieces = kKB * 2 / 16;   // 16-byte pieces per tile row and step
 constexpr int kSwz = 16 / kRowPieces;      // rows sharing one swizzle pattern
 constexpr int kRowsPerCopy = 64 / kRowPieces;   // tile rows per 1 KB copy instruction
-constexpr int kPer = kRowPieces;           // copy instructions per wave, operand and step
-constexpr int kCopyStride = 32 / (2 * kPer) > 0 ? 32 / (2 * kPer) : 1;   // products between two copies (spread over 32)
+constexpr int kPer = 4 * kRowPieces / kWaves;   // copy instructions per wave, operand and step (tile / waves / 1 KB)
+constexpr int kMfmaPerStep = (kKB / 16) * 4 * kNB;
+constexpr int kCopyStride = kMfmaPerStep / 2 / (2 * kPer) > 0 ? kMfmaPerStep / 2 / (2 * kPer) : 1;   // copies spread over half a step
 static_assert(kKB % 16 == 0 && 16 % kRowPieces == 0 && kBufs >= 2 && kBufs <= 5 && (kBufs - 2) * 2 * kPer < 64, "pipeline shape");
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -143,7 +151,12 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
   }
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / (kWaves / 2), wn = w % (kWaves / 2);
+  // the wave's 32-column blocks: with 8 waves, blocks 32*(wn%2) and +64 of
+  // map wn/2, so the RoPE partners d, d+64 sit in one lane of blocks 0 and 1
+  auto bcol = [&](int nb) __attribute__((always_inline)) {
+    return kWaves == 4 ? 128 * wn + 32 * nb : 128 * (wn >> 1) + 32 * (wn & 1) + 64 * nb;
+  };
   const int32_t t0 = tt * kTT;
   const int32_t T = a.T, H = a.H, IN = a.IN;
   const uint32_t slab_bytes = (uint32_t)T * kD * 2;
@@ -161,7 +174,7 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
   // take the same pieces (the swizzle term repeats every 16*kSwz rows), so
   // one per-lane offset per operand serves all: A adds the row step (and
   // skips rows past T), B folds it, modulo one map, into the scalar offset.
-  constexpr int kRowStep = 4 * kRowsPerCopy;                     // rows between a wave's instructions
+  constexpr int kRowStep = kWaves * kRowsPerCopy;                // rows between a wave's instructions
   constexpr int kMapWraps = kD / kRowStep;                       // instructions per map (B)
   static_assert((16 * kSwz) % kRowStep == 0 || kRowStep % (16 * kSwz) == 0, "swizzle period");
   const int r0 = kRowsPerCopy * w + lane / kRowPieces;
@@ -189,20 +202,20 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
     if (q < kPer) {
       const uint32_t va = voff_a0 + (uint32_t)(q * kRowStep * kD * 2);
       dma16(ra, va < a_lim ? va : kSkip, (uint32_t)(s % kStepsPerBlock) * (kKB * 2),   // (kSkip + 192 stays past every range)
-            (const char*)As[p] + 1024 * (w + 4 * q));
+            (const char*)As[p] + 1024 * (w + kWaves * q));
     } else {
       const int n = q - kPer;
       dma16(rs_b[n >= kPer / 2 ? 1 : 0], voff_b0,
             (uint32_t)s * (kKB * 2) + (uint32_t)((n % kMapWraps) * kRowStep) * (uint32_t)IN * 2,
-            (const char*)Bs[p] + 1024 * (w + 4 * n));
+            (const char*)Bs[p] + 1024 * (w + kWaves * n));
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][kNB];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
+    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x16{};
 
   // steps 0 .. kBufs-2 in flight before the loop (n_steps >= kBufs - 1:
   // at least 256 features, the host checks)
@@ -232,11 +245,11 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
     if constexpr (kIssue) ra = a_rsrc(ahead);
     const uint16_t* A = As[p];
     const uint16_t* B = Bs[p];
-    bf16x8 af[2][4], bfr[2][4];
+    bf16x8 af[2][4], bfr[2][kNB];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) af[0][mb] = *(const bf16x8*)&A[frag_off(128 * wm, 0) + mb * kBlockElems];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) bfr[0][nb] = *(const bf16x8*)&B[frag_off(128 * wn, 0) + nb * kBlockElems];
+    for (int nb = 0; nb < kNB; ++nb) bfr[0][nb] = *(const bf16x8*)&B[frag_off(bcol(nb), 0)];
 #pragma unroll
     for (int ks = 0; ks < kKB / 16; ++ks) {
       const int cur = ks & 1, nxt = cur ^ 1;
@@ -246,16 +259,16 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
         for (int mb = 0; mb < 4; ++mb)
           af[nxt][mb] = *(const bf16x8*)&A[frag_off(128 * wm, ks + 1) + mb * kBlockElems];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          bfr[nxt][nb] = *(const bf16x8*)&B[frag_off(128 * wn, ks + 1) + nb * kBlockElems];
+        for (int nb = 0; nb < kNB; ++nb)
+          bfr[nxt][nb] = *(const bf16x8*)&B[frag_off(bcol(nb), ks + 1)];
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
+        for (int nb = 0; nb < kNB; ++nb) {
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][mb], bfr[cur][nb], acc[mb][nb], 0, 0, 0);
           // the copies of the step ahead, one after every kCopyStride-th product
-          const int m = 16 * ks + 4 * mb + nb;
+          const int m = 4 * kNB * ks + kNB * mb + nb;
           if constexpr (kIssue)
             if (m % kCopyStride == kCopyStride - 1 && m / kCopyStride < 2 * kPer)
               copy_one(ahead, ahead % kBufs, m / kCopyStride, ra);
@@ -285,15 +298,15 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
   // ---- epilogue: this wave's map, bias, forward rotation (keys), store.
   // Accumulator register r of block (mb, nb) holds row 8*(r/4) + 4*(lane/32)
   // + r%4 of the block, column lane%32.
-  const int mi = 2 * ct + wn;
+  const int mi = 2 * ct + (kWaves == 4 ? wn : wn >> 1);
   const int kind = mi / H, h = mi % H;
   const int64_t grp = (int64_t)l * H + h;
   const float* bias = (kind ? a.b_v : a.b_k) + grp * kD;
   uint16_t* out = (kind ? a.out_v : a.out_k) + grp * T * kD;
   const int col = lane & 31;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int dlo = 32 * nb + col, dhi = dlo + kHalf;
+  for (int nb = 0; nb < kNB / 2; ++nb) {
+    const int dlo = (kWaves == 4 ? 32 * nb : 32 * (wn & 1)) + col, dhi = dlo + kHalf;
     const float blo = bias[dlo], bhi = bias[dhi];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -301,7 +314,7 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
       for (int r = 0; r < 16; ++r) {
         const int32_t t = t0 + 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (t >= T) continue;
-        float ylo = acc[mb][nb][r] + blo, yhi = acc[mb][nb + 2][r] + bhi;
+        float ylo = acc[mb][nb][r] + blo, yhi = acc[mb][nb + kNB / 2][r] + bhi;
         if (kind == 0) {
           const float2 cs = a.rope_tgt[rope_index(t, dlo, kHalf)];
           const float olo = fmaf(ylo, cs.x, -(yhi * cs.y));
