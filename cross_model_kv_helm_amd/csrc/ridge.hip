@@ -33,7 +33,11 @@
 //     matrix plus lambda I in upper storage, a blocked Cholesky A = U^T U in
 //     16-wide panels with the forward substitution of the right-hand sides
 //     folded into the panel updates, then the back substitution, W in fp32
-//     and b from the means.
+//     and b from the means.  Each panel pass reads and writes the trailing
+//     part of the group's fp64 matrix (2.6 MB at IN = 512, beyond L2 and the
+//     last-level cache for 1,024 groups), so the kernel is bound by those
+//     HBM passes; each memory loop issues 8 rows' accesses at once, and the
+//     panel rows sit in LDS sized to IN.
 #include "internal.hpp"
 #include "lds_dma.hpp"
 
@@ -312,7 +316,7 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_gram_kernel(GramArgs a) {
 }
 
 // ---------------------------------------------------------------- solve
-constexpr int kP = 16;   // panel width of the Cholesky
+constexpr int kP = 16;   // panel width of the Cholesky (8 measured slower: twice the passes over M)
 constexpr int kRB = 8;   // rows whose memory accesses are issued together
 
 struct SolveArgs {
@@ -333,13 +337,12 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-struct SolveSmem {
-  double Dg[kP][kP + 1];
-  double Pn[kP][kMaxIn + kD - kP];
-};
+// Dynamic LDS of the solve kernel: the panel rows, kP x (IN + D - kP) fp64.
+size_t solve_lds_bytes(int32_t IN) { return (size_t)kP * (IN + kD - kP) * sizeof(double); }
 
 __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
-  __shared__ SolveSmem sm;
+  __shared__ double Dg[kP][kP + 1];
+  extern __shared__ double pn_lds[];
   const int64_t g = blockIdx.x;
   const int n = a.IN, ld = n + kD, tid = threadIdx.x;
   const double invN = 1.0 / (double)a.N;
@@ -348,6 +351,8 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
   const float* __restrict__ sx = a.sums + g * (int64_t)(n + kD);
   const float* __restrict__ sy = sx + n;
   double* __restrict__ M = a.M + g * (int64_t)n * ld;
+  const int pld = n + kD - kP;   // row length of the panel rows in LDS
+  auto Pn = [&](int r, int c) __attribute__((always_inline)) -> double& { return pn_lds[r * pld + c]; };
 
   // centred normal matrix + lambda I (upper: row j, columns i >= j) and
   // centred right-hand sides X^T Y - sx sy^T / N
@@ -378,23 +383,23 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
     // diagonal block, factored in LDS
     for (int e = tid; e < kP * kP; e += kThreads) {
       const int r = e / kP, c = e % kP;
-      if (c >= r) sm.Dg[r][c] = M[(int64_t)(k0 + r) * ld + k0 + c];
+      if (c >= r) Dg[r][c] = M[(int64_t)(k0 + r) * ld + k0 + c];
     }
     __syncthreads();
     // (by wave 0 alone: one wave's LDS accesses take effect in issue order,
     // so a compiler barrier orders its lanes' steps)
     if (tid < 64) {
       for (int r = 0; r < kP; ++r) {
-        const double piv = sqrt(sm.Dg[r][r]);   // a non-positive pivot gives NaN
+        const double piv = sqrt(Dg[r][r]);   // a non-positive pivot gives NaN
         wave_sync();
         if (tid == r)
-          sm.Dg[r][r] = piv;
+          Dg[r][r] = piv;
         else if (tid > r && tid < kP)
-          sm.Dg[r][tid] /= piv;
+          Dg[r][tid] /= piv;
         wave_sync();
         for (int e = tid; e < kP * kP; e += 64) {
           const int s = e / kP, c = e % kP;
-          if (s > r && c >= s) sm.Dg[s][c] -= sm.Dg[r][s] * sm.Dg[r][c];
+          if (s > r && c >= s) Dg[s][c] -= Dg[r][s] * Dg[r][c];
         }
         wave_sync();
       }
@@ -402,7 +407,7 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
     __syncthreads();
     for (int e = tid; e < kP * kP; e += kThreads) {
       const int r = e / kP, c = e % kP;
-      if (c >= r) M[(int64_t)(k0 + r) * ld + k0 + c] = sm.Dg[r][c];
+      if (c >= r) M[(int64_t)(k0 + r) * ld + k0 + c] = Dg[r][c];
     }
     // panel rows k0 .. k0+15, columns past the block (the rest of U's rows
     // and the right-hand sides): solve U_kk^T X = panel, one column a thread
@@ -413,12 +418,12 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
       for (int r = 0; r < kP; ++r) {
         double v = M[(int64_t)(k0 + r) * ld + m0 + c];
 #pragma unroll
-        for (int p = 0; p < r; ++p) v -= sm.Dg[p][r] * x[p];
-        x[r] = v / sm.Dg[r][r];
+        for (int p = 0; p < r; ++p) v -= Dg[p][r] * x[p];
+        x[r] = v / Dg[r][r];
       }
 #pragma unroll
       for (int r = 0; r < kP; ++r) {
-        sm.Pn[r][c] = x[r];
+        Pn(r, c) = x[r];
         M[(int64_t)(k0 + r) * ld + m0 + c] = x[r];
       }
     }
@@ -430,7 +435,7 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
       const int j = m0 + c;
       double col[kP];
 #pragma unroll
-      for (int r = 0; r < kP; ++r) col[r] = sm.Pn[r][c];
+      for (int r = 0; r < kP; ++r) col[r] = Pn(r, c);
       const int s_stop = (j < n ? j : n - 1) + 1;
       int s = m0;
       for (; s + kRB <= s_stop; s += kRB) {
@@ -441,14 +446,14 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
         for (int u = 0; u < kRB; ++u) {
           double v = 0.0;
 #pragma unroll
-          for (int r = 0; r < kP; ++r) v += sm.Pn[r][s + u - m0] * col[r];
+          for (int r = 0; r < kP; ++r) v += Pn(r, s + u - m0) * col[r];
           M[(int64_t)(s + u) * ld + j] = mv[u] - v;
         }
       }
       for (; s < s_stop; ++s) {
         double v = 0.0;
 #pragma unroll
-        for (int r = 0; r < kP; ++r) v += sm.Pn[r][s - m0] * col[r];
+        for (int r = 0; r < kP; ++r) v += Pn(r, s - m0) * col[r];
         M[(int64_t)s * ld + j] -= v;
       }
     }
@@ -460,7 +465,7 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
   for (int k0 = ((n - 1) / kP) * kP; k0 >= 0; k0 -= kP) {
     for (int e = tid; e < kP * kP; e += kThreads) {
       const int r = e / kP, c = e % kP;
-      if (c >= r) sm.Dg[r][c] = M[(int64_t)(k0 + r) * ld + k0 + c];
+      if (c >= r) Dg[r][c] = M[(int64_t)(k0 + r) * ld + k0 + c];
     }
     __syncthreads();
     if (tid < kD) {
@@ -469,13 +474,13 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
       for (int r = kP - 1; r >= 0; --r) {
         double v = M[(int64_t)(k0 + r) * ld + n + tid];
 #pragma unroll
-        for (int p = r + 1; p < kP; ++p) v -= sm.Dg[r][p] * wv[p];
-        wv[r] = v / sm.Dg[r][r];
+        for (int p = r + 1; p < kP; ++p) v -= Dg[r][p] * wv[p];
+        wv[r] = v / Dg[r][r];
       }
 #pragma unroll
       for (int r = 0; r < kP; ++r) {
         M[(int64_t)(k0 + r) * ld + n + tid] = wv[r];
-        sm.Pn[r][tid] = wv[r];
+        Pn(r, tid) = wv[r];
       }
     }
     __syncthreads();
@@ -484,10 +489,10 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
       const int d = tid % kD, half = tid / kD;
       double wv[kP];
 #pragma unroll
-      for (int r = 0; r < kP; ++r) wv[r] = sm.Pn[r][d];
+      for (int r = 0; r < kP; ++r) wv[r] = Pn(r, d);
       // (rows in batches of kRB, their loads issued together; k0 is a
-      // multiple of 16, so each half has whole batches)
-      for (int j0 = half * (k0 / 2); j0 < (half + 1) * (k0 / 2); j0 += kRB) {
+      // multiple of kRB, the two halves take alternate batches)
+      for (int j0 = half * kRB; j0 < k0; j0 += 2 * kRB) {
         double mv[kRB], v[kRB];
 #pragma unroll
         for (int u = 0; u < kRB; ++u) {
@@ -559,7 +564,13 @@ hipError_t launch_ridge(const RidgeFit& f, bool gram, bool solve, hipStream_t st
     s.N = f.N;
     s.IN = f.IN;
     s.lambda = f.lambda;
-    hipLaunchKernelGGL(ridge_solve_kernel, dim3((unsigned)f.G), dim3(kThreads), 0, stream, s);
+    const size_t lds = solve_lds_bytes(f.IN);
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute((const void*)ridge_solve_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(ridge_solve_kernel, dim3((unsigned)f.G), dim3(kThreads), lds, stream, s);
   }
   return hipGetLastError();
 }
