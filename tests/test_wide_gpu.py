@@ -142,3 +142,29 @@ def test_wide_stages_equal_one_call():
         torch.cuda.synchronize()
         assert torch.equal(out[0], whole[0]) and torch.equal(out[1], whole[1]), f"pass {rep}"
     case.check(*whole)
+
+
+@pytest.mark.parametrize("bad,value", [(1, 99), (3, -1)])
+def test_wide_invalid_device_layer_sel_leaves_target_layer_unwritten(bad, value):
+    """A layer_sel row with an index outside [0, L_s) that reaches the device
+    is not read: that target layer keeps its previous contents (every
+    column tile of every token tile of it), the other layers are mapped."""
+    import cross_model_kv_helm_amd as hk
+    case = WideCase(W(f"wide_bad_{bad}", 5, 4, 2, 128, 600, 2, "bf16", 1e6, "shift4096", 66 + bad))
+    d, w = case.dev, case.w
+    sel = case.host["layer_sel"].copy()
+    sel[bad, 1] = value
+    d["layer_sel"] = torch.from_numpy(sel).cuda()
+    shape = (w.n_tgt_layers, w.n_kv_heads, case.T, w.head_dim)
+    sentinel = torch.full(shape, 3.0, dtype=torch.bfloat16, device="cuda")
+    out = (sentinel.clone(), sentinel.clone())
+    s = hk.make_shape(d["src_k"], d["W_k"], d["layer_sel"], w.theta, w.theta)
+    hk.helm_kv_transfer_wide(d["src_k"], d["src_v"], d["src_pos"], d["tgt_pos"], d["layer_sel"], d["W_k"],
+                             d["b_k"], d["W_v"], d["b_v"], out[0], out[1], s)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0][bad], sentinel[bad]) and torch.equal(out[1][bad], sentinel[bad])
+    good = [l for l in range(w.n_tgt_layers) if l != bad]
+    rows = np.concatenate([(l * w.n_kv_heads + h) * case.T + np.arange(case.T)
+                           for l in good for h in range(w.n_kv_heads)])
+    case.host["layer_sel"] = np.where((sel < 0) | (sel >= w.n_src_layers), 0, sel).astype(np.int32)
+    case.check(*out, rows=rows, label="valid rows of ")
