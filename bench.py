@@ -215,6 +215,66 @@ def wide_leg(hk, synth, w, src_k, c, out_k, out_v, steps, stream):
                          "kernel_ms": gms, "algorithmic_flops": flops, "traffic_source": note}}
 
 
+def paged_leg(hk, synth, steps, stream):
+    """The paged transfer (block tables, 16-token pages) on its workload:
+    28 -> 28 layers, 8 heads, k = 4, 32 requests of 256 .. 16,384 tokens with
+    per-request target offsets, pools with 12.5% spare blocks in seeded
+    permutation order (synth.paged_layout).  Times whole calls (tables,
+    slot maps, the keys and values launches) with HIP events; the roofline
+    divides the transfer's algorithmic bytes by that time."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    w = synth.CONFIGS["paged_32req"]
+    lay = synth.paged_layout(w)
+    N = lay.n_tokens
+    log(f"paged transfer: {len(lay.lens)} requests, {N} tokens; building pools")
+    c = synth.paged_content(w, lay, device=dev)
+    k_enc = encode_keys_on_gpu(hk, c.pop("k_content"), c["src_pos"], w.theta)
+    src_k_pool = synth.scatter_to_pool(k_enc, lay, lay.src_bt, lay.n_src_blocks)
+    del k_enc
+    src_v_pool = synth.scatter_to_pool(c.pop("src_v"), lay, lay.src_bt, lay.n_src_blocks)
+    torch.cuda.empty_cache()
+    tk = synth.empty_target_pool(w, lay, dev)
+    tv = synth.empty_target_pool(w, lay, dev)
+    sbt, tbt, cu = (torch.from_numpy(x).to(dev) for x in (lay.src_bt, lay.tgt_bt, lay.cu_seqlens))
+    shape = hk.make_paged_shape(src_k_pool, tk, c["W_k"], c["layer_sel"], sbt, tbt, N, w.theta, w.theta)
+    if hk.helm_paged_check(shape, lay.src_bt, lay.tgt_bt, lay.cu_seqlens) != 0:
+        raise SystemExit(f"paged check failed: {hk.helm_last_error()}")
+    shape.stream = hk.current_stream_ptr(dev)
+    ws = torch.empty(hk.helm_kv_paged_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+
+    def call():
+        hk.helm_kv_transfer_paged(src_k_pool, src_v_pool, sbt, tbt, cu, c["src_pos"], c["tgt_pos"],
+                                  c["layer_sel"], c["W_k"], c["b_k"], c["W_v"], c["b_v"], tk, tv, shape,
+                                  workspace=ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    B, F, parts = algorithmic_work(w, c["layer_sel"].cpu().numpy(), N)
+    B += 2 * lay.src_bt.size * 4 + (len(lay.lens) + 1) * 4   # the block tables and cu_seqlens
+    log(f"paged transfer: {ms:.3f} ms for {N} tokens, {N / ms * 1e3 / 1e6:.2f} M tok/s, "
+        f"{B / (ms * 1e-3) / 1e12:.2f} TB/s algorithmic")
+    del src_k_pool, src_v_pool, tk, tv, ws, c
+    torch.cuda.empty_cache()
+    return {"ms_per_transfer": ms, "tokens": N, "requests": int(len(lay.lens)), "tokens_per_s": N / (ms * 1e-3),
+            "launches": steps, "kernel": "transfer_mfma_kernel (paged instantiations), whole call",
+            "config": {"src_layers": w.n_src_layers, "tgt_layers": w.n_tgt_layers, "kv_heads": w.n_kv_heads,
+                       "head_dim": w.head_dim, "k": w.k, "block_size": lay.block_size},
+            "roofline": {"bound": "hbm", "achieved": B / (ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                         "frac": B / (ms * 1e-3) / HBM_PEAK, "traffic": None, "algorithmic_bytes": B,
+                         "mfma_frac": F / (ms * 1e-3) / MFMA_BF16_PEAK,
+                         "traffic_source": "not collected for the paged instantiations"}}
+
+
 def ridge_leg(hk, synth, w, groups, steps, stream):
     """The ridge fit of the maps at the calibration's shape: one group per
     (target layer, head, K|V) map of the 40 -> 64-layer pair (64 x 8 x 2 =
@@ -281,6 +341,7 @@ def main():
     ap.add_argument("--workload", default="qwen3_14b_32b_t32k")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--wide", type=int, default=1, help="also time the wide-input map (0 = skip)")
+    ap.add_argument("--paged", type=int, default=1, help="also time the paged transfer (0 = skip)")
     ap.add_argument("--ridge-groups", type=int, default=1024,
                     help="groups of the ridge-fit leg (0 = skip); fewer when device memory is short")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -404,6 +465,7 @@ def main():
                            "algorithmic_bytes": cos_bytes, "traffic_source": cos_note}}
 
     wide = wide_leg(hk, synth, w, src_k, c, out_k, out_v, args.steps, stream) if args.wide else None
+    paged = paged_leg(hk, synth, args.steps, stream) if args.paged else None
     ridge = ridge_leg(hk, synth, w, args.ridge_groups, args.steps, stream) if args.ridge_groups > 0 else None
 
     B, F, parts = algorithmic_work(w, c["layer_sel"].cpu().numpy(), T)
@@ -455,6 +517,7 @@ def main():
         "bytes_breakdown": parts,
         "kv_cosine": kv_cos,
         "wide_map": wide,
+        "paged": paged,
         "ridge_fit": ridge,
     }
     print(json.dumps(line), flush=True)
