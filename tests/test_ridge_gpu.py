@@ -143,3 +143,19 @@ def test_ridge_calibration_shape_sampled():
     X, Y = draw(16, 131072, 512, 7, mean=1.0, noise=0.1)
     W, b = fit(X, Y, 0.01)
     check(X, Y, W, b, 0.01, "ridge G16 N131072 IN512", groups=[0, 7, 15])
+
+
+def test_ridge_one_observation():
+    """N = 1: the centred data are zero, so W = 0 and b = that observation's
+    targets (exactly, after the fp32 store)."""
+    X, Y = draw(2, 1, 256, 8)
+    W, b = fit(X, Y, 0.01)
+    assert torch.equal(W, torch.zeros_like(W))
+    assert torch.equal(b, Y[:, 0].float())
+
+
+def test_ridge_one_row_in_the_last_step():
+    """N = 65: the second 64-observation step holds one row (the other 63
+    read zeros)."""
+    X, Y = draw(3, 65, 256, 9)
+    check(X, Y, *fit(X, Y, 0.01), 0.01, "ridge G3 N65 IN256")
