@@ -24,11 +24,18 @@
 //     observations 0..3, the transpose a fragment needs.  Tile rows
 //     are XOR-swizzled in 16-byte pieces (slot = piece ^ 4*((t%4) + 4*((t/8)%2)))
 //     so the 8 observation rows one read touches fall in 8 different bank
-//     groups.  Tiles: 256 x 256 outputs, four waves of 128 x 128 (fp32
-//     accumulators), one group's tiles on one XCD.  Only the upper tiles of
-//     the symmetric X^T X are formed; the X^T Y tiles have 128 spare columns,
-//     whose waves form the column sums as products with a constant fragment
-//     of ones (a contraction the matrix cores do anyway, the data read once).
+//     groups.  A wave owns a 128 x 128 block (fp32 accumulators); a
+//     workgroup's four waves share its two operand tiles, and one group's
+//     workgroups run on one XCD.  Only the blocks on and above the diagonal
+//     of the symmetric X^T X are formed.  A diagonal tile (X feature groups
+//     2r, 2r+1) needs one operand tile for its three blocks, so its second
+//     tile holds Y and its fourth wave forms the X^T Y block of group 2r; the
+//     X^T Y blocks of the odd groups go two to a workgroup as 128 x 64
+//     halves.  At IN = 512 that is 4 workgroups per group with every wave
+//     busy.  The waves of the diagonal blocks read one fragment set for both
+//     operands and form the column sums from it with v_dot2_f32_bf16 against
+//     ones (vector ALU that the products leave idle), as does the wave that
+//     holds Y's fragments.
 //   * Solve kernel (fp64, one workgroup per group): the centred normal
 //     matrix plus lambda I in upper storage, a blocked Cholesky A = U^T U in
 //     16-wide panels with the forward substitution of the right-hand sides
@@ -64,18 +71,87 @@ constexpr int kThreads = 256;
 constexpr int kPer = 8;            // copy instructions per wave, operand and step (32 KB tile / 4 waves / 1 KB)
 constexpr int kMaxIn = 1024;       // largest input width the solve kernel holds
 
-enum Role { kProducts = 0, kSums = 1, kIdle = 2 };
+constexpr int kGroupW = 128;       // features per group: one wave's block side
+constexpr int kYTile = -2;         // a B tile that holds Y (pieces 0-15) instead of X groups
 
 struct GramArgs {
   const uint16_t* X;     // [G, N, IN] bf16
   const uint16_t* Y;     // [G, N, D] bf16
-  float* gram;           // [G, IN, IN] fp32 (upper 256-tiles written)
+  float* gram;           // [G, IN, IN] fp32 (the 128-blocks on and above the diagonal written)
   float* cross;          // [G, IN, D] fp32
   float* sums;           // [G, IN + D] fp32: column sums of X, then of Y
   int64_t N;
-  int32_t G, IN, nX;     // nX = column tiles of X (IN / 256 rounded up)
-  int32_t tiles;         // per group: nX (nX + 1) / 2 upper tiles + nX cross tiles
+  int32_t G, IN, nF;     // nF = IN / 128 feature groups
+  int32_t tiles;         // workgroups per group (ridge_tiles_per_group)
 };
+
+// The operand tiles of a workgroup: which 128-feature groups of X its A
+// tile holds in pieces 0-15 and 16-31 (-1: none, read as zeros), and the
+// same for its B tile, or b0 = kYTile: the B tile holds Y.
+struct TileJob {
+  int a0, a1, b0, b1;
+};
+
+// What one wave computes (wave-uniform).
+enum Mode {
+  kIdle = 0,     // copies only
+  kFull = 1,     // a 128 x 128 block
+  kFullSumA = 2, // a diagonal 128 x 128 block (B = A) and the column sums of its features
+  kFullSumB = 3, // a 128 x 128 block of X^T Y and the column sums of Y
+  kHalfY = 4     // a 128 x 64 block of X^T Y
+};
+struct WaveJob {
+  int mode;
+  int a_p0, b_p0;   // first 16-byte piece of the wave's A rows / B columns in its tile
+  bool b_in_a;      // B columns come from the A tile
+  bool cross;       // the block belongs to X^T Y (else X^T X)
+  int row0, col0;   // the block's first row (feature) and column (feature or Y column)
+  int sum0;         // first sums entry the wave writes (kFullSumA / kFullSumB)
+};
+
+// The work of workgroup (tile) t of a group: first the diagonal tiles r <
+// nD = ceil(nF/2) (groups 2r, 2r+1: their three X^T X blocks on three
+// waves, the X^T Y block of group 2r on the fourth, with Y in the B tile
+// that a diagonal tile does not otherwise need), then the off-diagonal
+// tiles (r, c), r < c, in row order (four X^T X blocks), then the X^T Y
+// blocks of the odd groups two per tile, as 128 x 64 halves on four waves.
+// The column sums ride on the waves that already hold the fragments: the
+// diagonal blocks' waves sum their features, the first tile's X^T Y wave
+// sums Y.
+__device__ __forceinline__ void decode_tile(const GramArgs& a, int t, int w, TileJob& tj, WaveJob& wj) {
+  const int nF = a.nF, nD = (nF + 1) / 2, nP = nD * (nD - 1) / 2;
+  const int wm = w >> 1, wn = w & 1;
+  auto grp = [&](int i) { return i < nF ? i : -1; };
+  wj = WaveJob{kIdle, 0, 0, false, false, 0, 0, 0};
+  if (t < nD) {
+    const int r = t, f0 = kGroupW * 2 * r, f1 = f0 + kGroupW;
+    tj = TileJob{2 * r, grp(2 * r + 1), kYTile, -1};
+    const bool two = tj.a1 >= 0;
+    if (w == 0)
+      wj = WaveJob{kFullSumA, 0, 0, true, false, f0, f0, f0};
+    else if (w == 1 && two)
+      wj = WaveJob{kFull, 0, 16, true, false, f0, f1, 0};
+    else if (w == 2)
+      wj = WaveJob{r == 0 ? kFullSumB : kFull, 0, 0, false, true, f0, 0, a.IN};
+    else if (w == 3 && two)
+      wj = WaveJob{kFullSumA, 16, 16, true, false, f1, f1, f1};
+  } else if (t < nD + nP) {
+    int left = t - nD, r = 0;
+    while (left >= nD - 1 - r) {
+      left -= nD - 1 - r;
+      ++r;
+    }
+    const int c = r + 1 + left;
+    tj = TileJob{2 * r, grp(2 * r + 1), 2 * c, grp(2 * c + 1)};
+    const int ga = wm ? tj.a1 : tj.a0, gb = wn ? tj.b1 : tj.b0;
+    if (ga >= 0 && gb >= 0) wj = WaveJob{kFull, 16 * wm, 16 * wn, false, false, kGroupW * ga, kGroupW * gb, 0};
+  } else {
+    const int ci = t - nD - nP;
+    tj = TileJob{4 * ci + 1, grp(4 * ci + 3), kYTile, -1};
+    const int ga = wm ? tj.a1 : tj.a0;
+    if (ga >= 0) wj = WaveJob{kHalfY, 16 * wm, 8 * wn, false, true, kGroupW * ga, 64 * wn, 0};
+  }
+}
 
 // Swizzle of observation row t (multiples of 4 in 0..28: XOR on piece bits 2..4).
 __device__ __forceinline__ int row_swz(int t) { return 4 * ((t & 3) + 4 * ((t >> 3) & 1)); }
@@ -88,45 +164,52 @@ __device__ __forceinline__ bf16x8 read_frag(const char* tile, uint32_t lane_off,
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// s + the sum of the 8 values of a fragment (v_dot2_f32_bf16 against ones)
+__device__ __forceinline__ float frag_sum(const bf16x8& v, float s) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, s, false);
+}
+
 struct GramSmem {
   char A[2][kKB * kRowBytes] __attribute__((aligned(16)));
   char B[2][kKB * kRowBytes] __attribute__((aligned(16)));
 };
 
-template <int ROLE>
-__device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int64_t g, int rt, int ct, int w,
-                                           int lane, f32x16 (&acc)[4][4]) {
-  const int wm = w >> 1, wn = w & 1;
-  const bool cross_tile = ct == a.nX;
+template <int MODE>
+__device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int64_t g, const TileJob& tj,
+                                           const WaveJob& wj, int w, int lane, f32x16 (&acc)[4][4],
+                                           float (&tot)[4]) {
+  constexpr int NB = MODE == kHalfY ? 2 : 4;            // B 32-column blocks of the wave
+  constexpr bool kSame = MODE == kFullSumA;             // B fragments = A fragments
   const int64_t N = a.N;
   const int IN = a.IN;
   const int n_steps = (int)((N + kKB - 1) / kKB);
   const uint16_t* Xg = a.X + g * N * IN;
   const uint16_t* Yg = a.Y + g * N * kD;
+  const bool b_is_y = tj.b0 == kYTile;
 
   // ---- copies: wave w issues instructions n = w + 4jj (jj < 8) of each
   // operand; instruction n fills tile rows 2n, 2n+1, lane i row 2n + i/32,
-  // slot i % 32, i.e. the piece (i % 32) ^ row_swz(row).  A: X features
-  // 256 rt + 8 piece; B: X features 256 ct + 8 piece, or Y features 8 piece
-  // (pieces past 15 of Y, and features past IN, read zeros).
+  // slot i % 32, i.e. the piece (i % 32) ^ row_swz(row).  Piece p of an X
+  // tile holds features 128 (p < 16 ? g0 : g1) + 8 (p % 16) of its groups;
+  // pieces of a missing group, and pieces past 15 of a Y tile, read zeros.
   const int slot_i = lane & 31;
-  auto piece_of = [&](int jj) __attribute__((always_inline)) {
-    const int r = 2 * (w + 4 * jj) + (lane >> 5);
-    return slot_i ^ row_swz(r);
-  };
-  auto a_voff = [&](int jj) __attribute__((always_inline)) {
-    const int r = 2 * (w + 4 * jj) + (lane >> 5);
-    const int f = kFT * rt + 8 * piece_of(jj);
-    return f < IN ? (uint32_t)r * IN * 2 + 2 * f : kSkip;
+  auto row_of = [&](int jj) __attribute__((always_inline)) { return 2 * (w + 4 * jj) + (lane >> 5); };
+  auto x_voff = [&](int jj, int g0, int g1) __attribute__((always_inline)) {
+    const int r = row_of(jj), p = slot_i ^ row_swz(r);
+    const int gr = p < 16 ? g0 : g1;
+    return gr >= 0 ? (uint32_t)r * IN * 2 + 2 * (kGroupW * gr + 8 * (p & 15)) : kSkip;
   };
   auto b_voff = [&](int jj) __attribute__((always_inline)) {
-    const int r = 2 * (w + 4 * jj) + (lane >> 5);
-    if (cross_tile) {
-      const int p = piece_of(jj);
+    if (b_is_y) {
+      const int r = row_of(jj), p = slot_i ^ row_swz(r);
       return p < kD / 8 ? (uint32_t)r * kD * 2 + 16 * p : kSkip;
     }
-    const int f = kFT * ct + 8 * piece_of(jj);
-    return f < IN ? (uint32_t)r * IN * 2 + 2 * f : kSkip;
+    return x_voff(jj, tj.b0, tj.b1);
   };
   // descriptors of step s: the observations from 64 s on (rows past N read zeros)
   auto a_rsrc = [&](int s) __attribute__((always_inline)) {
@@ -135,12 +218,12 @@ __device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int6
   };
   auto b_rsrc = [&](int s) __attribute__((always_inline)) {
     const int64_t t0 = (int64_t)s * kKB;
-    return cross_tile ? rsrc_words(Yg + t0 * kD, (uint32_t)((N - t0) * kD * 2))
-                      : rsrc_words(Xg + t0 * IN, (uint32_t)((N - t0) * IN * 2));
+    return b_is_y ? rsrc_words(Yg + t0 * kD, (uint32_t)((N - t0) * kD * 2))
+                  : rsrc_words(Xg + t0 * IN, (uint32_t)((N - t0) * IN * 2));
   };
   auto copy_one = [&](int p, int q, const u32x4& ra, const u32x4& rb) __attribute__((always_inline)) {
     if (q < kPer)
-      dma16(ra, a_voff(q), 0, sm.A[p] + 1024 * (w + 4 * q));
+      dma16(ra, x_voff(q, tj.a0, tj.a1), 0, sm.A[p] + 1024 * (w + 4 * q));
     else
       dma16(rb, b_voff(q - kPer), 0, sm.B[p] + 1024 * (w + 4 * (q - kPer)));
   };
@@ -148,28 +231,19 @@ __device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int6
   // ---- fragment reads: lane l (16-lane group gg = l/16: feature half fb =
   // gg%2, k-group kg = gg/2; in the group e = (l%16)/4, q = l%4) names
   // observation row 8kg + e (+ 16ks + 4r) and features 32mb + 16fb + 4q ..
-  // +3 of its wave's 128; it receives feature 32mb + 16fb + l%16 of 4 rows.
+  // +3 of its wave's 128; it receives feature 32mb + 16fb + l%16 (= 32mb +
+  // l%32) of 4 rows.  Lanes l and l + 32 hold different observations.
   const int gg = lane >> 4, fb = gg & 1, kg = gg >> 1, e = (lane >> 2) & 3, q4 = lane & 3;
   const int trow = 8 * kg + e;
   const uint32_t row_base = (uint32_t)trow * kRowBytes + 8 * (q4 & 1);
-  // A rows: the wave's 128 X features (the sums waves read the same rows as
-  // the products waves of their row half); B columns likewise
-  const int a_half = wm, b_half = (ROLE == kSums) ? 0 : wn;
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[4], b_off[NB];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int pa = 16 * a_half + 4 * mb + 2 * fb + (q4 >> 1);
-    const int pb = 16 * b_half + 4 * mb + 2 * fb + (q4 >> 1);
-    a_off[mb] = row_base + 16 * (pa ^ row_swz(trow));
-    b_off[mb] = row_base + 16 * (pb ^ row_swz(trow));
-  }
-  // constant fragment: 1.0 in row (column) 0 of its 32, 0 elsewhere
-  bf16x8 ones;
+  for (int mb = 0; mb < 4; ++mb) a_off[mb] = row_base + 16 * ((wj.a_p0 + 4 * mb + 2 * fb + (q4 >> 1)) ^ row_swz(trow));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (lane & 31) == 0 ? (__bf16)1.0f : (__bf16)0.0f;
+  for (int nb = 0; nb < NB; ++nb) b_off[nb] = row_base + 16 * ((wj.b_p0 + 4 * nb + 2 * fb + (q4 >> 1)) ^ row_swz(trow));
 
   // step 0 in flight, then the pipeline: the copies of step s+1 go out
-  // between the first 32 products of step s
+  // between the first half of the products of step s
   {
     const u32x4 ra = a_rsrc(0), rb = b_rsrc(0);
 #pragma unroll
@@ -177,37 +251,42 @@ __device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int6
   }
   wait_vmcnt<0>();
   lds_barrier();
+  constexpr int kStride = NB / 2;   // products per copy in the first half of a step
   for (int s = 0; s < n_steps; ++s) {
     const int p = s & 1;
     const bool more = s + 1 < n_steps;
     const u32x4 ra = a_rsrc(more ? s + 1 : s), rb = b_rsrc(more ? s + 1 : s);
     const char* At = sm.A[p];
-    const char* Bt = sm.B[p];
+    const char* Bt = wj.b_in_a ? sm.A[p] : sm.B[p];
+    // this step's column sums (added to the totals once per step, so that
+    // each total takes N / 64 additions)
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kKB / 16; ++ks) {
-      bf16x8 af[4], bfr[4];
-      if constexpr (ROLE != kIdle) {
+      bf16x8 af[4], bfr[NB];
+      if constexpr (MODE != kIdle) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          af[i] = read_frag(At, a_off[i], ks);
-          bfr[i] = read_frag(Bt, b_off[i], ks);
-        }
+        for (int i = 0; i < 4; ++i) af[i] = read_frag(At, a_off[i], ks);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) bfr[i] = kSame ? af[i] : read_frag(Bt, b_off[i], ks);
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          if constexpr (ROLE == kProducts) {
+        for (int nb = 0; nb < NB; ++nb) {
+          if constexpr (MODE != kIdle)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-          } else if constexpr (ROLE == kSums) {
-            // acc[0][mb]: sums of the wave's X features (times a ones column);
-            // acc[1][nb]: sums of the Y features (a ones row times Y)
-            if (nb == 0) acc[0][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], ones, acc[0][mb], 0, 0, 0);
-            if (mb == 0) acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, bfr[nb], acc[1][nb], 0, 0, 0);
-          }
-          const int m = 16 * ks + 4 * mb + nb;
-          if (more && (m & 1) && m / 2 < 2 * kPer) copy_one(p ^ 1, m / 2, ra, rb);
+          if constexpr (MODE == kFullSumA)
+            if (nb == 0) part[mb] = frag_sum(af[mb], part[mb]);
+          if constexpr (MODE == kFullSumB)
+            if (mb == 0) part[nb] = frag_sum(bfr[nb], part[nb]);
+          const int m = 4 * NB * ks + NB * mb + nb;   // product index within the step
+          if (more && m % kStride == kStride - 1 && m / kStride < 2 * kPer) copy_one(p ^ 1, m / kStride, ra, rb);
         }
+    }
+    if constexpr (MODE == kFullSumA || MODE == kFullSumB) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tot[i] += part[i];
     }
     wait_vmcnt<0>();
     lds_barrier();   // step s+1 landed everywhere; everyone is done with buffer p
@@ -218,99 +297,64 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_gram_kernel(GramArgs a) {
   __shared__ GramSmem sm;
   // tile of this workgroup: with groups a multiple of 8, all tiles of group
   // g run on XCD g % 8 (workgroup id mod 8) and share its L2
-  const int64_t b = blockIdx.x;
+  const int64_t bid = blockIdx.x;
   int64_t g;
   int t;
   if (a.G % 8 == 0) {
-    const int64_t q = b / 8;
-    g = b % 8 + 8 * (q / a.tiles);
+    const int64_t q = bid / 8;
+    g = bid % 8 + 8 * (q / a.tiles);
     t = (int)(q % a.tiles);
   } else {
-    g = b / a.tiles;
-    t = (int)(b % a.tiles);
-  }
-  // tile t: the upper X^T X tiles (rt <= ct) in row order, then X^T Y for
-  // every row tile (ct = nX)
-  int rt = 0, ct;
-  const int n_upper = a.nX * (a.nX + 1) / 2;
-  if (t < n_upper) {
-    int left = t;
-    while (left >= a.nX - rt) {
-      left -= a.nX - rt;
-      ++rt;
-    }
-    ct = rt + left;
-  } else {
-    rt = t - n_upper;
-    ct = a.nX;
+    g = bid / a.tiles;
+    t = (int)(bid % a.tiles);
   }
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
-  const bool cross_tile = ct == a.nX;
   const int IN = a.IN;
-  // role of this wave: products where its rows and columns are real
-  // features (the lower half of a diagonal tile is the mirror of the upper:
-  // skipped), column sums in the spare half of a cross tile
-  int role;
-  const bool rows_ok = kFT * rt + 128 * wm < IN;
-  if (cross_tile)
-    role = !rows_ok ? kIdle : wn == 0 ? kProducts : kSums;
-  else
-    role = (rows_ok && kFT * ct + 128 * wn < IN && !(rt == ct && wm > wn)) ? kProducts : kIdle;
+  TileJob tj;
+  WaveJob wj;
+  decode_tile(a, t, w, tj, wj);
 
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  if (role == kProducts)
-    gram_steps<kProducts>(a, sm, g, rt, ct, w, lane, acc);
-  else if (role == kSums)
-    gram_steps<kSums>(a, sm, g, rt, ct, w, lane, acc);
-  else
-    gram_steps<kIdle>(a, sm, g, rt, ct, w, lane, acc);
+  float tot[4] = {0.f, 0.f, 0.f, 0.f};
+  switch (wj.mode) {
+    case kFull: gram_steps<kFull>(a, sm, g, tj, wj, w, lane, acc, tot); break;
+    case kFullSumA: gram_steps<kFullSumA>(a, sm, g, tj, wj, w, lane, acc, tot); break;
+    case kFullSumB: gram_steps<kFullSumB>(a, sm, g, tj, wj, w, lane, acc, tot); break;
+    case kHalfY: gram_steps<kHalfY>(a, sm, g, tj, wj, w, lane, acc, tot); break;
+    default: gram_steps<kIdle>(a, sm, g, tj, wj, w, lane, acc, tot); break;
+  }
 
   // ---- epilogue: accumulator register r of a 32 x 32 block holds row
   // 8(r/4) + 4(lane/32) + r%4, column lane%32
   const int col = lane & 31, rgrp = 4 * (lane >> 5);
-  if (role == kProducts) {
-    float* out;
-    int64_t ld;
-    int c0;
-    if (cross_tile) {
-      out = a.cross + g * (int64_t)IN * kD;
-      ld = kD;
-      c0 = 0;
-    } else {
-      out = a.gram + g * (int64_t)IN * IN;
-      ld = IN;
-      c0 = kFT * ct + 128 * wn;
-    }
-    const int r0 = kFT * rt + 128 * wm;
+  if (wj.mode != kIdle) {
+    float* out = wj.cross ? a.cross + g * (int64_t)IN * kD : a.gram + g * (int64_t)IN * IN;
+    const int64_t ld = wj.cross ? kD : IN;
+    const int nbs = wj.mode == kHalfY ? 2 : 4;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
+        if (nb < nbs) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = r0 + 32 * mb + 8 * (r >> 2) + rgrp + (r & 3);
-          out[(int64_t)row * ld + c0 + 32 * nb + col] = acc[mb][nb][r];
+          for (int r = 0; r < 16; ++r) {
+            const int row = wj.row0 + 32 * mb + 8 * (r >> 2) + rgrp + (r & 3);
+            out[(int64_t)row * ld + wj.col0 + 32 * nb + col] = acc[mb][nb][r];
+          }
         }
-  } else if (role == kSums) {
-    float* sums = a.sums + g * (int64_t)(IN + kD);
-    // X sums: column 0 of acc[0][mb] (lanes 0 and 32), rows of the wave's half
-    if (col == 0) {
+  }
+  if (wj.mode == kFullSumA || wj.mode == kFullSumB) {
+    // lanes l and l + 32 summed different observations of column 32i + l%32
+    float* sums = a.sums + g * (int64_t)(IN + kD) + wj.sum0;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sums[kFT * rt + 128 * wm + 32 * mb + 8 * (r >> 2) + rgrp + (r & 3)] = acc[0][mb][r];
-    }
-    // Y sums: row 0 of acc[1][nb] (register 0, lanes 0..31), once per group
-    if (rt == 0 && wm == 0 && lane < 32) {
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) sums[IN + 32 * nb + col] = acc[1][nb][0];
+    for (int i = 0; i < 4; ++i) {
+      const float v = tot[i] + __shfl_xor(tot[i], 32);
+      if (lane < 32) sums[32 * i + lane] = v;
     }
   }
 }
@@ -526,8 +570,8 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
 }  // namespace
 
 int64_t ridge_tiles_per_group(int32_t IN) {
-  const int64_t nX = (IN + kFT - 1) / kFT;
-  return nX * (nX + 1) / 2 + nX;
+  const int64_t nF = IN / kGroupW, nD = (nF + 1) / 2;
+  return nD + nD * (nD - 1) / 2 + (nF / 2 + 1) / 2;
 }
 
 bool ridge_supports(const RidgeFit& f) {
@@ -549,7 +593,7 @@ hipError_t launch_ridge(const RidgeFit& f, bool gram, bool solve, hipStream_t st
     a.N = f.N;
     a.G = (int32_t)f.G;
     a.IN = f.IN;
-    a.nX = (f.IN + kFT - 1) / kFT;
+    a.nF = f.IN / kGroupW;
     a.tiles = (int32_t)ridge_tiles_per_group(f.IN);
     hipLaunchKernelGGL(ridge_gram_kernel, dim3((unsigned)(f.G * a.tiles)), dim3(kThreads), 0, stream, a);
   }
