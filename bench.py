@@ -39,6 +39,7 @@ MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 matrix cores
 
 
 COUNTERS_MD = os.path.join(ROOT, "profiles", "transfer_mfma_qwen3_14b_32b_t32k_counters.md")
+PAGED_MD = os.path.join(ROOT, "profiles", "transfer_mfma_paged_32req_counters.md")
 KERNEL_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "transfer_mfma.hip")
 COSINE_MD = os.path.join(ROOT, "profiles", "kv_cosine_qwen3_14b_32b_t32k.md")
 COSINE_SRC = os.path.join(ROOT, "cross_model_kv_helm_amd", "csrc", "cosine.hip")
@@ -261,6 +262,7 @@ def paged_leg(hk, synth, steps, stream):
     ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
     B, F, parts = algorithmic_work(w, c["layer_sel"].cpu().numpy(), N)
     B += 2 * lay.src_bt.size * 4 + (len(lay.lens) + 1) * 4   # the block tables and cu_seqlens
+    traffic, note = recorded_traffic(PAGED_MD, KERNEL_SRC)
     log(f"paged transfer: {ms:.3f} ms for {N} tokens, {N / ms * 1e3 / 1e6:.2f} M tok/s, "
         f"{B / (ms * 1e-3) / 1e12:.2f} TB/s algorithmic")
     del src_k_pool, src_v_pool, tk, tv, ws, c
@@ -270,9 +272,8 @@ def paged_leg(hk, synth, steps, stream):
             "config": {"src_layers": w.n_src_layers, "tgt_layers": w.n_tgt_layers, "kv_heads": w.n_kv_heads,
                        "head_dim": w.head_dim, "k": w.k, "block_size": lay.block_size},
             "roofline": {"bound": "hbm", "achieved": B / (ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                         "frac": B / (ms * 1e-3) / HBM_PEAK, "traffic": None, "algorithmic_bytes": B,
-                         "mfma_frac": F / (ms * 1e-3) / MFMA_BF16_PEAK,
-                         "traffic_source": "not collected for the paged instantiations"}}
+                         "frac": B / (ms * 1e-3) / HBM_PEAK, "traffic": traffic, "algorithmic_bytes": B,
+                         "mfma_frac": F / (ms * 1e-3) / MFMA_BF16_PEAK, "traffic_source": note}}
 
 
 def ridge_leg(hk, synth, w, groups, steps, stream):
