@@ -5,12 +5,15 @@ The Qwen3 cache-mapping write-up, section "A linear bridge, strangely enough,
 suffices": each map is fitted by ridge regression on centred data with
 lambda = 0.01, the bias from the means.
 
-Tolerance, derived from the arithmetic.  The library accumulates X^T X,
-X^T Y and the column sums in fp32 from exact bf16 products, 16 products per
-matrix instruction, so an entry carries at most (N/16) * 2^-24 * sum|x_i x_j|
-of rounding error; the centring subtracts sx sx^T / N (in fp64), so relative
-to the centred matrix A the error is bounded by
-    eps_A = (N/16) * 2^-24 * (1 + max mean^2 / min variance) * (a small factor).
+Tolerance, derived from the arithmetic.  The library accumulates X^T X and
+X^T Y in fp32 from exact bf16 products, 16 products per matrix instruction,
+so an entry carries at most (N/16) * 2^-24 * sum|x_i x_j| of rounding error.
+The column sums add 2 values per instruction into a per-lane partial of at
+most 32 values, which joins the running sum once per 64 observations: at
+most (32 + N/64) * 2^-24 * sum|x_i|.  The centring subtracts sx sx^T / N (in
+fp64), so relative to the centred matrix A the error is bounded by
+    eps_A = max(N/16, 32 + N/64) * 2^-24 * (1 + max mean^2 / min variance)
+            * (a small factor).
 A solve turns that into at most cond(A) * eps_A relative error in W, and the
 result is rounded to fp32.  Each test computes cond(A) from the oracle's own
 centred data and checks  max|W - W_ref| <= 4 * cond(A) * eps_A * max|W_ref| +
@@ -67,7 +70,7 @@ def check(X, Y, W, b, lam, label, groups=None):
         A = xc.T @ xc + lam * np.eye(IN)
         cond = np.linalg.cond(A)
         ratio = 1.0 + (mx ** 2).max() / max(xc.var(axis=0).min(), 1e-30)
-        eps_a = (N / 16) * 2.0 ** -24 * ratio
+        eps_a = max(N / 16, 32 + N / 64) * 2.0 ** -24 * ratio
         scale = np.abs(Wr).max()
         tol_w = 4 * cond * eps_a * scale + 2.0 ** -23 * scale
         err_w = np.abs(Wg[gi] - Wr).max()
@@ -119,6 +122,15 @@ def test_ridge_in1024():
     """IN = 1024 (the largest width: four X tiles, ten upper tiles), N = 2500."""
     X, Y = draw(1, 2500, 1024, 5, mean=0.5)
     check(X, Y, *fit(X, Y, 0.01), 0.01, "ridge G1 N2500 IN1024")
+
+
+@pytest.mark.parametrize("IN", [640, 768, 896])
+def test_ridge_five_to_seven_feature_groups(IN):
+    """IN = 640 / 768 / 896: 5, 6 and 7 groups of 128 features, the widths
+    whose last diagonal tile holds a single group (5, 7) and whose X^T Y
+    blocks of the odd groups leave a half-empty pairing tile (6, 7)."""
+    X, Y = draw(2, 1500, IN, 20 + IN // 128, mean=0.5)
+    check(X, Y, *fit(X, Y, 0.01), 0.01, f"ridge G2 N1500 IN{IN}")
 
 
 def test_ridge_stages_equal_one_call():
