@@ -400,23 +400,22 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
 
   // centred normal matrix + lambda I (upper: row j, columns i >= j) and
   // centred right-hand sides X^T Y - sx sy^T / N
-  // (rows in batches of kRB, their loads issued together)
-  for (int j0 = 0; j0 < n; j0 += kRB) {
-    double sj[kRB];
-#pragma unroll
-    for (int u = 0; u < kRB; ++u) sj[u] = sx[j0 + u];
+  // (rows in batches of kRBs, their loads issued together)
+  constexpr int kRBs = 32;
+  static_assert(128 % kRBs == 0, "input widths are multiples of 128");
+  for (int j0 = 0; j0 < n; j0 += kRBs) {
     for (int i = j0 + tid; i < ld; i += kThreads) {
       const bool a_part = i < n;
       const double si = a_part ? (double)sx[i] : (double)sy[i - n];
-      double raw[kRB];
+      float raw[kRBs];
 #pragma unroll
-      for (int u = 0; u < kRB; ++u)
-        raw[u] = a_part ? (i >= j0 + u ? (double)G[(int64_t)(j0 + u) * n + i] : 0.0)
-                        : (double)C[(int64_t)(j0 + u) * kD + (i - n)];
+      for (int u = 0; u < kRBs; ++u)
+        raw[u] = a_part ? (i >= j0 + u ? G[(int64_t)(j0 + u) * n + i] : 0.0f) : C[(int64_t)(j0 + u) * kD + (i - n)];
 #pragma unroll
-      for (int u = 0; u < kRB; ++u) {
+      for (int u = 0; u < kRBs; ++u) {
         const int j = j0 + u;
-        if (!a_part || i >= j) M[(int64_t)j * ld + i] = raw[u] - sj[u] * si * invN + (i == j ? a.lambda : 0.0);
+        if (!a_part || i >= j)
+          M[(int64_t)j * ld + i] = (double)raw[u] - (double)sx[j] * si * invN + (i == j ? a.lambda : 0.0);
       }
     }
   }
@@ -505,11 +504,27 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
   }
 
   // ---- back substitution U W = Z, panels from the last: W_K from the
-  // diagonal block, then Z rows above it lose U[j][K] W_K
+  // diagonal block, then Z rows above it lose U[j][K] W_K.  The panel's
+  // column block of U above the diagonal (rows j < k0) is staged in the
+  // panel rows' LDS as Pn(r, kD + j) = U[j][k0 + r], read back by every
+  // lane of a wave at once.
   for (int k0 = ((n - 1) / kP) * kP; k0 >= 0; k0 -= kP) {
     for (int e = tid; e < kP * kP; e += kThreads) {
       const int r = e / kP, c = e % kP;
       if (c >= r) Dg[r][c] = M[(int64_t)(k0 + r) * ld + k0 + c];
+    }
+    for (int e0 = tid; e0 < k0 * kP; e0 += kRB * kThreads) {
+      double t[kRB];
+#pragma unroll
+      for (int u = 0; u < kRB; ++u) {
+        const int e = e0 + u * kThreads;
+        t[u] = e < k0 * kP ? M[(int64_t)(e / kP) * ld + k0 + e % kP] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kRB; ++u) {
+        const int e = e0 + u * kThreads;
+        if (e < k0 * kP) Pn(e % kP, kD + e / kP) = t[u];
+      }
     }
     __syncthreads();
     if (tid < kD) {
@@ -546,7 +561,7 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
 #pragma unroll
         for (int r = 0; r < kP; ++r)
 #pragma unroll
-          for (int u = 0; u < kRB; ++u) v[u] += M[(int64_t)(j0 + u) * ld + k0 + r] * wv[r];
+          for (int u = 0; u < kRB; ++u) v[u] += Pn(r, kD + j0 + u) * wv[r];
 #pragma unroll
         for (int u = 0; u < kRB; ++u) M[(int64_t)(j0 + u) * ld + n + d] = mv[u] - v[u];
       }
@@ -562,7 +577,13 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
   }
   if (tid < kD) {
     double v = (double)sy[tid] * invN;
-    for (int i = 0; i < n; ++i) v -= (double)sx[i] * invN * M[(int64_t)i * ld + n + tid];
+    for (int i0 = 0; i0 < n; i0 += kRB) {   // (n is a multiple of kRB)
+      double mv[kRB];
+#pragma unroll
+      for (int u = 0; u < kRB; ++u) mv[u] = M[(int64_t)(i0 + u) * ld + n + tid];
+#pragma unroll
+      for (int u = 0; u < kRB; ++u) v -= (double)sx[i0 + u] * invN * mv[u];
+    }
     a.b[g * kD + tid] = (float)v;
   }
 }
