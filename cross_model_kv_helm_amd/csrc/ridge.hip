@@ -43,8 +43,9 @@
 //     and b from the means.  Each panel pass reads and writes the trailing
 //     part of the group's fp64 matrix (2.6 MB at IN = 512, beyond L2 and the
 //     last-level cache for 1,024 groups), so the kernel is bound by those
-//     HBM passes; each memory loop issues 8 rows' accesses at once, and the
-//     panel rows sit in LDS sized to IN.
+//     HBM passes; each memory loop issues 8 rows' accesses at once (32 in
+//     the setup pass), the back substitution stages its column block of U
+//     in LDS, and the panel rows sit in LDS sized to IN.
 #include "internal.hpp"
 #include "lds_dma.hpp"
 
