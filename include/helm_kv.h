@@ -280,10 +280,10 @@ int helm_kv_cosine(const void* k_mapped, const void* v_mapped,
  * independent groups g (one (target layer, head, K|V) map each), with
  * observations X[g] [N, IN] and targets Y[g] [N, D]:
  *   W[g] = (Xc^T Xc + lambda I)^-1 Xc^T Yc,   b[g] = mean(Y[g]) - mean(X[g]) W[g]
- * (Xc, Yc = the data minus its column means).  X^T X, X^T Y and the column
- * sums are accumulated in fp32 on the matrix cores (bf16 products are
- * exact); the centring, lambda, the Cholesky solve and b are fp64; W and b
- * are stored as fp32.
+ * (Xc, Yc = the data minus its column means).  X^T X and X^T Y are
+ * accumulated in fp32 on the matrix cores (bf16 products are exact), the
+ * column sums in fp32 on the vector ALU; the centring, lambda, the Cholesky
+ * solve and b are fp64; W and b are stored as fp32.
  *   X : [n_groups, n_obs, in_features] bf16, device, 16-byte aligned
  *   Y : [n_groups, n_obs, out_features] bf16, device, 16-byte aligned
  *   W : [n_groups, in_features, out_features] fp32 (in-major, the layout of
