@@ -275,6 +275,19 @@ def test_paged_small_full():
     pc.check(tk, tv)
 
 
+@pytest.mark.parametrize("k", [1, 3])
+def test_paged_k1_k3_full(k):
+    """The paged instantiations for k = 1 and k = 3 (the other tests take
+    k = 2 and 4): four requests whose lengths cross 32-token tiles and
+    16-token pages unevenly, with per-request target offsets."""
+    w = synth.Workload(f"paged_k{k}", 6, 5, 2, 128, 0, k, "bf16", 1e6, "same", 40 + k, paged=True,
+                       n_requests=4, max_offset=500)
+    pc = PagedCase(w, lens=[33, 70, 5, 129])
+    tk, tv = pc.run_gpu()
+    torch.cuda.synchronize()
+    pc.check(tk, tv)
+
+
 def test_paged_32_requests_sampled():
     w = synth.CONFIGS["paged_32req"]
     pc = PagedCase(w)
