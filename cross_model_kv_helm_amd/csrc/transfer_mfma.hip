@@ -78,7 +78,6 @@ constexpr int kDepth = 2;        // source-row register sets of a data thread (p
 constexpr int kTile = 32;        // tokens per tile = MFMA B-block width
 constexpr int kStageRows = 64;   // W rows staged per pass
 constexpr int kStageRow = kStageRows + 8;  // W^T staging row (padded)
-constexpr int kCtRow = kHalf + 2;          // staged target (cos, sin) row: 64 float2 + pad
 constexpr int kOtRow = kD + 8;             // staged output row: 128 bf16 + pad
 constexpr int kRowBytes = kD * 2;          // one bf16 head row
 constexpr int kCsTileBytes = kTile * kHalf * 8;   // one tile's (cos, sin) block (rope_index layout)
