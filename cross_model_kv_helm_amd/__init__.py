@@ -219,6 +219,19 @@ def _dev_ptr(t, name, dtype=None, shape=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _workspace_ptr(ws, device):
+    """(address, bytes) of a caller's workspace: a contiguous tensor on the
+    same GPU as the data (any dtype; its size in bytes counts)."""
+    import torch
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch tensor")
+    if ws.device.type != "cuda" or ws.device != torch.device(device):
+        raise ValueError(f"workspace must live on {device} (got {ws.device})")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
 def current_stream_ptr(device=None) -> int:
     import torch
     return int(torch.cuda.current_stream(device).cuda_stream)
@@ -269,8 +282,7 @@ def helm_kv_transfer_stage(stages: int, src_k, src_v, src_pos, tgt_pos, layer_se
         raise ValueError("a single stage needs the caller's workspace (the tables live there)")
     if workspace is None:
         workspace = torch.empty(helm_kv_workspace_bytes(shape), dtype=torch.uint8, device=src_k.device)
-    shape.workspace = workspace.data_ptr()
-    shape.workspace_bytes = workspace.numel()
+    shape.workspace, shape.workspace_bytes = _workspace_ptr(workspace, src_k.device)
     _raise(lib().helm_kv_transfer_stage(int(stages), *ptrs, ctypes.byref(shape)))
 
 
@@ -315,8 +327,7 @@ def helm_kv_transfer_wide_stage(stages: int, src_k, src_v, src_pos, tgt_pos, lay
         shape.stream = current_stream_ptr(src_k.device)
     if workspace is None:
         workspace = torch.empty(helm_kv_wide_workspace_bytes(shape), dtype=torch.uint8, device=src_k.device)
-    shape.workspace = workspace.data_ptr()
-    shape.workspace_bytes = workspace.numel()
+    shape.workspace, shape.workspace_bytes = _workspace_ptr(workspace, src_k.device)
     _raise(lib().helm_kv_transfer_wide_stage(int(stages), *ptrs, ctypes.byref(shape)))
 
 
@@ -381,8 +392,7 @@ def helm_kv_transfer_paged(src_k_pool, src_v_pool, src_block_table, tgt_block_ta
         s.stream = current_stream_ptr(src_k_pool.device)
     if workspace is None:
         workspace = torch.empty(helm_kv_paged_workspace_bytes(s), dtype=torch.uint8, device=src_k_pool.device)
-    s.workspace = workspace.data_ptr()
-    s.workspace_bytes = workspace.numel()
+    s.workspace, s.workspace_bytes = _workspace_ptr(workspace, src_k_pool.device)
     _raise(lib().helm_kv_transfer_paged(*ptrs, ctypes.byref(s)))
 
 
@@ -418,7 +428,6 @@ def helm_ridge_fit(X, Y, lam: float = 0.01, W=None, b=None, workspace=None, stag
     shape.stream = current_stream_ptr(X.device)
     if workspace is None:
         workspace = torch.empty(helm_ridge_workspace_bytes(shape), dtype=torch.uint8, device=X.device)
-    shape.workspace = workspace.data_ptr()
-    shape.workspace_bytes = workspace.numel()
+    shape.workspace, shape.workspace_bytes = _workspace_ptr(workspace, X.device)
     _raise(lib().helm_ridge_fit_stage(int(stages), *ptrs, ctypes.byref(shape)))
     return W, b

@@ -262,3 +262,13 @@ def test_ridge_workspace_and_refusals():
     for stages in (0, 4):
         assert L.helm_ridge_fit_stage(stages, *fake, ctypes.byref(s)) == 1
     assert L.helm_ridge_fit(None, *fake[1:], ctypes.byref(s)) == 1
+
+
+def test_binding_refuses_a_workspace_off_the_gpu():
+    """The binding hands the library only device memory: a caller's
+    workspace on the host, or not contiguous, is refused before any call."""
+    import torch
+    with pytest.raises(ValueError, match="workspace must live on"):
+        hk._workspace_ptr(torch.empty(64, dtype=torch.uint8), torch.device("cuda:0"))
+    with pytest.raises(TypeError):
+        hk._workspace_ptr(bytearray(64), torch.device("cuda:0"))
