@@ -59,6 +59,7 @@
 //     hardware drop any access outside the tensor.
 #include "internal.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace helm {
@@ -582,18 +583,18 @@ transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t 
   }
 }
 
-int g_cu_count = 0;
-
+// CUs of the current device, looked up once per device (safe from any thread)
 int cu_count() {
-  if (g_cu_count == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      g_cu_count = n;
-    else
-      g_cu_count = 256;
+  constexpr int kDevices = 64;
+  static std::atomic<int> counts[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
+  int n = counts[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev].store(n, std::memory_order_relaxed);
   }
-  return g_cu_count;
+  return n;
 }
 
 }  // namespace
