@@ -85,6 +85,17 @@ def test_wide_small_ragged_full():
     case.check(*out)
 
 
+@pytest.mark.parametrize("k", [3, 6])
+def test_wide_k3_k6_full(k):
+    """k = 3 (IN = 1,536 with two heads) and k = 6 (more selected layers
+    than the per-head kernel takes; IN = 1,536 with one head), 100 tokens."""
+    H = 2 if k == 3 else 1
+    case = WideCase(W(f"wide_k{k}", 8, 3, H, 128, 100, k, "bf16", 1e6, "shift4096", 70 + k))
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    case.check(*out)
+
+
 def test_wide_one_head_k1_short_full():
     """H = 1 (one column tile: the key map and the value map of head 0),
     k = 1 (IN = 256, four pipeline steps), 33 tokens."""
