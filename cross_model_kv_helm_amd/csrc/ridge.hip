@@ -45,7 +45,9 @@
 //     last-level cache for 1,024 groups), so the kernel is bound by those
 //     HBM passes; each memory loop issues 8 rows' accesses at once (32 in
 //     the setup pass), the back substitution stages its column block of U
-//     in LDS, and the panel rows sit in LDS sized to IN.
+//     in LDS, and the panel rows sit in LDS sized to IN.  At IN <= 512 two
+//     workgroups share a CU (80 KB of LDS each), so two groups' memory
+//     latency overlaps.
 #include "internal.hpp"
 #include "lds_dma.hpp"
 
@@ -385,8 +387,14 @@ __device__ __forceinline__ void wave_sync() {
 // Dynamic LDS of the solve kernel: the panel rows, kP x (IN + D - kP) fp64.
 size_t solve_lds_bytes(int32_t IN) { return (size_t)kP * (IN + kD - kP) * sizeof(double); }
 
-__global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
-  __shared__ double Dg[kP][kP + 1];
+// MIN_WAVES: waves per SIMD the register budget must allow.  With IN <= 512
+// the kernel's LDS (the panel rows and the diagonal block, unpadded) fits
+// twice in a CU, so it is built for two workgroups per CU: two groups'
+// memory latency overlap (some registers spill at that budget, and it still
+// runs faster).
+template <int MIN_WAVES>
+__global__ void __launch_bounds__(kThreads, MIN_WAVES) ridge_solve_kernel(SolveArgs a) {
+  __shared__ double Dg[kP][kP];
   extern __shared__ double pn_lds[];
   const int64_t g = blockIdx.x;
   const int n = a.IN, ld = n + kD, tid = threadIdx.x;
@@ -457,13 +465,18 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_solve_kernel(SolveArgs a) {
     // and the right-hand sides): solve U_kk^T X = panel, one column a thread
     const int m0 = k0 + kP, width = ld - m0;
     for (int c = tid; c < width; c += kThreads) {
+      // the diagonal block is read anew for each column (an opaque offset):
+      // hoisted out of the loop, its 136 values would hold registers
+      int dz = 0;
+      asm volatile("" : "+v"(dz));
+      const double* dg = &Dg[0][0] + dz;
       double x[kP];
 #pragma unroll
       for (int r = 0; r < kP; ++r) {
         double v = M[(int64_t)(k0 + r) * ld + m0 + c];
 #pragma unroll
-        for (int p = 0; p < r; ++p) v -= Dg[p][r] * x[p];
-        x[r] = v / Dg[r][r];
+        for (int p = 0; p < r; ++p) v -= dg[p * kP + r] * x[p];
+        x[r] = v / dg[r * kP + r];
       }
 #pragma unroll
       for (int r = 0; r < kP; ++r) {
@@ -631,12 +644,16 @@ hipError_t launch_ridge(const RidgeFit& f, bool gram, bool solve, hipStream_t st
     s.IN = f.IN;
     s.lambda = f.lambda;
     const size_t lds = solve_lds_bytes(f.IN);
+    const bool two = lds + sizeof(double) * kP * kP <= 80 * 1024;   // two workgroups' LDS in one CU
+    const void* fn = two ? (const void*)ridge_solve_kernel<2> : (const void*)ridge_solve_kernel<1>;
     if (lds > 65536) {
-      const hipError_t e = hipFuncSetAttribute((const void*)ridge_solve_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(ridge_solve_kernel, dim3((unsigned)f.G), dim3(kThreads), lds, stream, s);
+    if (two)
+      hipLaunchKernelGGL(ridge_solve_kernel<2>, dim3((unsigned)f.G), dim3(kThreads), lds, stream, s);
+    else
+      hipLaunchKernelGGL(ridge_solve_kernel<1>, dim3((unsigned)f.G), dim3(kThreads), lds, stream, s);
   }
   return hipGetLastError();
 }
