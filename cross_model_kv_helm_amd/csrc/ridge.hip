@@ -264,15 +264,22 @@ __device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int6
     // this step's column sums (added to the totals once per step, so that
     // each total takes N / 64 additions)
     float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < kKB / 16; ++ks) {
-      bf16x8 af[4], bfr[NB];
+    // fragments of slice ks + 1 are read while the products of slice ks run
+    bf16x8 afs[2][4], bfs[2][NB];
+    auto read_ks = [&](int ks, bf16x8* af, bf16x8* bfr) __attribute__((always_inline)) {
       if constexpr (MODE != kIdle) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) af[i] = read_frag(At, a_off[i], ks);
 #pragma unroll
         for (int i = 0; i < NB; ++i) bfr[i] = kSame ? af[i] : read_frag(Bt, b_off[i], ks);
       }
+    };
+    read_ks(0, afs[0], bfs[0]);
+#pragma unroll
+    for (int ks = 0; ks < kKB / 16; ++ks) {
+      bf16x8* af = afs[ks & 1];
+      bf16x8* bfr = bfs[ks & 1];
+      if (ks + 1 < kKB / 16) read_ks(ks + 1, afs[(ks + 1) & 1], bfs[(ks + 1) & 1]);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
