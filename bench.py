@@ -276,6 +276,69 @@ def paged_leg(hk, synth, steps, stream):
                          "mfma_frac": F / (ms * 1e-3) / MFMA_BF16_PEAK, "traffic_source": note}}
 
 
+def config_leg(hk, synth, name, steps, stream):
+    """One more contiguous configuration, timed like the main workload: whole
+    transfers (tables + map) with HIP events on the launch stream, inputs
+    resident in HBM; workloads that fit the 256 MB last-level cache get a
+    512 MB buffer rewritten between steps, so they are timed from HBM.  The
+    roofline divides the configuration's algorithmic bytes and flops by the
+    map stage's time in the same steps."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    w = synth.CONFIGS[name]
+    c = synth.contiguous_inputs(w, device=dev)
+    src_k = encode_keys_on_gpu(hk, c.pop("k_content"), c["src_pos"], w.theta)
+    T = src_k.shape[2]
+    out_k = torch.empty((w.n_tgt_layers, w.n_kv_heads, T, w.head_dim), dtype=src_k.dtype, device=dev)
+    out_v = torch.empty_like(out_k)
+    shape = hk.make_shape(src_k, c["W_k"], c["layer_sel"], w.theta, w.theta)
+    shape.stream = hk.current_stream_ptr(dev)
+    ws = torch.empty(hk.helm_kv_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if out_k.numel() * 8 < (1 << 30) else None
+
+    def st(stages):
+        hk.helm_kv_transfer_stage(stages, src_k, c["src_v"], c["src_pos"], c["tgt_pos"], c["layer_sel"], c["W_k"],
+                                  c["b_k"], c["W_v"], c["b_v"], out_k, out_v, shape, workspace=ws)
+
+    for _ in range(3):
+        st(hk.HELM_STAGE_ALL)
+    n = steps if flush is None else max(steps, 50)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        ev[i][0].record(stream)
+        st(hk.HELM_STAGE_TABLES)
+        ev[i][1].record(stream)
+        st(hk.HELM_STAGE_MAP)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e[0].elapsed_time(e[2]) for e in ev]))
+    kms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    B, F, parts = algorithmic_work(w, c["layer_sel"].cpu().numpy(), T)
+    t_hbm, t_mfma = B / HBM_PEAK, F / MFMA_BF16_PEAK
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    hbm_frac, mfma_frac = B / (kms * 1e-3) / HBM_PEAK, F / (kms * 1e-3) / MFMA_BF16_PEAK
+    log(f"{name}: transfer {ms:.4f} ms (median of {n}), map stage {kms:.4f} ms, HBM {hbm_frac:.3f}, "
+        f"MFMA {mfma_frac:.3f} of peak")
+    del src_k, out_k, out_v, ws, c, flush
+    torch.cuda.empty_cache()
+    roof = ({"bound": "hbm", "achieved": B / (kms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+             "frac": hbm_frac} if bound == "hbm" else
+            {"bound": "mfma", "achieved": F / (kms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+             "unit": "TFLOP/s", "frac": mfma_frac})
+    roof.update({"kernel_ms": kms, "hbm_frac": hbm_frac, "mfma_frac": mfma_frac, "algorithmic_bytes": B,
+                 "algorithmic_flops": F, "traffic": None, "binding_time_ms": max(t_hbm, t_mfma) * 1e3,
+                 "roofline_frac_of_binding": max(t_hbm, t_mfma) / (kms * 1e-3)})
+    return {"workload": name, "tokens": T, "ms_per_transfer": ms, "tokens_per_s": T / (ms * 1e-3),
+            "steps": n, "statistic": "median", "positions": w.positions,
+            "config": {"src_layers": w.n_src_layers, "tgt_layers": w.n_tgt_layers, "kv_heads": w.n_kv_heads,
+                       "head_dim": w.head_dim, "k": w.k},
+            "roofline": roof}
+
+
 def ridge_leg(hk, synth, w, groups, steps, stream):
     """The ridge fit of the maps at the calibration's shape: one group per
     (target layer, head, K|V) map of the 40 -> 64-layer pair (64 x 8 x 2 =
@@ -290,8 +353,12 @@ def ridge_leg(hk, synth, w, groups, steps, stream):
     dev = torch.device("cuda:0")
     N, IN, D = 131072, w.k * w.head_dim, w.head_dim
     per_group = N * (IN + D) * 2 + IN * IN * 4 + IN * D * 4 + (IN + D) * 4 + IN * (IN + D) * 8 + IN * D * 4 + D * 4
-    free, _ = torch.cuda.mem_get_info(dev)
-    fit_groups = min(groups, int((free - (8 << 30)) // per_group) // 8 * 8)
+    free, total = torch.cuda.mem_get_info(dev)
+    # headroom beyond the leg's own tensors: the input draws' 6 GiB of
+    # temporaries, and device memory that tools attached to the process
+    # (profilers collecting counters per dispatch) allocate as it runs
+    headroom = (6 << 30) + max(16 << 30, total // 20)
+    fit_groups = min(groups, int((free - headroom) // per_group) // 8 * 8)
     if fit_groups < 8:
         log(f"ridge fit: skipped ({free / 2**30:.1f} GiB free)")
         return {"skipped": f"{free / 2**30:.1f} GiB of device memory free"}
@@ -343,6 +410,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--wide", type=int, default=1, help="also time the wide-input map (0 = skip)")
     ap.add_argument("--paged", type=int, default=1, help="also time the paged transfer (0 = skip)")
+    ap.add_argument("--configs", default="qwen3_0.6b_1.7b_t512,qwen3_0.6b_1.7b_t2048,qwen3_14b_32b_t128k_shift",
+                    help="other contiguous configurations timed after the main one (comma list; '' = none)")
     ap.add_argument("--ridge-groups", type=int, default=1024,
                     help="groups of the ridge-fit leg (0 = skip); fewer when device memory is short")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -405,41 +474,32 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # each timed step is the two stages of one transfer, with an event
+    # between them: the step time (tables + map) and the transfer kernel's
+    # time (the map stage: its keys and values launches) come from the same
+    # launches, so the kernel time never exceeds the step time
     stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
         if flush is not None:
             flush.fill_(i & 0xFF)
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
+        ev[i][0].record(stream)
+        step(hk.HELM_STAGE_TABLES)
+        ev[i][1].record(stream)
+        step(hk.HELM_STAGE_MAP)
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])   # ms
+    per = np.array([e[0].elapsed_time(e[2]) for e in ev])   # ms
+    kper = np.array([e[1].elapsed_time(e[2]) for e in ev])
     ms = float(per.mean())
+    kms = float(kper.mean())
     log(f"per step: mean {ms:.4f} ms, median {np.median(per):.4f}, p10 {np.percentile(per, 10):.4f}, "
         f"p90 {np.percentile(per, 90):.4f}; wall {wall:.3f} s")
-
-    # the transfer kernel alone: the map stage, reading the tables the steps
-    # above left in the workspace (same positions)
-    log(f"timing {args.steps} launches of the transfer kernel alone")
-    kstarts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    kends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
-        kstarts[i].record(stream)
-        step(hk.HELM_STAGE_MAP)
-        kends[i].record(stream)
-    torch.cuda.synchronize()
-    kper = np.array([s.elapsed_time(e) for s, e in zip(kstarts, kends)])
-    kms = float(kper.mean())
-    log(f"transfer kernel: mean {kms:.4f} ms, median {np.median(kper):.4f}")
+    log(f"transfer kernel (map stage) in the same steps: mean {kms:.4f} ms, median {np.median(kper):.4f}")
 
     # the KV-cosine diagnostic on the mapped cache against a reference cache
     # of the same shape (here a copy: the timing does not depend on values)
@@ -457,15 +517,18 @@ def main():
     torch.cuda.synchronize()
     cms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(cstarts, cends)]))
     cos_bytes = 4 * out_k.numel() * out_k.element_size()   # both caches, K and V, read once
-    log(f"KV cosine: mean {cms:.4f} ms, {cos_bytes / cms / 1e6:.1f} GB/s; min cosine {cos_out.min().item():.6f}")
+    log(f"KV cosine: mean {cms:.4f} ms, {cos_bytes / cms / 1e6:.1f} GB/s (reference = a copy: timing only)")
     del ref_k, ref_v
     cos_traffic, cos_note = recorded_traffic(COSINE_MD, COSINE_SRC)
     kv_cos = {"ms": cms, "kernel": "kv_cosine_kernel",
+              "reference": "a copy of the mapped cache: the time does not depend on the values, so the "
+                           "cosines themselves carry no information here (parity tests check them)",
               "roofline": {"bound": "hbm", "achieved": cos_bytes / (cms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
                            "unit": "GB/s", "frac": cos_bytes / (cms * 1e-3) / HBM_PEAK, "traffic": cos_traffic,
                            "algorithmic_bytes": cos_bytes, "traffic_source": cos_note}}
 
     wide = wide_leg(hk, synth, w, src_k, c, out_k, out_v, args.steps, stream) if args.wide else None
+    others = [config_leg(hk, synth, nm, args.steps, stream) for nm in args.configs.split(",") if nm]
     paged = paged_leg(hk, synth, args.steps, stream) if args.paged else None
     ridge = ridge_leg(hk, synth, w, args.ridge_groups, args.steps, stream) if args.ridge_groups > 0 else None
 
@@ -506,7 +569,7 @@ def main():
         "ms_per_step": ms,
         "ms_per_transfer": ms,
         "higher_is_better": True,
-        "scaling": "weak",
+        "scaling": None,
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
@@ -516,6 +579,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "bytes_breakdown": parts,
+        "other_configs": others,
         "kv_cosine": kv_cos,
         "wide_map": wide,
         "paged": paged,

@@ -24,9 +24,10 @@ STATUS = {0: "HELM_OK", 1: "HELM_E_INVALID_ARG", 2: "HELM_E_PAIR_SHAPE", 3: "HEL
           8: "HELM_E_ALIAS", 9: "HELM_E_PAGED_TABLE", 10: "HELM_E_LAUNCH"}
 
 HELM_STAGE_TABLES, HELM_STAGE_MAP, HELM_STAGE_ALL = 1, 2, 3
+HELM_PATH_MATRIX, HELM_PATH_PORTABLE = 1, 2
 
-EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_stage", "helm_kv_transfer_paged", "helm_kv_cosine",
-            "helm_kv_transfer_wide", "helm_kv_transfer_wide_stage", "helm_kv_wide_workspace_bytes",
+EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_stage", "helm_kv_transfer_path", "helm_kv_transfer_paged",
+            "helm_kv_cosine", "helm_kv_transfer_wide", "helm_kv_transfer_wide_stage", "helm_kv_wide_workspace_bytes",
             "helm_ridge_fit", "helm_ridge_fit_stage", "helm_ridge_workspace_bytes", "helm_kv_workspace_bytes",
             "helm_kv_paged_workspace_bytes", "helm_mapper_check", "helm_paged_check",
             "helm_device_check", "helm_arch_supported", "helm_last_error", "helm_status_string",
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.helm_kv_transfer.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
         L.helm_kv_transfer_stage.argtypes = [ctypes.c_int] + [vp] * 11 + [ctypes.POINTER(HelmShape)]
         L.helm_kv_transfer_stage.restype = ctypes.c_int
+        L.helm_kv_transfer_path.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape), ctypes.POINTER(ctypes.c_int)]
+        L.helm_kv_transfer_path.restype = ctypes.c_int
         L.helm_kv_transfer_wide.restype = ctypes.c_int
         L.helm_kv_transfer_wide.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
         L.helm_ridge_workspace_bytes.restype = ctypes.c_size_t
@@ -237,6 +240,33 @@ def current_stream_ptr(device=None) -> int:
     return int(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _call_shape(shape, device):
+    """A copy of the caller's shape for one call, with the launch stream
+    resolved (the caller's stream, else torch's current stream on `device`
+    at this call); the caller's structure is left as it was."""
+    s = type(shape).from_buffer_copy(shape)
+    if not s.stream:
+        s.stream = current_stream_ptr(device) or None
+    return s
+
+
+def _own_workspace(nbytes, device, stream_ptr):
+    """A workspace allocated for one call.  It is freed when the call returns
+    while the kernels may still read it on the launch stream, so the caching
+    allocator is told that stream uses it (record_stream): the memory is not
+    handed to another allocation before that stream's work is done."""
+    import torch
+    dev = torch.device(device)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ptr = int(stream_ptr or 0)
+    if ptr != current_stream_ptr(dev):   # allocated on torch's current stream: nothing to record
+        launch = torch.cuda.default_stream(dev) if ptr == 0 else torch.cuda.ExternalStream(ptr, device=dev)
+        ws.record_stream(launch)
+    return ws
+
+
 def make_shape(src_k, W_k, layer_sel, theta_src: float, theta_tgt: float) -> HelmShape:
     """helm_shape_t from tensor shapes: src_k [L_s,H,T,D], W_k [L_t,H,k*D,D], layer_sel [L_t,k]."""
     L_s, H, T, D = src_k.shape
@@ -259,16 +289,12 @@ def helm_kv_transfer(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b
                            out_k, out_v, shape, workspace)
 
 
-def helm_kv_transfer_stage(stages: int, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v,
-                           out_k, out_v, shape: HelmShape, workspace=None) -> None:
-    """One or both stages of the transfer (HELM_STAGE_TABLES, HELM_STAGE_MAP,
-    HELM_STAGE_ALL); the map stage reads the tables an earlier tables stage
-    left in the same ``workspace``."""
+def _transfer_ptrs(shape, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v):
     import torch
     L_s, L_t, H, D, k, T = (shape.n_src_layers, shape.n_tgt_layers, shape.n_kv_heads,
                             shape.head_dim, shape.k, shape.n_tokens)
     dt = torch.bfloat16 if shape.dtype == HELM_BF16 else torch.float32
-    ptrs = [
+    return [
         _dev_ptr(src_k, "src_k", dt, (L_s, H, T, D)), _dev_ptr(src_v, "src_v", dt, (L_s, H, T, D)),
         _dev_ptr(src_pos, "src_pos", torch.int32, (T,)), _dev_ptr(tgt_pos, "tgt_pos", torch.int32, (T,)),
         _dev_ptr(layer_sel, "layer_sel", torch.int32, (L_t, k)),
@@ -276,14 +302,32 @@ def helm_kv_transfer_stage(stages: int, src_k, src_v, src_pos, tgt_pos, layer_se
         _dev_ptr(W_v, "W_v", dt, (L_t, H, k * D, D)), _dev_ptr(b_v, "b_v", torch.float32, (L_t, H, D)),
         _dev_ptr(out_k, "out_k", dt, (L_t, H, T, D)), _dev_ptr(out_v, "out_v", dt, (L_t, H, T, D)),
     ]
-    if not shape.stream:
-        shape.stream = current_stream_ptr(src_k.device)
+
+
+def helm_kv_transfer_stage(stages: int, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v,
+                           out_k, out_v, shape: HelmShape, workspace=None) -> None:
+    """One or both stages of the transfer (HELM_STAGE_TABLES, HELM_STAGE_MAP,
+    HELM_STAGE_ALL); the map stage reads the tables an earlier tables stage
+    left in the same ``workspace``."""
+    ptrs = _transfer_ptrs(shape, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v)
+    s = _call_shape(shape, src_k.device)
     if stages != HELM_STAGE_ALL and workspace is None:
         raise ValueError("a single stage needs the caller's workspace (the tables live there)")
     if workspace is None:
-        workspace = torch.empty(helm_kv_workspace_bytes(shape), dtype=torch.uint8, device=src_k.device)
-    shape.workspace, shape.workspace_bytes = _workspace_ptr(workspace, src_k.device)
-    _raise(lib().helm_kv_transfer_stage(int(stages), *ptrs, ctypes.byref(shape)))
+        workspace = _own_workspace(helm_kv_workspace_bytes(s), src_k.device, s.stream)
+    s.workspace, s.workspace_bytes = _workspace_ptr(workspace, src_k.device)
+    _raise(lib().helm_kv_transfer_stage(int(stages), *ptrs, ctypes.byref(s)))
+
+
+def helm_kv_transfer_path(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v,
+                          shape: HelmShape) -> int:
+    """HELM_PATH_MATRIX or HELM_PATH_PORTABLE: the kernel helm_kv_transfer
+    would run with these arguments (nothing is enqueued)."""
+    ptrs = _transfer_ptrs(shape, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v)
+    s = _call_shape(shape, src_k.device)
+    path = ctypes.c_int(0)
+    _raise(lib().helm_kv_transfer_path(*ptrs, ctypes.byref(s), ctypes.byref(path)))
+    return int(path.value)
 
 
 def helm_kv_wide_workspace_bytes(shape: HelmShape) -> int:
@@ -323,12 +367,11 @@ def helm_kv_transfer_wide_stage(stages: int, src_k, src_v, src_pos, tgt_pos, lay
         _dev_ptr(W_v, "W_v", dt, (L_t, H, IN, D)), _dev_ptr(b_v, "b_v", torch.float32, (L_t, H, D)),
         _dev_ptr(out_k, "out_k", dt, (L_t, H, T, D)), _dev_ptr(out_v, "out_v", dt, (L_t, H, T, D)),
     ]
-    if not shape.stream:
-        shape.stream = current_stream_ptr(src_k.device)
+    s = _call_shape(shape, src_k.device)
     if workspace is None:
-        workspace = torch.empty(helm_kv_wide_workspace_bytes(shape), dtype=torch.uint8, device=src_k.device)
-    shape.workspace, shape.workspace_bytes = _workspace_ptr(workspace, src_k.device)
-    _raise(lib().helm_kv_transfer_wide_stage(int(stages), *ptrs, ctypes.byref(shape)))
+        workspace = _own_workspace(helm_kv_wide_workspace_bytes(s), src_k.device, s.stream)
+    s.workspace, s.workspace_bytes = _workspace_ptr(workspace, src_k.device)
+    _raise(lib().helm_kv_transfer_wide_stage(int(stages), *ptrs, ctypes.byref(s)))
 
 
 def helm_kv_cosine(k_mapped, v_mapped, k_ref, v_ref, shape: HelmShape, out=None):
@@ -343,9 +386,8 @@ def helm_kv_cosine(k_mapped, v_mapped, k_ref, v_ref, shape: HelmShape, out=None)
     if out is None:
         out = torch.empty((2, L_t, H), dtype=torch.float32, device=k_mapped.device)
     optr = _dev_ptr(out, "out", torch.float32, (2, L_t, H))
-    if not shape.stream:
-        shape.stream = current_stream_ptr(k_mapped.device)
-    _raise(lib().helm_kv_cosine(*ptrs, optr, ctypes.byref(shape)))
+    s = _call_shape(shape, k_mapped.device)
+    _raise(lib().helm_kv_cosine(*ptrs, optr, ctypes.byref(s)))
     return out
 
 
@@ -388,10 +430,9 @@ def helm_kv_transfer_paged(src_k_pool, src_v_pool, src_block_table, tgt_block_ta
         _dev_ptr(tgt_k_pool, "tgt_k_pool", dt, (L_t, s.n_tgt_blocks, B, H, D)),
         _dev_ptr(tgt_v_pool, "tgt_v_pool", dt, (L_t, s.n_tgt_blocks, B, H, D)),
     ]
-    if not s.stream:
-        s.stream = current_stream_ptr(src_k_pool.device)
+    s = _call_shape(s, src_k_pool.device)
     if workspace is None:
-        workspace = torch.empty(helm_kv_paged_workspace_bytes(s), dtype=torch.uint8, device=src_k_pool.device)
+        workspace = _own_workspace(helm_kv_paged_workspace_bytes(s), src_k_pool.device, s.stream)
     s.workspace, s.workspace_bytes = _workspace_ptr(workspace, src_k_pool.device)
     _raise(lib().helm_kv_transfer_paged(*ptrs, ctypes.byref(s)))
 
@@ -427,7 +468,7 @@ def helm_ridge_fit(X, Y, lam: float = 0.01, W=None, b=None, workspace=None, stag
             _dev_ptr(W, "W", torch.float32, (G, IN, D)), _dev_ptr(b, "b", torch.float32, (G, D))]
     shape.stream = current_stream_ptr(X.device)
     if workspace is None:
-        workspace = torch.empty(helm_ridge_workspace_bytes(shape), dtype=torch.uint8, device=X.device)
+        workspace = _own_workspace(helm_ridge_workspace_bytes(shape), X.device, shape.stream)
     shape.workspace, shape.workspace_bytes = _workspace_ptr(workspace, X.device)
     _raise(lib().helm_ridge_fit_stage(int(stages), *ptrs, ctypes.byref(shape)))
     return W, b

@@ -307,13 +307,15 @@ int helm_paged_check(const helm_paged_shape_t* s, const int32_t* sbt, const int3
   return HELM_OK;
 }
 
-int helm_kv_transfer_stage(int stages, const void* src_k, const void* src_v, const int32_t* src_pos,
-                           const int32_t* tgt_pos, const int32_t* layer_sel, const void* W_k,
-                           const float* b_k, const void* W_v, const float* b_v, void* out_k, void* out_v,
-                           const helm_shape_t* s) {
-  clear_error();
-  if (stages < HELM_STAGE_TABLES || stages > HELM_STAGE_ALL)
-    return fail(HELM_E_INVALID_ARG, "stages = %d; expected 1 (tables), 2 (map) or 3 (both)", stages);
+}  // extern "C"
+
+namespace {
+// Every check of the contiguous transfer, then its kernel arguments.  With
+// need_workspace false (the path query) the workspace fields are not read
+// and the tables' addresses stand for any 256-byte aligned workspace.
+int contiguous_args(const void* src_k, const void* src_v, const int32_t* src_pos, const int32_t* tgt_pos,
+                    const int32_t* layer_sel, const void* W_k, const float* b_k, const void* W_v, const float* b_v,
+                    void* out_k, void* out_v, const helm_shape_t* s, bool need_workspace, helm::XferArgs& a) {
   if (!s) return fail(HELM_E_INVALID_ARG, "shape is NULL");
   int rc = check_common(common_of(s));
   if (rc != HELM_OK) return rc;
@@ -346,23 +348,26 @@ int helm_kv_transfer_stage(int stages, const void* src_k, const void* src_v, con
 
   Workspace w;
   if (!workspace_layout(s->n_tokens, s->head_dim, false, w)) return fail(HELM_E_INVALID_ARG, "size overflow");
-  if (!s->workspace || s->workspace_bytes < w.total)
-    return fail(HELM_E_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", s->workspace_bytes,
-                s->workspace, w.total);
-  if ((uintptr_t)s->workspace % kAlign)
-    return fail(HELM_E_WORKSPACE, "workspace %p is not %zu-byte aligned", s->workspace, kAlign);
-  for (const auto& in : ins)
-    if (overlaps(s->workspace, (int64_t)w.total, in.p, in.n))
-      return fail(HELM_E_ALIAS, "workspace overlaps %s", in.name);
-  if (overlaps(s->workspace, (int64_t)w.total, out_k, out_b) || overlaps(s->workspace, (int64_t)w.total, out_v, out_b))
-    return fail(HELM_E_ALIAS, "workspace overlaps an output");
+  char* ws = (char*)(uintptr_t)kAlign;   // stands for any aligned workspace (path query)
+  if (need_workspace) {
+    if (!s->workspace || s->workspace_bytes < w.total)
+      return fail(HELM_E_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", s->workspace_bytes,
+                  s->workspace, w.total);
+    if ((uintptr_t)s->workspace % kAlign)
+      return fail(HELM_E_WORKSPACE, "workspace %p is not %zu-byte aligned", s->workspace, kAlign);
+    for (const auto& in : ins)
+      if (overlaps(s->workspace, (int64_t)w.total, in.p, in.n))
+        return fail(HELM_E_ALIAS, "workspace overlaps %s", in.name);
+    if (overlaps(s->workspace, (int64_t)w.total, out_k, out_b) ||
+        overlaps(s->workspace, (int64_t)w.total, out_v, out_b))
+      return fail(HELM_E_ALIAS, "workspace overlaps an output");
+    ws = (char*)s->workspace;
+  }
 
   rc = device_gate(-1);
   if (rc != HELM_OK) return rc;
-  if (s->n_tokens == 0) return HELM_OK;
 
-  char* ws = (char*)s->workspace;
-  helm::XferArgs a{};
+  a = helm::XferArgs{};
   a.src_k = src_k; a.src_v = src_v; a.layer_sel = layer_sel;
   a.W_k = W_k; a.b_k = b_k; a.W_v = W_v; a.b_v = b_v; a.out_k = out_k; a.out_v = out_v;
   a.rope_src = (const float2*)ws;
@@ -373,8 +378,42 @@ int helm_kv_transfer_stage(int stages, const void* src_k, const void* src_v, con
   a.src_tok = s->head_dim; a.src_head = s->n_tokens * s->head_dim; a.src_layer = a.src_head * s->n_kv_heads;
   a.dst_tok = a.src_tok; a.dst_head = a.src_head; a.dst_layer = a.src_layer;
   a.src_rows = a.dst_rows = s->n_tokens;
+  return HELM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int helm_kv_transfer_stage(int stages, const void* src_k, const void* src_v, const int32_t* src_pos,
+                           const int32_t* tgt_pos, const int32_t* layer_sel, const void* W_k,
+                           const float* b_k, const void* W_v, const float* b_v, void* out_k, void* out_v,
+                           const helm_shape_t* s) {
+  clear_error();
+  if (stages < HELM_STAGE_TABLES || stages > HELM_STAGE_ALL)
+    return fail(HELM_E_INVALID_ARG, "stages = %d; expected 1 (tables), 2 (map) or 3 (both)", stages);
+  helm::XferArgs a;
+  const int rc = contiguous_args(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v, s,
+                                 true, a);
+  if (rc != HELM_OK || s->n_tokens == 0) return rc;
   return run_transfer(a, s->dtype, src_pos, tgt_pos, s->rope_theta_src, s->rope_theta_tgt,
                       (hipStream_t)s->stream, stages);
+}
+
+int helm_kv_transfer_path(const void* src_k, const void* src_v, const int32_t* src_pos, const int32_t* tgt_pos,
+                          const int32_t* layer_sel, const void* W_k, const float* b_k, const void* W_v,
+                          const float* b_v, void* out_k, void* out_v, const helm_shape_t* s, int* path_out) {
+  clear_error();
+  if (!path_out) return fail(HELM_E_INVALID_ARG, "path_out is NULL");
+  helm::XferArgs a;
+  const int rc = contiguous_args(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v, s,
+                                 false, a);
+  if (rc != HELM_OK) return rc;
+  if (s->n_tokens == 0) {
+    *path_out = s->dtype == HELM_BF16 && s->head_dim == 128 && s->k <= 4 ? HELM_PATH_MATRIX : HELM_PATH_PORTABLE;
+    return HELM_OK;
+  }
+  *path_out = s->dtype == HELM_BF16 && helm::mfma_supports(a) ? HELM_PATH_MATRIX : HELM_PATH_PORTABLE;
+  return HELM_OK;
 }
 
 int helm_kv_transfer(const void* src_k, const void* src_v, const int32_t* src_pos,

@@ -321,9 +321,37 @@ int helm_ridge_fit_stage(int stages, const void* X, const void* Y, float* W, flo
                          const helm_ridge_shape_t* shape);
 
 /* Workspace bytes the call with this shape needs (0 on an invalid shape;
- * helm_last_error() then says why).  Pure host arithmetic. */
+ * helm_last_error() then says why).  Pure host arithmetic.  The workspace
+ * holds what the transfer derives from the positions — the (cos, sin)
+ * tables of the source and target RoPE angles ("Helm Intelligent Routing",
+ * section "Why carrying the cache across is the hard part": keys are
+ * un-rotated at their source positions and re-rotated at their target
+ * positions) — and, for paged caches, the per-token slot of every block
+ * table entry (knlp "Routing", request-flow figure). */
 size_t helm_kv_workspace_bytes(const helm_shape_t* shape);
 size_t helm_kv_paged_workspace_bytes(const helm_paged_shape_t* shape);
+
+/* Which kernel a helm_kv_transfer call with exactly these arguments would
+ * run, without enqueueing anything (so a caller can see the performance
+ * class of a call before making it).  Same arguments and the same checks as
+ * helm_kv_transfer; on HELM_OK, *path_out is
+ *   HELM_PATH_MATRIX    the matrix-core kernel (bf16, head_dim 128,
+ *                       1 <= k <= 4, every tensor 16-byte aligned, every
+ *                       cache slab and output below 4 GB of addressing);
+ *   HELM_PATH_PORTABLE  the portable fp32 vector-ALU kernel (fp32 storage,
+ *                       head_dim 64, k > 4 or a misaligned view): the same
+ *                       results within tolerance, several times slower.
+ * The paged transfer follows the same rule on its pools.  Does not touch
+ * the device beyond the arch gate; the workspace fields may be zero. */
+#define HELM_PATH_MATRIX 1
+#define HELM_PATH_PORTABLE 2
+int helm_kv_transfer_path(const void* src_k, const void* src_v,
+                          const int32_t* src_pos, const int32_t* tgt_pos,
+                          const int32_t* layer_sel,
+                          const void* W_k, const float* b_k,
+                          const void* W_v, const float* b_v,
+                          void* out_k, void* out_v,
+                          const helm_shape_t* shape, int* path_out);
 
 /* Registration-time check of a mapper ("Helm Intelligent Routing", section
  * "Requirements": an impossible pair is refused with the specific reason
@@ -351,14 +379,23 @@ int helm_device_check(int device);
  * "gfx950:sramecc+:xnack-") names a supported target, else 0. */
 int helm_arch_supported(const char* gcn_arch_name);
 
-/* The calling thread's last error text ("" after success).  Owned by the
- * library; valid until the thread's next call. */
+/* The calling thread's last error text ("" after success): the specific
+ * reason for a refusal, with the offending value ("Helm Intelligent
+ * Routing", section "Requirements": an impossible pair is refused at
+ * registration with the specific reason).  Owned by the library; valid
+ * until the thread's next call. */
 const char* helm_last_error(void);
 
-/* Static name of a status code ("HELM_OK", ...; "unknown" otherwise). */
+/* Static name of a status code ("HELM_OK", ...; "unknown" otherwise), so a
+ * caller can log the typed refusal it falls back on ("Helm Intelligent
+ * Routing", section "What happens when a transfer cannot be used"). */
 const char* helm_status_string(int status);
 
-/* HELM_ABI_VERSION of the built library. */
+/* HELM_ABI_VERSION of the built library: a caller that registers mappers
+ * against this header can check at load time that the library it found
+ * takes the same structures ("Helm Intelligent Routing", section
+ * "Requirements": an incompatible pairing is refused up front rather than
+ * failing later). */
 int helm_abi_version(void);
 
 #ifdef __cplusplus

@@ -39,10 +39,12 @@ pure-Python brute force.  No function is "parity unpinned".
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 
 import numpy as np
+import scipy.linalg
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhelm_oracle.so")
@@ -394,20 +396,25 @@ def ridge_fit(x, y, lam: float = 0.01, dtype: int = BF16):
     """The ridge fit of the per-(target layer, head, K|V) maps, fp64 (the
     Qwen3 cache-mapping write-up, section "A linear bridge, strangely enough,
     suffices": each target head's key map and value map are fitted
-    separately by ridge regression with centred data and lambda = 0.01).
+    separately by ridge regression, lambda = 0.01, with an unpenalised bias).
 
     x: [G, N, IN] observations of the map's input per group (bf16 storage as
-    uint16, or float); y: [G, N, D] the targets.  For every group g, with the
-    column means mx = mean_n x[g], my = mean_n y[g] and the centred data
-    xc = x[g] - mx, yc = y[g] - my, the map W[g] [IN, D] solves
-        (xc^T xc + lam * I) W = xc^T yc
-    and the bias is b[g] = my - mx @ W (so x @ W + b reproduces y's mean).
-    Returns (W [G, IN, D], b [G, D]) in fp64.  The products are numpy
-    matmuls and the solve is LAPACK's (numpy.linalg.solve), in fp64."""
+    uint16, or float); y: [G, N, D] the targets.  For every group g the fit
+    is the minimiser of the ridge objective
+        |x[g] W + 1 b - y[g]|^2 + lam |W|^2        (b not penalised),
+    written as one ordinary least-squares problem on the augmented system
+        [ x[g]          1 ] [W]   [ y[g] ]
+        [ sqrt(lam) I   0 ] [b] = [  0   ]
+    and solved by LAPACK's SVD-based least squares (gelsd, through
+    scipy.linalg.lstsq) in fp64.  (The write-up's listing reaches the same minimiser by centring x
+    and y and solving the normal equations; the pins check the two agree.)
+    Returns (W [G, IN, D], b [G, D]) in fp64."""
     X = _decode(x, dtype)
     Y = _decode(y, dtype)
     if X.ndim != 3 or Y.ndim != 3 or X.shape[:2] != Y.shape[:2]:
         raise ValueError("x [G, N, IN] and y [G, N, D] must share G and N")
+    if lam < 0:
+        raise ValueError("lambda must be >= 0")
     G, N, IN = X.shape
     D = Y.shape[2]
     if N < 1:
@@ -415,12 +422,14 @@ def ridge_fit(x, y, lam: float = 0.01, dtype: int = BF16):
     W = np.empty((G, IN, D))
     b = np.empty((G, D))
     for g in range(G):
-        mx = X[g].sum(axis=0) / N
-        my = Y[g].sum(axis=0) / N
-        xc = X[g] - mx
-        yc = Y[g] - my
-        normal = xc.T @ xc
-        normal[np.diag_indices(IN)] += lam
-        W[g] = np.linalg.solve(normal, xc.T @ yc)
-        b[g] = my - mx @ W[g]
+        A = np.zeros((N + IN, IN + 1), order="F")
+        A[:N, :IN] = X[g]
+        A[:N, IN] = 1.0
+        A[N:, :IN] = math.sqrt(lam) * np.eye(IN)
+        rhs = np.zeros((N + IN, D), order="F")
+        rhs[:N] = Y[g]
+        sol = scipy.linalg.lstsq(A, rhs, lapack_driver="gelsd", overwrite_a=True, overwrite_b=True,
+                                 check_finite=False)[0]
+        W[g] = sol[:IN]
+        b[g] = sol[IN]
     return W, b

@@ -301,10 +301,14 @@ def ridge_inputs(n_groups: int, n_obs: int, in_features: int, out_features: int,
         m = torch.randn((n_groups, 1, F), generator=g, device=device)
         sc = torch.exp(0.5 * torch.randn((n_groups, 1, F), generator=g, device=device))
         t = torch.empty((n_groups, n_obs, F), dtype=torch.bfloat16, device=device)
-        step = max(1, (1 << 30) // max(1, n_obs * F * 4))     # about 1 GiB of fp32 per draw
+        # about 4 GiB of fp32 per draw, transformed in place and rounded once
+        # on the copy into t: four kernel launches per draw
+        step = max(1, (4 << 30) // max(1, n_obs * F * 4))
         for i in range(0, n_groups, step):
             j = min(n_groups, i + step)
             z = torch.randn((j - i, n_obs, F), generator=g, device=device)
-            t[i:j] = ((z + m[i:j]) * sc[i:j]).to(torch.bfloat16)
+            z.add_(m[i:j]).mul_(sc[i:j])
+            t[i:j].copy_(z)
+            del z
         out.append(t)
     return out[0], out[1]

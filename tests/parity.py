@@ -92,22 +92,30 @@ class Case:
                             d["b_k"], d["W_v"], d["b_v"], out[0], out[1], s)
         return out
 
-    def oracle_rows(self, rows=None):
+    def oracle_rows(self, rows=None, quantize_content=True):
         h = self.host
-        return oracle.transfer_rows(self.problem(), h["src_k"], h["src_v"], h["src_pos"], h["tgt_pos"],
+        pb = self.problem()
+        pb.quantize_content = quantize_content
+        return oracle.transfer_rows(pb, h["src_k"], h["src_v"], h["src_pos"], h["tgt_pos"],
                                     h["layer_sel"], h["W_k"], h["b_k"], h["W_v"], h["b_v"], rows=rows)
 
 
-def sample_rows(L_t: int, H: int, T: int, per_slab: int, seed: int) -> np.ndarray:
+def sample_rows(L_t: int, H: int, T: int, per_slab: int, seed: int, tile: int = 0) -> np.ndarray:
     """Flat rows (l*H + h)*T + t: per (l, h) slab the first and last token,
-    tile edges, and random tokens."""
+    tile edges, `per_slab` random tokens on top of those, and, when `tile` is
+    set, one random token inside every `tile`-token window [i*tile, (i+1)*tile)
+    so that every tile of a launch's schedule is compared in every slab."""
     rng = np.random.default_rng(seed)
-    fixed = sorted({0, T - 1, min(T - 1, 15), min(T - 1, 16), min(T - 1, 63), min(T - 1, 64), T // 2})
+    fixed = np.array(sorted({0, T - 1, min(T - 1, 15), min(T - 1, 16), min(T - 1, 63), min(T - 1, 64), T // 2}))
+    n_tiles = (T + tile - 1) // tile if tile else 0
+    starts = np.arange(n_tiles, dtype=np.int64) * tile if tile else None
     out = []
     for g in range(L_t * H):
-        extra = rng.integers(0, T, max(0, per_slab - len(fixed)))
-        toks = np.unique(np.concatenate([fixed, extra]))
-        out.append(g * T + toks)
+        parts = [fixed, rng.integers(0, T, per_slab)]
+        if tile:
+            span = np.minimum(starts + tile, T) - starts
+            parts.append(starts + (rng.random(n_tiles) * span).astype(np.int64))
+        out.append(g * T + np.unique(np.concatenate(parts)))
     return np.concatenate(out).astype(np.int64)
 
 
@@ -152,8 +160,11 @@ def compare(gpu: np.ndarray, ref: np.ndarray, slab_of_row: np.ndarray, dtype: st
     return summary
 
 
-def check_case(case: Case, out_k: torch.Tensor, out_v: torch.Tensor, rows=None, label=""):
-    """Compares the library's outputs with the oracle on `rows` (all when None)."""
+def check_case(case: Case, out_k: torch.Tensor, out_v: torch.Tensor, rows=None, label="", exact=False):
+    """Compares the library's outputs with the oracle on `rows` (all when None).
+    With `exact`, also reports (never gates) the same outputs against the
+    oracle without the bf16 operand rounding (EXACT mode): what the mandated
+    bf16 contraction costs against the unrounded definition."""
     w = case.w
     D = w.head_dim
     if rows is None:
@@ -168,4 +179,29 @@ def check_case(case: Case, out_k: torch.Tensor, out_v: torch.Tensor, rows=None, 
         slab = rows // case.T
     sk = compare(g_k, ref_k, slab, w.dtype, f"{label}{w.name} K")
     sv = compare(g_v, ref_v, slab, w.dtype, f"{label}{w.name} V")
+    if exact:
+        ex_k, ex_v = case.oracle_rows(rows, quantize_content=False)
+        sk["exact"] = exact_report(g_k, ex_k.reshape(-1, D), slab, f"{label}{w.name} K")
+        sv["exact"] = exact_report(g_v, ex_v.reshape(-1, D), slab, f"{label}{w.name} V")
     return sk, sv
+
+
+def exact_report(gpu: np.ndarray, ref: np.ndarray, slab_of_row: np.ndarray, name: str) -> dict:
+    """EXACT-mode statistics (reported, not gated): per slab max |gpu - ref| /
+    rms(ref), the excess over half an output ulp / rms, and the cosine; the
+    worst over slabs, plus the overall rms error / rms."""
+    worst_err = worst_excess = 0.0
+    min_cos = 1.0
+    sq_err = sq_ref = 0.0
+    for s in np.unique(slab_of_row):
+        g, r = gpu[slab_of_row == s].ravel(), ref[slab_of_row == s].ravel()
+        st = slab_stats(g, r, "bf16")
+        worst_err = max(worst_err, st["max_err_rel"])
+        worst_excess = max(worst_excess, st["max_excess_rel"])
+        min_cos = min(min_cos, st["cos"])
+        sq_err += float(np.sum((g - r) ** 2))
+        sq_ref += float(np.sum(r * r))
+    rep = dict(max_err_rel=worst_err, max_excess_rel=worst_excess, min_cos=min_cos,
+               rms_err_rel=math.sqrt(sq_err / max(sq_ref, 1e-300)))
+    log(f"{name} EXACT mode (reported, not gated): {rep}")
+    return rep

@@ -116,6 +116,26 @@ def test_workspace_checks():
     assert "aligned" in hk.helm_last_error()
 
 
+def test_path_query_checks_like_the_transfer():
+    """helm_kv_transfer_path runs the transfer's checks (same statuses) and
+    needs no workspace; with every argument valid it stops only at the
+    device gate (no GPU here) or reports a path."""
+    s = shape(n_tokens=16, n_src_layers=2, n_tgt_layers=2, k=1, n_kv_heads=1)
+    ptrs = [ctypes.c_void_p(0x10000000 + 0x1000000 * i) for i in range(11)]
+    path = ctypes.c_int(0)
+    assert hk.lib().helm_kv_transfer_path(*ptrs, ctypes.byref(s), None) == 1
+    assert "path_out" in hk.helm_last_error()
+    bad = list(ptrs)
+    bad[9] = bad[0]
+    assert hk.lib().helm_kv_transfer_path(*bad, ctypes.byref(s), ctypes.byref(path)) == 8
+    assert hk.lib().helm_kv_transfer_path(*ptrs, ctypes.byref(shape(head_dim=96)), ctypes.byref(path)) == 2
+    rc = hk.lib().helm_kv_transfer_path(*ptrs, ctypes.byref(s), ctypes.byref(path))
+    if _gpu_present():
+        assert rc == 0 and path.value in (hk.HELM_PATH_MATRIX, hk.HELM_PATH_PORTABLE)
+    else:
+        assert rc == 4 and path.value == 0
+
+
 def test_mapper_check():
     s = shape(n_src_layers=5, n_tgt_layers=3, k=2)
     good = np.array([[0, 4], [3, 3], [1, 2]], np.int32)

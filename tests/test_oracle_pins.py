@@ -233,6 +233,32 @@ def test_shift_is_textbook_rope_shift(oracle_mod):
             np.testing.assert_array_equal(ov[l], case["src_v"][s].astype(np.float64))
 
 
+@pytest.mark.parametrize("quantize,dtype", [(False, F32), (True, BF16)])
+def test_transfer_relative_position_shift(oracle_mod, quantize, dtype):
+    """P3 applied to the transfer itself, with a random map and bias: moving
+    every target position by d rotates each key output by R(d) (complex
+    form) and leaves the values unchanged, so q.k between the transferred
+    keys and any query moved by the same d is unchanged.  Links the 32K-token
+    workload at tgt_pos = src_pos with the long-context one at src_pos + 4096.
+    Catches re-rotation at source positions, a bias added after the rotation,
+    a map applied after the re-rotation."""
+    L_s, L_t, H, D, T, k = 5, 3, 2, 16, 11, 3
+    rng = np.random.default_rng(31)
+    case = random_case(rng, L_s, L_t, H, D, T, k, dtype=dtype)
+    src = rng.integers(-5000, 5000, T).astype(np.int32)
+    tgt = rng.integers(0, 100000, T).astype(np.int32)
+    k0, v0 = run(oracle_mod, L_s, L_t, H, D, T, k, case, src, tgt, 1e6, 1e6, dtype=dtype, quantize=quantize)
+    for d in [1, 4096, -777]:
+        k1, v1 = run(oracle_mod, L_s, L_t, H, D, T, k, case, src, tgt + d, 1e6, 1e6, dtype=dtype, quantize=quantize)
+        np.testing.assert_allclose(k1, rope_complex(k0, d, 1e6), rtol=0, atol=1e-11)
+        np.testing.assert_array_equal(v1, v0)
+        q = rng.standard_normal(D)
+        for t in range(T):
+            a = rope_complex(q, int(tgt[t]) + 50, 1e6) @ k0[0, 0, t]
+            b = rope_complex(q, int(tgt[t]) + 50 + d, 1e6) @ k1[0, 0, t]
+            assert b == pytest.approx(a, rel=1e-9, abs=1e-9)
+
+
 def test_selector_pins_concatenation_order(oracle_mod):
     """P6: W = selector of row block j -> output is layer layer_sel[l, j]
     (in the order of the layer_sel row as given), re-rotated by the offset."""
@@ -692,6 +718,41 @@ def test_ridge_recovers_planted_map_and_bias(oracle_mod):
     assert W.shape == (3, 7, 5) and b.shape == (3, 5)
     np.testing.assert_allclose(W, Wt, rtol=0, atol=1e-9)
     np.testing.assert_allclose(b, bt, rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("lam", [0.01, 3.0])
+def test_ridge_equals_the_centred_closed_form(oracle_mod, lam):
+    """The write-up's own route to the fit (centre x and y, add lambda on the
+    diagonal of xc^T xc, solve for W, b = mean(y) - mean(x) W), written out
+    here with numpy's solve, gives the oracle's minimiser of the augmented
+    least-squares problem."""
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((2, 250, 9)) * np.linspace(0.3, 3, 9) + 4.0
+    Y = rng.standard_normal((2, 250, 5)) + X[:, :, :5] * 0.2
+    W, b = oracle_mod.ridge_fit(X, Y, lam=lam, dtype=F32)
+    for g in range(2):
+        mx, my = X[g].mean(axis=0), Y[g].mean(axis=0)
+        xc, yc = X[g] - mx, Y[g] - my
+        Wc = np.linalg.solve(xc.T @ xc + lam * np.eye(9), xc.T @ yc)
+        np.testing.assert_allclose(W[g], Wc, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(b[g], my - mx @ Wc, rtol=0, atol=1e-10)
+
+
+def test_ridge_rank_deficient_with_penalty(oracle_mod):
+    """N <= IN (fewer observations than inputs, as in the short GPU cases):
+    lambda > 0 makes the minimiser unique; it matches the closed form
+    W = xc^T (xc xc^T + lambda I)^-1 yc (the push-through identity, an N x N
+    solve) and b = mean(y) - mean(x) W."""
+    rng = np.random.default_rng(22)
+    X = rng.standard_normal((1, 6, 10)) + 1.0
+    Y = rng.standard_normal((1, 6, 3))
+    lam = 0.01
+    W, b = oracle_mod.ridge_fit(X, Y, lam=lam, dtype=F32)
+    mx, my = X[0].mean(axis=0), Y[0].mean(axis=0)
+    xc, yc = X[0] - mx, Y[0] - my
+    Wp = xc.T @ np.linalg.solve(xc @ xc.T + lam * np.eye(6), yc)
+    np.testing.assert_allclose(W[0], Wp, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(b[0], my - mx @ Wp, rtol=0, atol=1e-9)
 
 
 def test_ridge_zero_lambda_is_least_squares_with_intercept(oracle_mod):
