@@ -31,7 +31,7 @@ EXPORTED = ("helm_kv_transfer", "helm_kv_transfer_stage", "helm_kv_transfer_path
             "helm_ridge_fit", "helm_ridge_fit_stage", "helm_ridge_workspace_bytes", "helm_kv_workspace_bytes",
             "helm_kv_paged_workspace_bytes", "helm_mapper_check", "helm_paged_check",
             "helm_device_check", "helm_arch_supported", "helm_last_error", "helm_status_string",
-            "helm_abi_version")
+            "helm_abi_version", "helm_kv_transfer_noalloc", "helm_kv_noalloc_max_bytes")
 
 
 class HelmError(RuntimeError):
@@ -95,6 +95,10 @@ def lib() -> ctypes.CDLL:
         L.helm_kv_transfer_stage.restype = ctypes.c_int
         L.helm_kv_transfer_path.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape), ctypes.POINTER(ctypes.c_int)]
         L.helm_kv_transfer_path.restype = ctypes.c_int
+        L.helm_kv_transfer_noalloc.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
+        L.helm_kv_transfer_noalloc.restype = ctypes.c_int
+        L.helm_kv_noalloc_max_bytes.argtypes = []
+        L.helm_kv_noalloc_max_bytes.restype = ctypes.c_size_t
         L.helm_kv_transfer_wide.restype = ctypes.c_int
         L.helm_kv_transfer_wide.argtypes = [vp] * 11 + [ctypes.POINTER(HelmShape)]
         L.helm_ridge_workspace_bytes.restype = ctypes.c_size_t
@@ -317,6 +321,21 @@ def helm_kv_transfer_stage(stages: int, src_k, src_v, src_pos, tgt_pos, layer_se
         workspace = _own_workspace(helm_kv_workspace_bytes(s), src_k.device, s.stream)
     s.workspace, s.workspace_bytes = _workspace_ptr(workspace, src_k.device)
     _raise(lib().helm_kv_transfer_stage(int(stages), *ptrs, ctypes.byref(s)))
+
+
+def helm_kv_transfer_noalloc(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v,
+                             shape: HelmShape) -> None:
+    """helm_kv_transfer without a workspace: the tables go to the library's
+    static per-GPU scratch (helm_kv_noalloc_max_bytes(); up to 65,536 tokens
+    at head_dim 128).  Nothing is allocated, here or in the library.  Calls
+    that overlap on one GPU share that scratch and race."""
+    ptrs = _transfer_ptrs(shape, src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v)
+    s = _call_shape(shape, src_k.device)
+    _raise(lib().helm_kv_transfer_noalloc(*ptrs, ctypes.byref(s)))
+
+
+def helm_kv_noalloc_max_bytes() -> int:
+    return int(lib().helm_kv_noalloc_max_bytes())
 
 
 def helm_kv_transfer_path(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v,

@@ -399,6 +399,72 @@ int helm_kv_transfer_stage(int stages, const void* src_k, const void* src_v, con
                       (hipStream_t)s->stream, stages);
 }
 
+}  // extern "C"
+
+namespace {
+// ---- allocation-free variant --------------------------------------------
+// The transfer's one scratch buffer is its pair of RoPE (cos, sin) tables.
+// For callers that cannot allocate, they live in this file-scope device
+// array: one copy per GPU the library runs on, held until the process ends.
+// 64 MiB holds the tables of 65,536 tokens at head_dim 128 (131,072 at 64).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (host code never passes the array's own name: on the
+// host it only stands for the symbol, not a device address).
+std::atomic<uintptr_t> g_scratch_addr[kMaxDevices];
+
+int scratch_of_current_device(char** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HELM_E_NO_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HELM_E_INVALID_ARG, "device %d is beyond the %d devices the static scratch is kept for", dev,
+                kMaxDevices);
+  uintptr_t p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == 0) {
+    void* addr = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || addr == nullptr)
+      return fail(HELM_E_LAUNCH, "hipGetSymbolAddress of the static scratch failed: %s", hipGetErrorString(r));
+    p = (uintptr_t)addr;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = (char*)p;
+  return HELM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t helm_kv_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int helm_kv_transfer_noalloc(const void* src_k, const void* src_v, const int32_t* src_pos, const int32_t* tgt_pos,
+                             const int32_t* layer_sel, const void* W_k, const float* b_k, const void* W_v,
+                             const float* b_v, void* out_k, void* out_v, const helm_shape_t* s) {
+  clear_error();
+  helm::XferArgs a;
+  int rc = contiguous_args(src_k, src_v, src_pos, tgt_pos, layer_sel, W_k, b_k, W_v, b_v, out_k, out_v, s, false,
+                           a);
+  if (rc != HELM_OK || s->n_tokens == 0) return rc;
+  Workspace w;
+  if (!workspace_layout(s->n_tokens, s->head_dim, false, w)) return fail(HELM_E_INVALID_ARG, "size overflow");
+  if (w.total > kScratchBytes)
+    return fail(HELM_E_WORKSPACE,
+                "n_tokens = %lld needs %zu bytes of tables; the static scratch holds %zu (up to %lld tokens at "
+                "head_dim %d)",
+                (long long)s->n_tokens, w.total, kScratchBytes,
+                (long long)(kScratchBytes / (2 * (size_t)s->head_dim / 2 * sizeof(float2))), s->head_dim);
+  char* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != HELM_OK) return rc;
+  a.rope_src = (const float2*)ws;
+  a.rope_tgt = (const float2*)(ws + w.rope_bytes);
+  return run_transfer(a, s->dtype, src_pos, tgt_pos, s->rope_theta_src, s->rope_theta_tgt, (hipStream_t)s->stream,
+                      HELM_STAGE_ALL);
+}
+
 int helm_kv_transfer_path(const void* src_k, const void* src_v, const int32_t* src_pos, const int32_t* tgt_pos,
                           const int32_t* layer_sel, const void* W_k, const float* b_k, const void* W_v,
                           const float* b_v, void* out_k, void* out_v, const helm_shape_t* s, int* path_out) {

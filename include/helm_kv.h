@@ -182,6 +182,28 @@ int helm_kv_transfer_stage(int stages,
                            void* out_k, void* out_v,
                            const helm_shape_t* shape);
 
+/* helm_kv_transfer for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, checks and results as helm_kv_transfer
+ * (bit-identical outputs); shape->workspace and workspace_bytes are ignored:
+ * the RoPE tables go to a static device buffer of
+ * helm_kv_noalloc_max_bytes() bytes (64 MiB) that the library holds on each
+ * GPU it runs on until the process ends.  Nothing is allocated or freed.
+ * Limit: n_tokens <= 65,536 at head_dim 128 (131,072 at 64); larger calls
+ * return HELM_E_WORKSPACE with nothing enqueued.  Every call on one GPU
+ * shares that GPU's buffer: calls that overlap on one GPU (other streams,
+ * other host threads) race and must be ordered by the caller; calls in
+ * stream order on one stream are safe.  The buffer needs no clearing (each
+ * call writes the tables it reads). */
+size_t helm_kv_noalloc_max_bytes(void);
+int helm_kv_transfer_noalloc(const void* src_k, const void* src_v,
+                             const int32_t* src_pos, const int32_t* tgt_pos,
+                             const int32_t* layer_sel,
+                             const void* W_k, const float* b_k,
+                             const void* W_v, const float* b_v,
+                             void* out_k, void* out_v,
+                             const helm_shape_t* shape);
+
 /* The same transfer on paged caches driven by block tables (knlp "Routing"
  * page, request-flow figure: the selection is applied to the block table and
  * only the selected blocks are written into the paged cache; "Helm
