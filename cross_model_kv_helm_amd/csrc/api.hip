@@ -83,7 +83,7 @@ Common common_of(const helm_paged_shape_t* s) {
 
 size_t elem_bytes(int32_t dtype) { return dtype == HELM_BF16 ? 2 : 4; }
 
-// Workspace: [rope_src: ceil(N/32)*32*D/2 float2][rope_tgt: same]{[src_row: N int32][dst_row: N int32]}
+// Workspace: [rope_src: ceil(N/16)*16*D/2 float2][rope_tgt: same]{[src_row: N int32][dst_row: N int32]}
 struct Workspace {
   size_t rope_bytes = 0, rows_bytes = 0, total = 0;
 };

@@ -23,8 +23,8 @@ struct XferArgs {
   const float* b_v;
   void* out_k;
   void* out_v;
-  const float2* rope_src;     // (cos, sin) at src_pos, theta_src, in rope_index layout
-  const float2* rope_tgt;     // (cos, sin) at tgt_pos, theta_tgt, in rope_index layout
+  const float2* rope_src;     // (cos, sin) at src_pos, theta_src, in rope_src_index layout
+  const float2* rope_tgt;     // (cos, sin) at tgt_pos, theta_tgt, in rope_tgt_index layout
   const int32_t* src_row;     // [n_tok] or nullptr (identity)
   const int32_t* dst_row;     // [n_tok] or nullptr (identity)
   int64_t n_tok;
@@ -36,18 +36,28 @@ struct XferArgs {
 
 enum class Dtype : int { BF16 = 0, F32 = 1 };
 
-// Layout of the (cos, sin) tables written by K1, blocked by 32-token tiles so
-// that a wave's 16-byte loads of a tile's table are contiguous: within the
-// block of tokens [32b, 32b+32), the pair of (token t, frequency i) lives at
-//   float2 index  b*32*half + e*(32*half/4) + (t%32)*(half/8)*2 + (i/8)*2 + (i%2)
-// with e = (i%8)/2, i.e. [e][t%32][i/8][2 pairs].  half = D/2 (a multiple of 8).
-constexpr int kRopeBlock = 32;
-__host__ __device__ inline int64_t rope_index(int64_t t, int32_t i, int32_t half) {
+// Layouts of the (cos, sin) tables written by K1, blocked by 16-token tiles
+// (the matrix-core kernel's token tile) and different for the two sides, so
+// that each side's readers make contiguous 16-byte accesses.  half = D/2 (a
+// multiple of 8); within the block of tokens [16b, 16b+16), with tt = t%16,
+// pair i of token t lives at float2 index b*16*half + ...:
+//   source table (read by the gather/un-rotation: one 16-byte piece of pairs
+//   (8c + 2e, 8c + 2e + 1) per lane):  e*4*half + tt*(half/4) + (i/8)*2 + i%2,
+//   with e = (i%8)/2, i.e. [e][tt][i/8][2 pairs];
+//   target table (read by the epilogue: pairs 4g .. 4g+3 of a token as two
+//   16-byte halves):  (i/4)*64 + ((i%4)/2)*32 + tt*2 + i%2,
+//   i.e. [i/4][(i%4)/2][tt][2 pairs].
+constexpr int kRopeBlock = 16;
+__host__ __device__ inline int64_t rope_src_index(int64_t t, int32_t i, int32_t half) {
   const int64_t b = t / kRopeBlock;
   const int32_t tt = (int32_t)(t - b * kRopeBlock);
-  const int32_t e = (i & 7) >> 1;
-  return b * kRopeBlock * half + (int64_t)e * (kRopeBlock * half / 4) + (int64_t)tt * (half / 4) +
-         (i >> 3) * 2 + (i & 1);
+  return b * kRopeBlock * half + (int64_t)((i & 7) >> 1) * (4 * half) + (int64_t)tt * (half / 4) + (i >> 3) * 2 +
+         (i & 1);
+}
+__host__ __device__ inline int64_t rope_tgt_index(int64_t t, int32_t i, int32_t half) {
+  const int64_t b = t / kRopeBlock;
+  const int32_t tt = (int32_t)(t - b * kRopeBlock);
+  return b * kRopeBlock * half + (int64_t)(i >> 2) * 64 + ((i & 3) >> 1) * 32 + tt * 2 + (i & 1);
 }
 inline int64_t rope_table_entries(int64_t n_tok, int32_t half) {
   return (n_tok + kRopeBlock - 1) / kRopeBlock * kRopeBlock * half;
@@ -89,7 +99,7 @@ struct WideXfer {
   const float* b_v;
   void* out_k;                // [L_t, H, T, D]
   void* out_v;
-  const float2* rope_src;     // K1 tables (rope_index layout)
+  const float2* rope_src;     // K1 tables (rope_src_index / rope_tgt_index layouts)
   const float2* rope_tgt;
   uint16_t* U;
   uint16_t* WT_k;

@@ -1,7 +1,8 @@
 // rope_tables.hip — per-token prologue kernels.
 //
 // K1 writes the cos/sin of every RoPE angle the transfer needs, once per
-// token (in the tile-blocked layout of rope_index), so the transfer kernels never evaluate trigonometry: the angle of
+// token (in the tile-blocked layouts rope_src_index / rope_tgt_index), so the
+// transfer kernels never evaluate trigonometry: the angle of
 // pair i at position p is p * theta^(-2i/D) (rotate-half RoPE), formed in
 // fp64 because at p ~ 1.3e5 an fp32 product alone would be off by ~1e-2 rad;
 // cos and sin are evaluated in fp64 and rounded once to fp32.  The pages use
@@ -34,12 +35,11 @@ rope_tables_kernel(const int32_t* __restrict__ src_pos, const int32_t* __restric
     const double ex = inv_d * (double)i;
     const double w_s = pow(theta_src, ex);
     const double w_t = pow(theta_tgt, ex);
-    const int64_t at = rope_index(t, i, half);
     double s, c;
     sincos((double)src_pos[t] * w_s, &s, &c);
-    rope_src[at] = make_float2((float)c, (float)s);
+    rope_src[rope_src_index(t, i, half)] = make_float2((float)c, (float)s);
     sincos((double)tgt_pos[t] * w_t, &s, &c);
-    rope_tgt[at] = make_float2((float)c, (float)s);
+    rope_tgt[rope_tgt_index(t, i, half)] = make_float2((float)c, (float)s);
   }
 }
 

@@ -62,7 +62,7 @@ transfer_generic_kernel(XferArgs a, int32_t tile) {
         const int64_t base = (int64_t)sel[j] * a.src_layer + (int64_t)h * a.src_head + row * a.src_tok;
         if (is_k) {
           const int32_t i = d < half ? d : d - half;
-          const float2 cs = a.rope_src[rope_index(n, i, half)];
+          const float2 cs = a.rope_src[rope_src_index(n, i, half)];
           const float lo = load_as_f32(src, base + i), hi = load_as_f32(src, base + i + half);
           // R(-p): (lo, hi) -> (lo c + hi s, hi c - lo s)
           x = d < half ? fmaf(lo, cs.x, hi * cs.y) : fmaf(hi, cs.x, -(lo * cs.y));
@@ -93,7 +93,7 @@ transfer_generic_kernel(XferArgs a, int32_t tile) {
     }
     float o_lo = y_lo, o_hi = y_hi;
     if (is_k) {  // R(+p'): (lo, hi) -> (lo c - hi s, hi c + lo s)
-      const float2 cs = a.rope_tgt[rope_index(n, i, half)];
+      const float2 cs = a.rope_tgt[rope_tgt_index(n, i, half)];
       o_lo = fmaf(y_lo, cs.x, -(y_hi * cs.y));
       o_hi = fmaf(y_hi, cs.x, y_lo * cs.y);
     }

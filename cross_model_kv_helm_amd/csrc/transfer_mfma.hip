@@ -1,63 +1,67 @@
 // transfer_mfma.hip — matrix-core transfer kernel for bf16 storage (gfx950).
 //
-// What it computes is the whole transfer for one (target layer l, head h,
-// K|V) group over a range of tokens (pages: "Helm Intelligent Routing",
-// section "Why carrying the cache across is the hard part"; the Qwen3
-// cache-mapping write-up, section "A linear bridge, strangely enough,
+// What it computes is the whole transfer for two target layers l0, l1 of one
+// head h, keys or values, over a range of tokens (pages: "Helm Intelligent
+// Routing", section "Why carrying the cache across is the hard part"; the
+// Qwen3 cache-mapping write-up, section "A linear bridge, strangely enough,
 // suffices"):
-//   prologue  gather the k selected source layers' rows of head h and, for
-//             keys, un-rotate them at src_pos (R(-p)), rounding the content
-//             key once to bf16 — the operand type of the map;
+//   gather    the k selected source layers' rows of head h and, for keys,
+//             un-rotate them at src_pos (R(-p)), rounding the content key
+//             once to bf16 — the operand type of the map;
 //   product   Y = X W on the matrix cores, bf16 x bf16 -> fp32
-//             (v_mfma_f32_32x32x16_bf16), computed as Y^T = W^T X^T so that
-//             a lane's accumulators hold 4 consecutive output columns;
-//   epilogue  + b, then for keys the forward rotation R(+p') at tgt_pos —
-//             always applied — and a nearest-even store to bf16.
+//             (v_mfma_f32_16x16x32_bf16), computed as Y^T = W^T X^T;
+//   epilogue  + b (the accumulators start at the bias), then for keys the
+//             forward rotation R(+p') at tgt_pos — always applied — and a
+//             nearest-even store to bf16.
 //
 // Design for MI355X:
-//   * Matrix instruction v_mfma_f32_32x32x16_bf16.  A matrix wave owns one
-//     32-row block of Y^T: rows 0..15 are output columns 16q..16q+15 and rows
-//     16..31 are columns 64+16q..64+16q+15 (q = wave within its role).  In the
-//     32x32 accumulator layout rows r and r+16 live in the same lane, so the
-//     RoPE partners n and n+64 meet in one lane and the rotation needs no
-//     exchange.  W stays in registers (128 VGPRs per wave for k = 4) for the
-//     whole token sweep of an item.
-//   * Two roles per CU, one wave of each on every SIMD: four matrix waves
-//     (products, epilogue, target-table copies, output stores) and four data
-//     waves (source-row loads, un-rotation into LDS).  One LDS barrier ends
-//     each 32-token phase; the matrix pipe of one wave overlaps the vector ALU
-//     and memory work of the other.
-//   * Register prefetch.  The data waves load the source rows of a tile two
-//     phases ahead, layer by layer between the un-rotation arithmetic.
-//   * Keys and values are separate launches: values have no rotation, so
-//     their items issue no table loads or copies.
-//   * No hidden waits.  gfx9 counts outstanding global loads and stores in
-//     one in-order counter, so a wait for any one result also waits for
-//     everything issued before it.  Every global access of the tile loop is
-//     therefore issued unconditionally (tokens outside the range get a byte
-//     offset beyond the descriptor, which the hardware turns into a zero
-//     load or a dropped store), and the paged row maps are loaded one phase
-//     before they are used: the only waits left are for data that has had a
-//     whole phase to arrive.
-//   * Persistent sweep over tokens.  Work items are (token chunk, target
-//     layer, head); a workgroup maps all tokens of its item, so W is read
-//     from HBM once per item.
-//   * XCD-aware order.  Workgroups are dispatched round-robin over the 8
-//     XCDs (id mod 8); with the head as the fastest-varying coordinate of the
-//     item index and 8 heads, every workgroup of an XCD works on the same
-//     head, so the ~3 target layers that select a source row read it from
-//     that XCD's L2 at about the same time.
-//   * Stores through LDS: the epilogue writes its 32x32 block into an LDS
-//     output tile; two phases later each wave stores whole 256-byte token
-//     rows (16 bytes per lane), so every store touches full cache lines.  The
-//     tile's (cos, sin) tables use a tile-blocked layout for the same reason:
-//     each 16-byte load of a wave is contiguous.
-//   * Buffer descriptors.  Source rows, cos/sin tables and output rows are
-//     addressed through 128-bit buffer descriptors whose bases are uniform
-//     (per layer and head) and live in scalar registers; a lane carries one
-//     32-bit byte offset.  The descriptors' record counts also make the
-//     hardware drop any access outside the tensor.
+//   * Two target layers per workgroup ("slots").  With 64 target layers x 8
+//     heads there are 512 (layer, head) maps per launch; two per workgroup
+//     puts all of them on the 256 CUs at once, so every source row is
+//     fetched from HBM by one token sweep (one map per workgroup needs two
+//     sweeps, reading the selected source layers twice), and the target
+//     RoPE tables of a tile serve both slots.  Work items are (token chunk,
+//     layer pair, head) with the head fastest: workgroups go to the 8 XCDs
+//     round robin, so with 8 heads each XCD maps one head's 64 target layers
+//     and its L2 holds that head's source rows for all of them.
+//   * One wave per SIMD, each holding W for 64 output columns of one slot
+//     (256 registers at k = 4): columns 32c .. 32c+31 and their RoPE
+//     partners 64+32c .. 64+32c+31 (c = the wave's half), as four 16-row
+//     blocks of Y^T whose rows n and n+64 sit in the same lane and register,
+//     so the rotation needs no exchange.  Every 16x16x32 product takes A
+//     from registers and B (32 features x 16 tokens) from the LDS
+//     activation tile, one read for four products.  The tile is read by two
+//     waves per slot instead of four: LDS traffic, not the matrix pipe, is
+//     what bounds a design with W for 32 columns per wave.
+//   * Every wave also gathers: per 16-token tile, lane (token, 16-byte chunk
+//     c, pair lane r) loads chunk c of the low half and its partner chunk of
+//     the high half from k of the 2k (slot, layer) source rows, un-rotates
+//     them and writes the bf16 result into the tile.  The chunk is the
+//     lane's lowest three bits: every eight consecutive lanes read one
+//     128-byte line, the pattern the per-CU load path returns fastest (lanes
+//     alternating between lines return at about 60% of that rate).  The two
+//     lanes of a pair (l, l ^ 8) need the same 8 (cos, sin) pairs; each loads
+//     half and they swap the rest by DPP.  The gather's vector-ALU work is
+//     interleaved step by step with
+//     the product loop of the same wave, so one wave keeps both the matrix
+//     pipe and the vector ALU of its SIMD busy.
+//   * 16-token tiles, two activation buffers, one LDS barrier per tile.
+//     Loads run two tiles ahead (register sets by tile parity), the target
+//     tables one tile ahead (shared through LDS), and the output tile is
+//     stored from LDS one tile later as whole 256-byte rows, 16 bytes per
+//     lane, non-temporal.
+//   * No hidden waits.  gfx9 counts outstanding vector memory operations in
+//     one in-order counter, so every global access of the tile loop is
+//     issued unconditionally (tokens outside the item read a valid row and
+//     are never stored; table reads and stores past a range use buffer
+//     offsets beyond the descriptor, which read zeros / are dropped): every
+//     phase issues the same operations, and the waits the compiler derives
+//     are exactly for data that has had its pipeline depth to arrive.
+//   * Bias as the products' initial accumulator (exact fp32, no extra work).
+//   * W is staged through LDS as stored and turned into A fragments with the
+//     transposing ds_read_b64_tr_b16.
 #include "internal.hpp"
+#include "lds_dma.hpp"
 
 #include <atomic>
 #include <type_traits>
@@ -65,30 +69,36 @@
 namespace helm {
 namespace {
 
+using lds::lds_barrier;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kD = 128;          // head dimension
 constexpr int kHalf = 64;
-constexpr int kThreads = 512;    // 8 waves: groups A (0-3) and B (4-7)
-constexpr int kGroupThreads = 256;
-constexpr int kDepth = 2;        // source-row register sets of a data thread (prefetch depth)
-constexpr int kTile = 32;        // tokens per tile = MFMA B-block width
-constexpr int kStageRows = 64;   // W rows staged per pass
-constexpr int kStageRow = kStageRows + 8;  // W^T staging row (padded)
-constexpr int kOtRow = kD + 8;             // staged output row: 128 bf16 + pad
-constexpr int kRowBytes = kD * 2;          // one bf16 head row
-constexpr int kCsTileBytes = kTile * kHalf * 8;   // one tile's (cos, sin) block (rope_index layout)
-// Byte offset of a skipped token's row: beyond every descriptor's record
-// count (descriptors are limited to kMaxRange bytes), so its loads return
-// zero and its stores are dropped.  Adding a row's in-row offset (< 256)
-// cannot wrap.
+constexpr int kThreads = 256;    // 4 waves, one per SIMD
+constexpr int kTile = 16;        // tokens per tile = the product's N
+constexpr int kRowBytes = kD * 2;
+constexpr int kOtRow = kD + 8;   // LDS output row (bf16), 16-byte pad
+constexpr int kTabTile = kTile * kHalf;   // float2 entries of one tile's table
+constexpr int kStageRows = 32;   // W rows staged per pass (one product step)
+// Byte offset past every descriptor's range: loads there return zero and
+// stores are dropped (descriptor ranges stay below it; adding < 256 cannot wrap).
 constexpr uint32_t kMaxRange = 0xffffff00u;
-constexpr uint32_t kSkipRow = 0xffffff00u;
+constexpr uint32_t kSkip = 0xffffff00u;
 constexpr int kStoreNT = 2;      // cache-policy bits of the output stores: nt (streaming)
+
+template <int KSEL>
+struct Cfg {
+  static constexpr int KD = KSEL * kD;        // product depth
+  static constexpr int KSTEPS = KD / 32;      // 16x16x32 steps
+  static constexpr int ROW = KD + 8;          // activation row (bf16), 16-byte pad
+  static constexpr int NJ = KSEL;             // (slot, layer) rows a gathering lane handles
+};
 
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -101,485 +111,454 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Workgroup barrier that orders LDS accesses only.  The barriers of this
-// kernel hand LDS tiles between waves; no wave reads another's global
-// stores, so outstanding global loads and stores may stay in flight across
-// it (a full __syncthreads() would wait for all of them every phase).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Raw buffer over [base, base + bytes); accesses beyond it read 0 / are dropped.
+// A buffer descriptor from workgroup-uniform values.  The values are passed
+// through readfirstlane so that the compiler keeps the descriptor in scalar
+// registers (a descriptor it takes for per-lane makes every access a loop).
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t p = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* q = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-template <int KSEL>
-struct Cfg {
-  static constexpr int KD = KSEL * kD;          // GEMM depth
-  static constexpr int KSTEPS = KD / 16;        // 32x32x16 MFMA steps
-  static constexpr int ROW = KD + 8;            // LDS row: one token, padded by 16 bytes
-  static constexpr int TILE_ELEMS = kTile * ROW;
-  // a group's LDS buffer holds its activation tile, and before that the W^T
-  // staging block (kD rows of kStageRow)
-  static constexpr int BUF_ELEMS = TILE_ELEMS > kD * kStageRow ? TILE_ELEMS : kD * kStageRow;
-};
-
-template <int KSEL>
-__device__ __forceinline__ int lds_off(int t, int c) {
-  return t * Cfg<KSEL>::ROW + (c << 3);
+// Each lane receives the vector of lane l ^ 8, the other lane of its pair
+// (DPP row_ror:8 rotates each row of 16 lanes by half a row).
+__device__ __forceinline__ f32x4 pair_swap(const f32x4& v) {
+  f32x4 o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    o[d] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[d]), 0x128, 0xF, 0xF, false));
+  return o;
 }
 
-// What one thread prefetches for its share of a tile's un-rotation: 16-byte
-// chunks pc (low half) and pc+8 (high half) of token pt for each selected
-// layer, and the (cos, sin) pairs of dims 8pc .. 8pc+7 of that token.
+// Activation tile layout.  A token's row holds the k selected layers' 128
+// features each; within a layer's 256 bytes, 16-byte chunk c of layer j is
+// stored at chunk c ^ X(j), X(j) = 8 (j & 1) + 4 (j >> 1), and the second
+// slot's tile starts 128 bytes past a multiple of 256.  The gather writes
+// one chunk of two (slot, layer) rows from the two halves of a 16-lane row
+// at once; the swizzle and the offset put those halves on different LDS
+// banks.  The product reads chunk 4(s%4) + lg of layer s/4 at step s (lg in
+// 0..3 is untouched by the XOR), so its element offset is a compile-time
+// constant plus 8 lg.
+__device__ __forceinline__ constexpr int xswz(int j) { return 8 * (j & 1) + 4 * (j >> 1); }
+__device__ __forceinline__ constexpr int kswz(int s) { return kD * (s / 4) + 8 * ((4 * (s % 4)) ^ xswz(s / 4)); }
+
+// What a gathering lane holds of one tile: per (slot, layer) row jj the
+// 16-byte chunk of the low half and its partner chunk of the high half, and
+// its half of the tile's source (cos, sin) pairs (keys).
 template <int KSEL>
 struct Raw {
-  u32x4 lo[KSEL], hi[KSEL];
-  f32x4 cs[4];
-  int32_t row;        // paged: source slot of this thread's token of the next tile to load
+  u32x4 lo[Cfg<KSEL>::NJ], hi[Cfg<KSEL>::NJ];
+  f32x4 cs[2];
 };
 
-typedef __attribute__((address_space(3))) void* lds_void_t;
-
-// Copies 16 bytes per lane from a buffer into LDS (buffer->LDS DMA): lane
-// i reads the 16 bytes at byte offset soff + 16*i of the buffer described by
-// `rsrc` and they land at lds_base + 16*i, so one wave moves 1 KB with no
-// registers in between.  rsrc, soff and lds_base are wave-uniform.  Written
-// as inline assembly on purpose: the compiler cannot tell which LDS buffer a
-// copy targets and would otherwise make every later LDS access of the wave
-// wait for all outstanding global loads.  The kernel orders these copies
-// itself: the issuing wave waits (wait_vmcnt) before the barrier that
-// publishes the buffer, and no wave touches a buffer while a copy into it is
-// pending.
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t soff, const void* lds_base, uint32_t lane16) {
-  const uint32_t m = (uint32_t)(uintptr_t)(lds_void_t)lds_base;
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(lane16), "s"(rsrc), "s"(soff), "s"(m)
-               : "memory", "m0");
-}
-
-// Plain buffer descriptor words for [base, base + bytes): the same fields
-// as make_rsrc, for use as an inline-assembly operand.
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t p = (uint64_t)(uintptr_t)base;
-  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
-}
-
-// Waits until at most N of this wave's global loads, stores and
-// global->LDS copies are outstanding (they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// The workgroup's LDS tiles.
 template <int KSEL>
 struct Smem {
-  // activation tiles and output tiles by tile parity
-  __attribute__((aligned(16))) __bf16 xs[2][Cfg<KSEL>::BUF_ELEMS];
-  __attribute__((aligned(16))) __bf16 ot_s[2][kTile * kOtRow];
-  // target-side (cos, sin) blocks of a tile (tile-blocked table layout) for
-  // the epilogue, by tile index mod 3 (keys only)
-  __attribute__((aligned(16))) float2 ct_s[3][kTile * kHalf];
+  static constexpr int SLOT = kTile * Cfg<KSEL>::ROW + 64;   // a slot's tile + 128-byte offset
+  union {
+    __bf16 act[2][2 * SLOT];                    // [tile parity][slot, token, feature]
+    __bf16 stage[2][kStageRows * kD];           // W staging: [slot][row][column]
+  };
+  __bf16 ot[2][2][kTile * kOtRow];              // [tile parity][slot][token][column]
+  float2 ct[3][kTabTile];                       // target (cos, sin) of a tile, by tile index mod 3
+  float bias[2][kD];                            // the slots' bias rows
 };
 
-// One work item: target layer l, head h, keys (KEYS) or values, tokens of
-// chunk `chunk`.  Values have no rotation on either side, so their items
-// issue no table loads or copies at all.  PAGED: source and target rows
-// come from the per-token slot maps (a.src_row, a.dst_row; -1 = skip);
-// otherwise row = token.
+// One work item: target layers l0 (slot 0) and l1 (slot 1, none when
+// l1 >= L_t), head h, keys (KEYS) or values, tokens [t_begin, t_end).
+// PAGED: source and target rows come from the per-token slot maps
+// (a.src_row, a.dst_row; -1 = skip); otherwise row = token.
 template <int KSEL, bool PAGED, bool KEYS>
-__device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l, int32_t h, int32_t chunk,
-                                              int32_t chunk_tokens, Smem<KSEL>& sm) {
+__device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l0, int32_t l1, int32_t h,
+                                              int32_t t_begin, int32_t t_end, Smem<KSEL>& sm) {
   using C = Cfg<KSEL>;
-  constexpr int D = kDepth;
-  constexpr bool keys = KEYS;
-  // contiguous caches: the matrix waves store the output tiles; paged: the
-  // data waves do (they hold the target slot maps)
-  constexpr bool kMatrixStores = !PAGED;
-  auto& xs = sm.xs;
-  auto& ot_s = sm.ot_s;
-  auto& ct_s = sm.ct_s;
-
+  constexpr int NJ = C::NJ;
+  constexpr int S = C::KSTEPS;
+  constexpr int SLOT = Smem<KSEL>::SLOT;
   const int tid = threadIdx.x;
-  // role (0 = matrix waves, 1 = data waves) and wave within the role are
-  // wave-uniform; wave q of each role runs on SIMD q
-  const int role = __builtin_amdgcn_readfirstlane(tid >> 8);
-  const int wq = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
-  const int gtid = tid & 255;
   const int lane = tid & 63;
-  const int lr = lane & 31;                // MFMA A row / B column of this lane
-  const int lk = lane >> 5;                // MFMA k-half of this lane
-  const int wcol = 16 * wq;
-  const int my_col = lr < 16 ? wcol + lr : kHalf + wcol + (lr - 16);
-  const int pt = gtid >> 3;                // un-rotation share: token of the tile
-  const int pc = gtid & 7;                 //   and 16-byte chunk of the low half
-  // byte offset of this lane's first epilogue (cos, sin) piece in a tile's
-  // target-side table block: piece e = 2lk of chunk 2wq, token lr
-  const int ep_off = 2 * lk * (kCsTileBytes / 4) + 128 * lr + 32 * wq;
-  const int32_t n_tok = (int32_t)a.n_tok;
-  const uint32_t src_tok_b = (uint32_t)a.src_tok * 2, dst_tok_b = (uint32_t)a.dst_tok * 2;
-  const uint32_t src_bytes = (uint32_t)((a.src_rows - 1) * a.src_tok * 2 + kRowBytes);
-  const uint32_t dst_bytes = (uint32_t)((a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes);
-  const uint32_t tab_bytes = (uint32_t)((a.n_tok + kTile - 1) / kTile * kCsTileBytes);
-  const u32x4 tab_tgt = rsrc_words(a.rope_tgt, tab_bytes);
-  {
-    const int32_t t_begin = chunk * chunk_tokens;   // a multiple of kTile
-    const int32_t t_end = min(t_begin + chunk_tokens, n_tok);
-    const int nt = (t_end - t_begin + kTile - 1) / kTile;
-    const int32_t blk0 = t_begin / kTile;  // table block of the item's first tile
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lam = w >> 1, hc = w & 1;                // product role: slot, column half
+  const int ln = lane & 15, lg = lane >> 4;          // product lane: token / block row, k-group
+  const int gc = lane & 7, gr = (lane >> 3) & 1;     // gathering lane: 16-byte chunk, pair lane
+  const int gt = 4 * w + (lane >> 4);                //   and token of the tile
+  const int st = tid >> 4, sg = tid & 15;            // storing lane: token, 16-byte segment
+  const int nt = (t_end - t_begin + kTile - 1) / kTile;
+  const int32_t blk0 = t_begin / kTile;              // table block of the item's first tile
 
-    // the selected source layers; an out-of-range entry skips the item (the
-    // target layer is left unwritten)
-    bool active = true;
-    rsrc_t srs[KSEL];
+  // ---- the two slots: active when the layer exists and its selection row
+  // is in range (an out-of-range entry leaves that target layer unwritten)
+  int32_t lay[2] = {l0, l1};
+  bool act_slot[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    bool ok = lay[s] < a.L_t;
 #pragma unroll
     for (int j = 0; j < KSEL; ++j) {
-      const int32_t sj = a.layer_sel[l * KSEL + j];
-      const bool ok = sj >= 0 && sj < a.L_s;
-      active = active && ok;
-      srs[j] = make_rsrc((const uint16_t*)(keys ? a.src_k : a.src_v) +
-                             (ok ? (int64_t)sj * a.src_layer + (int64_t)h * a.src_head : 0),
-                         src_bytes);
+      const int32_t sj = ok ? a.layer_sel[lay[s] * KSEL + j] : 0;
+      ok = ok && sj >= 0 && sj < a.L_s;
     }
-    if (!active) return;                   // uniform over the workgroup
-    const rsrc_t cs_rs = make_rsrc(a.rope_src, tab_bytes);   // source-side tables (keys)
-    const int32_t grp = l * a.H + h;
-    const uint16_t* W = (const uint16_t*)(keys ? a.W_k : a.W_v) + (int64_t)grp * C::KD * kD;
-    const float* bias = (keys ? a.b_k : a.b_v) + (int64_t)grp * kD;
-    const rsrc_t dst = make_rsrc((const uint16_t*)(keys ? a.out_k : a.out_v) + (int64_t)l * a.dst_layer +
-                                     (int64_t)h * a.dst_head,
-                                 dst_bytes);
+    act_slot[s] = ok;
+  }
+  if (!act_slot[0] && !act_slot[1]) return;          // uniform over the workgroup
 
-    bf16x8 wf[C::KSTEPS];       // matrix waves: W^T fragments (see below)
-    bf16x8 wb = {}, ones = {};  // matrix waves: the bias step
+  const char* src = (const char*)(KEYS ? a.src_k : a.src_v);
+  const uint16_t* Wt = (const uint16_t*)(KEYS ? a.W_k : a.W_v);
+  const float* bias = KEYS ? a.b_k : a.b_v;
+  const uint32_t src_tok_b = (uint32_t)a.src_tok * 2, dst_tok_b = (uint32_t)a.dst_tok * 2;
+  const uint32_t tab_bytes = (uint32_t)((a.n_tok + kTile - 1) / kTile * kTabTile * 8);
+  const rsrc_t tab_src = make_rsrc(a.rope_src, tab_bytes);
+  const rsrc_t tab_tgt = make_rsrc(a.rope_tgt, tab_bytes);
+  // output slots (stores): range 0 when a slot is inactive
+  const uint32_t dst_bytes = (uint32_t)((a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes);
+  auto dst_of = [&](int s) __attribute__((always_inline)) {
+    return make_rsrc((const char*)(KEYS ? a.out_k : a.out_v) +
+                         ((int64_t)(act_slot[s] ? lay[s] : 0) * a.dst_layer + (int64_t)h * a.dst_head) * 2,
+                     act_slot[s] ? dst_bytes : 0u);
+  };
+  const rsrc_t dst0 = dst_of(0), dst1 = dst_of(1);
 
-    // ---- data-wave pieces
-    // Issues the loads of tile `tile`'s source rows (this thread's token pt,
-    // chunks pc and pc+8 of each selected layer).  Tokens outside the item
-    // load zeros.
-    auto raw_offset = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
-      const int32_t n = t_begin + tile * kTile + pt;
-      const bool ok = tile < nt && n < t_end;
-      uint32_t rowb;
-      if constexpr (PAGED) {
-        rowb = ok && r.row >= 0 ? (uint32_t)r.row * src_tok_b : kSkipRow;
-        // slot of this thread's token of the next tile this register set loads
-        r.row = a.src_row[max(min(n + D * kTile, t_end - 1), 0)];
-      } else {
-        rowb = ok ? (uint32_t)n * src_tok_b : kSkipRow;
-      }
-      return rowb + 16 * pc;
-    };
-    auto load_layer = [&](Raw<KSEL>& r, uint32_t off, int j) __attribute__((always_inline)) {
-      r.lo[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off, 0, 0);
-      r.hi[j] = __builtin_amdgcn_raw_buffer_load_b128(srs[j], off + kHalf * 2, 0, 0);
-    };
-    // tile-blocked table: piece e of (token pt, chunk pc) at e*4KB + pt*128 + pc*16
-    auto load_tables = [&](Raw<KSEL>& r, int tile) __attribute__((always_inline)) {
-      if constexpr (KEYS) {
-        const uint32_t toff = tile < nt ? (uint32_t)(blk0 + tile) * kCsTileBytes + 128 * pt + 16 * pc : kSkipRow;
+  // ---- gathering lane: base address of each of its (slot, layer) rows
+  // (combination c = gr + 2jj: slot c / KSEL, layer c % KSEL; rows of an
+  // inactive slot read layer 0: that slot's products are never stored)
+  const char* gbase[NJ];
+  int gfeat[NJ], gfeat_hi[NJ];
+  __bf16* gdst[NJ][2];   // by tile parity
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          r.cs[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cs_rs, toff + e * (kCsTileBytes / 4), 0, 0));
-      }
-    };
-    auto load_raw = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
-      const uint32_t off = raw_offset(tile, r);
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int c = gr + 2 * jj;
+    const int s = c / KSEL, j = c % KSEL;
+    const int32_t sl = act_slot[s] ? a.layer_sel[lay[s] * KSEL + j] : 0;
+    gfeat[jj] = j * kD + 8 * (gc ^ xswz(j));              // low-half chunk gc, swizzled
+    gfeat_hi[jj] = j * kD + 8 * ((gc + 8) ^ xswz(j));     // its partner chunk gc + 8
+    gbase[jj] = src + ((int64_t)sl * a.src_layer + (int64_t)h * a.src_head) * 2 + 16 * gc;
 #pragma unroll
-      for (int j = 0; j < KSEL; ++j) load_layer(r, off, j);
-      load_tables(r, tile);
-    };
-    // Un-rotates (keys) the register set's rows and writes them into an
-    // activation tile (when `use`), refilling the set with tile `next` layer
-    // by layer, so that the loads leave between the arithmetic instead of in
-    // one burst.  A skipped token's row is zero in, and whatever it becomes
-    // only reaches its own output column, which is never stored.
-    auto turn_tile = [&](Raw<KSEL>& r, bool use, __bf16* xt, int next) __attribute__((always_inline)) {
-      const uint32_t off = raw_offset(next, r);
-#pragma unroll
-      for (int j = 0; j < KSEL; ++j) {
-        if (use) {
-          u32x4 lo = r.lo[j], hi = r.hi[j];
-          if (keys) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const f32x4 v = r.cs[e];    // (cos, sin) of dims 8pc+2e and 8pc+2e+1
-              const float l0 = bf16lo(lo[e]), l1 = bf16hi(lo[e]);
-              const float h0 = bf16lo(hi[e]), h1 = bf16hi(hi[e]);
-              // R(-p): (lo, hi) -> (lo c + hi s, hi c - lo s)
-              lo[e] = pack_bf16(fmaf(l0, v.x, h0 * v.y), fmaf(l1, v.z, h1 * v.w));
-              hi[e] = pack_bf16(fmaf(h0, v.x, -(l0 * v.y)), fmaf(h1, v.z, -(l1 * v.w)));
-            }
-          }
-          *(u32x4*)&xt[lds_off<KSEL>(pt, 16 * j + pc)] = lo;
-          *(u32x4*)&xt[lds_off<KSEL>(pt, 16 * j + 8 + pc)] = hi;
-        }
-        load_layer(r, off, j);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      load_tables(r, next);
-    };
-    // Writes a computed tile from an LDS output tile to the target cache: 16
-    // threads per token row, 16 bytes each, so a wave stores whole 256-byte
-    // rows.  read_out fetches this thread's two 16-byte pieces from LDS;
-    // write_out issues exactly two stores (a negative tile stores nothing).
-    auto read_out = [&](const __bf16* ot, u32x4* v) __attribute__((always_inline)) {
-      const int seg = gtid & 15;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) v[hh] = *(const u32x4*)&ot[((gtid >> 4) + 16 * hh) * kOtRow + 8 * seg];
-    };
-    auto write_out = [&](int tile, const u32x4* v, const int32_t* drow) __attribute__((always_inline)) {
-      const int seg = gtid & 15;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r = (gtid >> 4) + 16 * hh;
-        const int32_t n = t_begin + tile * kTile + r;
-        const int32_t row = PAGED ? drow[hh] : n;
-        const uint32_t rowb = tile >= 0 && n < t_end && row >= 0 ? (uint32_t)row * dst_tok_b : kSkipRow;
-        // non-temporal: the kernel never reads its output back
-        __builtin_amdgcn_raw_buffer_store_b128(v[hh], dst, rowb + 16 * seg, 0, kStoreNT);
-      }
-    };
-    // ---- matrix-wave pieces
-    // One of the four 1 KB pieces that this wave copies of a tile's (cos,
-    // sin) block (keys only): piece q of wave wq is bytes [(4q + wq) KB, +1 KB).
-    auto table_piece = [&](const u32x4& table, float2* dst_tab, int tile, int q) __attribute__((always_inline)) {
-      if (keys && tile < nt) {
-        const uint32_t off = (4 * q + wq) * 1024;
-        dma16(table, (uint32_t)(blk0 + tile) * kCsTileBytes + off, (char*)dst_tab + off, 16 * lane);
-      }
-    };
-    // Forward rotation of one finished accumulator block into the LDS
-    // output tile ot: half g of this lane's columns.  Accumulator j < 8 is
-    // column wcol + 8*(j/4) + 4*lk + j%4 of token lr; j + 8 is its partner
-    // 64 columns up.  ec holds the (cos, sin) pieces of those columns.
-    auto epilogue_half = [&](const f32x16& acc, const float4* ec, __bf16* ot, int g) __attribute__((always_inline)) {
-      const int c0 = wcol + 8 * g + 4 * lk;
-      float y0[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-      float y1[4] = {acc[8 + 4 * g], acc[9 + 4 * g], acc[10 + 4 * g], acc[11 + 4 * g]};
-      if (keys) {
-        const float4 v0 = ec[2 * g], v1 = ec[2 * g + 1];
-        const float cc[4] = {v0.x, v0.z, v1.x, v1.z};
-        const float ss[4] = {v0.y, v0.w, v1.y, v1.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // R(+p'): (lo, hi) -> (lo c - hi s, hi c + lo s)
-          const float o0 = fmaf(y0[j], cc[j], -(y1[j] * ss[j]));
-          const float o1 = fmaf(y1[j], cc[j], y0[j] * ss[j]);
-          y0[j] = o0;
-          y1[j] = o1;
-        }
-      }
-      *(uint2*)&ot[lr * kOtRow + c0] = make_uint2(pack_bf16(y0[0], y0[1]), pack_bf16(y0[2], y0[3]));
-      *(uint2*)&ot[lr * kOtRow + c0 + kHalf] = make_uint2(pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]));
-    };
-    // The (cos, sin) pieces of this lane's epilogue columns: pieces e = 2lk
-    // and 2lk+1 of chunks 2wq and 2wq+1, token lr (tile-blocked layout).
-    auto epilogue_tables = [&](const float2* ct_tab, float4* ec) __attribute__((always_inline)) {
-      if (keys) {
-        const char* tb = (const char*)ct_tab + ep_off;
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          ec[2 * g] = *(const float4*)(tb + 16 * g);
-          ec[2 * g + 1] = *(const float4*)(tb + 16 * g + kCsTileBytes / 4);
-        }
-      }
-    };
-    // One matrix-wave phase: the products Y^T = W^T X^T + b of tile `tile`
-    // from xt into acc, with the epilogue of the previous tile (accp, target
-    // tables ct_prev, output tile ot_prev) and the copy of the target
-    // tables of tile+1 (into ct_next) interleaved between the products, whose
-    // dependent chain leaves the wave idle between issues.  The wave ends
-    // with the copy of the previous phase complete; this phase's copy stays
-    // in flight until the end of the next one.
-    auto compute_tile = [&](int tile, const __bf16* xt, f32x16& acc, const f32x16& accp, const float2* ct_prev,
-                            __bf16* ot_prev, float2* ct_next, const __bf16* ot_store) __attribute__((always_inline)) {
-      // LDS fragments read ahead (with k >= 3 the registers go to W)
-      constexpr int kAhead = C::KSTEPS < 8 ? C::KSTEPS : (KSEL >= 3 ? 4 : 8);
-      static_assert(8 <= C::KSTEPS, "every table copy and epilogue piece is issued inside the products");
-      bf16x8 xf[kAhead];
-      float4 ec[4];
-      u32x4 ov[2];
-#pragma unroll
-      for (int s = 0; s < kAhead; ++s) xf[s] = *(const bf16x8*)&xt[lds_off<KSEL>(lr, 2 * s + lk)];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, ones, f32x16{}, 0, 0, 0);
-      epilogue_tables(ct_prev, ec);
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-        __builtin_amdgcn_sched_barrier(0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], xf[s % kAhead], acc, 0, 0, 0);
-        if (s + kAhead < C::KSTEPS) xf[s % kAhead] = *(const bf16x8*)&xt[lds_off<KSEL>(lr, 2 * (s + kAhead) + lk)];
-        if (s < 4) table_piece(tab_tgt, ct_next, tile + 1, s);
-        if (s == 4) epilogue_half(accp, ec, ot_prev, 0);
-        if (s == 6) epilogue_half(accp, ec, ot_prev, 1);
-        if constexpr (kMatrixStores) {
-          if (s == 1) read_out(ot_store, ov);
-          if (s == C::KSTEPS - 1) write_out(tile - 2, ov, nullptr);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // The matrix waves' only other global accesses are their stores (two
-      // per phase, after the copies): the previous phase's four copies are
-      // complete once at most its stores and this phase's copies and stores
-      // remain.  (Values copy nothing and never wait.)
-      if constexpr (KEYS) wait_vmcnt<kMatrixStores ? 8 : 4>();
-    };
-
-    // ---- the tile pipeline.  Phase i (i = 0 .. nt+1): the matrix waves
-    // compute tile i from xs[i%2] (accumulators kept in registers) while
-    // rotating tile i-1 into ot_s[(i-1)%2] with the target tables in
-    // ct_s[(i-1)%3], and copy the target tables of tile i+1 into
-    // ct_s[(i+1)%3]; the data waves store tile i-2 from ot_s[i%2], un-rotate
-    // tile i+1 into xs[(i+1)%2] and issue the loads of tile i+1+D (source
-    // rows and source-side tables) into the register set that tile i+1 used
-    // (D sets, so loads have D-1 phases to land).  A barrier ends every
-    // phase.  The phase loop is unrolled by 6 so that buffer indices and
-    // register sets are fixed per copy; the roles run separate loops that
-    // meet the same barriers.
-    static_assert(6 % D == 0, "register sets cycle with the 6-fold unrolled phase loop");
-    lds_barrier();                                   // the previous item's readers of xs[0] are done
-    if (role == 0) {
-      // W^T fragments of this wave's 32 columns, in registers: lane holds
-      // W[m = 16s + 8*lk + i][my_col], i < 8.  The matrix waves stage W
-      // through xs[0] 64 rows at a time, transposed on the way in
-      // (coalesced 16-byte global loads, 2-byte LDS stores), so that each
-      // fragment is one 16-byte LDS read.  (Set up inside the role branch
-      // so that the fragments are live only where they are used.)
-      __bf16* stage = xs[0];
-#pragma unroll
-      for (int part = 0; part < C::KD / kStageRows; ++part) {
-        const u32x4* gsrc = (const u32x4*)(W + (int64_t)part * kStageRows * kD);
-#pragma unroll
-        for (int e = gtid; e < kStageRows * kD / 8; e += kGroupThreads) {
-          const u32x4 v = gsrc[e];
-          const int m = e >> 4, n0 = (e & 15) << 3;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            stage[(n0 + 2 * q) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] & 0xffffu));
-            stage[(n0 + 2 * q + 1) * kStageRow + m] = __builtin_bit_cast(__bf16, (uint16_t)(v[q] >> 16));
-          }
-        }
-        lds_barrier();
-#pragma unroll
-        for (int s4 = 0; s4 < kStageRows / 16; ++s4)
-          wf[(kStageRows / 16) * part + s4] = *(const bf16x8*)&stage[my_col * kStageRow + 16 * s4 + 8 * lk];
-        lds_barrier();                               // the stage may be overwritten
-      }
-      // The bias enters the products as one more 16-deep step: A holds the
-      // column's fp32 bias split exactly into three bf16 parts (b = b1 + b2
-      // + b3), B holds ones in the matching rows, so the accumulator starts
-      // at b with no LDS traffic and no epilogue additions.
-      if (lk == 0) {
-        const float b = bias[my_col];
-        const __bf16 b1 = (__bf16)b;
-        const __bf16 b2 = (__bf16)(b - (float)b1);
-        const __bf16 b3 = (__bf16)(b - (float)b1 - (float)b2);
-        wb[0] = b1;
-        wb[1] = b2;
-        wb[2] = b3;
-        ones[0] = ones[1] = ones[2] = (__bf16)1.0f;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) table_piece(tab_tgt, ct_s[0], 0, q);
-      if constexpr (KEYS) wait_vmcnt<0>();
-      lds_barrier();                                 // tile 0 un-rotated
-      f32x16 acc[2] = {{}, {}};   // accumulators by tile parity
-      auto phase = [&](int i, auto kk) __attribute__((always_inline)) {
-        constexpr int K = decltype(kk)::value;      // i % 6
-        constexpr int P = K & 1, T = K % 3, Tp = (K + 2) % 3, Tn = (K + 1) % 3;
-        if (i < nt) {
-          // (in phase 0 the epilogue rotates an empty block into ot_s[1];
-          // the data waves never store it)
-          compute_tile(i, xs[P], acc[P], acc[P ^ 1], ct_s[Tp], ot_s[P ^ 1], ct_s[Tn], ot_s[P]);
-        } else if (i == nt) {
-          if constexpr (KEYS) wait_vmcnt<0>();
-          float4 ec[4];
-          epilogue_tables(ct_s[Tp], ec);
-          epilogue_half(acc[P ^ 1], ec, ot_s[P ^ 1], 0);
-          epilogue_half(acc[P ^ 1], ec, ot_s[P ^ 1], 1);
-        }
-        if constexpr (kMatrixStores) {
-          if (i >= nt && i <= nt + 1) {   // the last two tiles' stores
-            u32x4 ov[2];
-            read_out(ot_s[P], ov);
-            write_out(i - 2, ov, nullptr);
-          }
-        }
-        (void)T;
-        lds_barrier();
-      };
-      for (int i = 0; i <= nt + 1; i += 6) {
-        phase(i, std::integral_constant<int, 0>());
-        phase(i + 1, std::integral_constant<int, 1>());
-        phase(i + 2, std::integral_constant<int, 2>());
-        phase(i + 3, std::integral_constant<int, 3>());
-        phase(i + 4, std::integral_constant<int, 4>());
-        phase(i + 5, std::integral_constant<int, 5>());
-      }
+    for (int p = 0; p < 2; ++p) gdst[jj][p] = sm.act[p] + s * SLOT + gt * C::ROW;
+  }
+  // Row of the gathering lane's token of tile `tile` (clamped into the item:
+  // rows outside it are read but never stored).  Paged caches read the slot
+  // map a phase before the rows, so the load never waits on its own index.
+  auto src_row_of = [&](int tile) __attribute__((always_inline)) -> int32_t {
+    const int32_t n = min(t_begin + tile * kTile + gt, t_end - 1);
+    if constexpr (PAGED) {
+      return a.src_row[n];
     } else {
-      Raw<KSEL> raw[D];
-      int32_t drow[2][2] = {{0, 0}, {0, 0}};   // paged: target slots of this thread's rows, by tile parity
+      return n;
+    }
+  };
+  auto load_row = [&](int32_t row, int jj, Raw<KSEL>& r) __attribute__((always_inline)) {
+    const u32x4* p = (const u32x4*)(gbase[jj] + (int64_t)(row >= 0 ? row : 0) * src_tok_b);
+    r.lo[jj] = p[0];
+    r.hi[jj] = p[kHalf / 8];
+  };
+  auto load_cs = [&](int tile, Raw<KSEL>& r) __attribute__((always_inline)) {
+    if constexpr (KEYS) {
+      // pieces e = 2 gr, 2 gr + 1 of (token, chunk): pairs 8c + 2e, 8c + 2e + 1
+      const uint32_t off = tile < nt ? (uint32_t)((blk0 + tile) * kTabTile + 2 * gr * 256 + gt * 16 + gc * 2) * 8u
+                                     : kSkip;
+      r.cs[0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tab_src, off, 0, 0));
+      r.cs[1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tab_src, off + 256 * 8, 0, 0));
+    }
+  };
+  // One unit of the un-rotation (keys): piece e of row jj, with v = the
+  // (cos, sin) of dims 8c+2e and 8c+2e+1.  R(-p): (lo, hi) -> (lo c + hi s,
+  // hi c - lo s).
+  auto turn_unit = [&](Raw<KSEL>& r, int jj, int e, const f32x4& v) __attribute__((always_inline)) {
+    const float l0 = bf16lo(r.lo[jj][e]), l1 = bf16hi(r.lo[jj][e]);
+    const float h0 = bf16lo(r.hi[jj][e]), h1 = bf16hi(r.hi[jj][e]);
+    r.lo[jj][e] = pack_bf16(fmaf(l0, v.x, h0 * v.y), fmaf(l1, v.z, h1 * v.w));
+    r.hi[jj][e] = pack_bf16(fmaf(h0, v.x, -(l0 * v.y)), fmaf(h1, v.z, -(l1 * v.w)));
+  };
+  // the (cos, sin) of piece e: this lane's (e = 2 gr, 2 gr + 1) or its pair partner's
+  auto piece_cs = [&](const Raw<KSEL>& r, int e) __attribute__((always_inline)) {
+    const f32x4 own = r.cs[e & 1], other = pair_swap(r.cs[e & 1]);
+    return (e >> 1) == gr ? own : other;
+  };
+  auto put_row = [&](const Raw<KSEL>& r, int jj, int par) __attribute__((always_inline)) {
+    *(u32x4*)&gdst[jj][par][gfeat[jj]] = r.lo[jj];
+    *(u32x4*)&gdst[jj][par][gfeat_hi[jj]] = r.hi[jj];
+  };
+
+  // ---- product lane: W^T fragments of its four blocks (block b: rows
+  // 32hc + 16(b%2) + 64(b/2) of Y^T), from LDS staging one step at a time
+  bf16x8 wf[S][4];
+  {
+    const int64_t grp[2] = {(int64_t)(act_slot[0] ? lay[0] : 0) * a.H + h,
+                            (int64_t)(act_slot[1] ? lay[1] : 0) * a.H + h};
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        if constexpr (PAGED) raw[d].row = a.src_row[max(min(t_begin + d * kTile + pt, t_end - 1), 0)];
-        load_raw(d, raw[d]);
+    for (int s = 0; s < S; ++s) {
+      // rows 32 s .. 32 s + 31 of both slots' W: 1,024 pieces of 16 bytes
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = tid + kThreads * u;
+        const int sl = c >> 9, row = (c >> 4) & 31, c16 = c & 15;
+        const u32x4* g = (const u32x4*)(Wt + (grp[sl] * C::KD + kStageRows * s + row) * kD + 8 * c16);
+        v[u] = act_slot[sl] ? *g : u32x4{0u, 0u, 0u, 0u};
       }
+      lds_barrier();                                 // the staging area is free
 #pragma unroll
-      for (int part = 0; part < C::KD / kStageRows; ++part) {   // the matrix waves stage W
-        lds_barrier();
-        lds_barrier();
+      for (int u = 0; u < 4; ++u) {
+        const int c = tid + kThreads * u;
+        const int sl = c >> 9, row = (c >> 4) & 31, c16 = c & 15;
+        *(u32x4*)&sm.stage[sl][row * kD + 8 * c16] = v[u];
       }
-      turn_tile(raw[0], true, xs[0], D);
-      lds_barrier();                                 // tile 0 un-rotated
-      auto phase = [&](int i, auto kk) __attribute__((always_inline)) {
-        constexpr int P = decltype(kk)::value & 1;          // i % 2
-        constexpr int S = (decltype(kk)::value + 1) % D;    // (i + 1) % D
-        // the output reads first: their latency hides behind the un-rotation
-        if constexpr (kMatrixStores) {
-          turn_tile(raw[S], i + 1 < nt, xs[P ^ 1], i + 1 + D);
-        } else {
-          u32x4 ov[2];
-          read_out(ot_s[P], ov);
-          turn_tile(raw[S], i + 1 < nt, xs[P ^ 1], i + 1 + D);
-          write_out(i - 2, ov, drow[P]);
-        }
-        if constexpr (PAGED) {
+      lds_barrier();
+      // A fragment of block b: lane l gets W[32 s + 8 lg + 0..7][col + ln];
+      // within a 16-lane group lane 4e + qq names row (.. + e) and columns
+      // 4qq .. 4qq+3, and receives its column of 4 rows
+      const int e = ln >> 2, qq = ln & 3;
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-            drow[P ^ 1][hh] = a.dst_row[max(min(t_begin + (i - 1) * kTile + (gtid >> 4) + 16 * hh, t_end - 1), 0)];
-        }
-        lds_barrier();
-      };
-      for (int i = 0; i <= nt + 1; i += 6) {
-        phase(i, std::integral_constant<int, 0>());
-        phase(i + 1, std::integral_constant<int, 1>());
-        phase(i + 2, std::integral_constant<int, 2>());
-        phase(i + 3, std::integral_constant<int, 3>());
-        phase(i + 4, std::integral_constant<int, 4>());
-        phase(i + 5, std::integral_constant<int, 5>());
+      for (int b = 0; b < 4; ++b) {
+        const int row = 8 * lg + e, col = 32 * hc + 16 * (b & 1) + 64 * (b >> 1) + 4 * qq;
+        const __bf16* p = &sm.stage[lam][row * kD + col];
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * kD));
+        wf[s][b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
   }
+  // the slots' bias rows into LDS: the accumulators of every tile start at
+  // the bias of the lane's rows (columns)
+  {
+    const int sl = tid >> 7, col = tid & 127;
+    sm.bias[sl][col] = act_slot[sl] ? bias[((int64_t)lay[sl] * a.H + h) * kD + col] : 0.f;
+  }
+  auto load_bias = [&](f32x4* bv) __attribute__((always_inline)) {
+    const float* bb = &sm.bias[lam][32 * hc + 4 * lg];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bv[b] = *(const f32x4*)(bb + 16 * (b & 1) + 64 * (b >> 1));
+  };
+
+  // ---- target table: each wave loads four pair groups of the tile's
+  // table (groups 4w .. 4w+3, both halves: 2 KB) and puts them into LDS;
+  // the epilogue reads its pairs there
+  const uint32_t tq_off = (uint32_t)((4 * w + lg) * 64 + ln * 2) * 8u;
+  auto load_tq = [&](int tile, f32x4* v) __attribute__((always_inline)) {
+    if constexpr (KEYS) {
+      const uint32_t off = tile < nt ? (uint32_t)(blk0 + tile) * (kTabTile * 8u) + tq_off : kSkip;
+      v[0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tab_tgt, off, 0, 0));
+      v[1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tab_tgt, off + 32 * 8, 0, 0));
+    }
+  };
+  auto put_tq = [&](const f32x4* v, float2* ct) __attribute__((always_inline)) {
+    if constexpr (KEYS) {
+      *(f32x4*)((char*)ct + tq_off) = v[0];
+      *(f32x4*)((char*)ct + tq_off + 32 * 8) = v[1];
+    }
+  };
+
+  // ---- epilogue of a finished tile, in two parts per block pair (g = 0:
+  // blocks 0, 2; g = 1: blocks 1, 3 — RoPE partners, rows n and n + 64):
+  // part hh handles rows 2hh, 2hh + 1 of the lane's four, and the second
+  // part writes the four finished columns of both halves into the LDS output
+  // tile.  (cos, sin) of pairs 32hc + 16g + 4lg + 0..3 sit in table group
+  // 8hc + 4g + lg.
+  auto epi_tables = [&](const float2* ct, int g, f32x4* cv) __attribute__((always_inline)) {
+    if constexpr (KEYS) {
+      const char* tb = (const char*)ct + (uint32_t)((8 * hc + 4 * g + lg) * 64 + ln * 2) * 8u;
+      cv[0] = *(const f32x4*)tb;              // pairs 4G, 4G+1
+      cv[1] = *(const f32x4*)(tb + 32 * 8);   // pairs 4G+2, 4G+3
+    }
+  };
+  auto epi_part = [&](const f32x4* acc, const f32x4* cv, __bf16* ot, int g, int hh, uint32_t* pk)
+                      __attribute__((always_inline)) {
+    float y0[2] = {acc[g][2 * hh], acc[g][2 * hh + 1]};
+    float y1[2] = {acc[g + 2][2 * hh], acc[g + 2][2 * hh + 1]};
+    if constexpr (KEYS) {
+      const f32x4 v = cv[hh];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float c = q ? v.z : v.x, sn = q ? v.w : v.y;
+        // R(+p'): (lo, hi) -> (lo c - hi s, hi c + lo s)
+        const float o0 = fmaf(y0[q], c, -(y1[q] * sn));
+        const float o1 = fmaf(y1[q], c, y0[q] * sn);
+        y0[q] = o0;
+        y1[q] = o1;
+      }
+    }
+    pk[hh] = pack_bf16(y0[0], y0[1]);
+    pk[2 + hh] = pack_bf16(y1[0], y1[1]);
+    if (hh == 1) {
+      const int c0 = 32 * hc + 16 * g + 4 * lg;
+      *(uint2*)&ot[ln * kOtRow + c0] = make_uint2(pk[0], pk[1]);
+      *(uint2*)&ot[ln * kOtRow + c0 + kHalf] = make_uint2(pk[2], pk[3]);
+    }
+  };
+  // ---- stores of a finished tile: token st, 16-byte segment sg, both slots;
+  // `row` is the token's target row (paged: its slot, -1 = skip)
+  auto dst_row_of = [&](int tile) __attribute__((always_inline)) -> int32_t {
+    const int32_t n = t_begin + tile * kTile + st;
+    if constexpr (PAGED) {
+      return a.dst_row[max(min(n, t_end - 1), 0)];
+    } else {
+      return n;
+    }
+  };
+  auto read_out = [&](__bf16 (*ot)[kTile * kOtRow], u32x4* v) __attribute__((always_inline)) {
+    v[0] = *(const u32x4*)&ot[0][st * kOtRow + 8 * sg];
+    v[1] = *(const u32x4*)&ot[1][st * kOtRow + 8 * sg];
+  };
+  auto write_out = [&](int tile, int32_t row, const u32x4* v) __attribute__((always_inline)) {
+    const int32_t n = t_begin + tile * kTile + st;
+    const uint32_t off = tile >= 0 && n < t_end && row >= 0 ? (uint32_t)row * dst_tok_b + 16 * sg : kSkip;
+    // non-temporal: the kernel never reads its output back
+    __builtin_amdgcn_raw_buffer_store_b128(v[0], dst0, off, 0, kStoreNT);
+    __builtin_amdgcn_raw_buffer_store_b128(v[1], dst1, off, 0, kStoreNT);
+  };
+
+  // ---- prologue: tile 0 gathered, tile 1 loaded, tile 2 loading, the
+  // target table of tile 0 in LDS, the bias of tile 0's accumulators read
+  // (paged: the slots of tile 3's rows loading)
+  lds_barrier();                                     // staging reads done: the tiles may be written
+  Raw<KSEL> raw[2];
+  f32x4 accs[2][4];
+  f32x4 bv[4];
+  int32_t srow[2] = {0, 0}, drow[2] = {0, 0};
+  {
+    f32x4 tq[2];
+    load_tq(0, tq);
+    const int32_t r0 = src_row_of(0), r1 = src_row_of(1);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) load_row(r0, jj, raw[0]);
+    load_cs(0, raw[0]);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) load_row(r1, jj, raw[1]);
+    load_cs(1, raw[1]);
+    put_tq(tq, sm.ct[0]);
+  }
+  if constexpr (KEYS) {
+#pragma unroll
+    for (int u = 0; u < NJ * 4; ++u) turn_unit(raw[0], u % NJ, u / NJ, piece_cs(raw[0], u / NJ));
+  }
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) put_row(raw[0], jj, 0);
+  {
+    const int32_t r2 = src_row_of(2);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) load_row(r2, jj, raw[0]);
+    load_cs(2, raw[0]);
+  }
+  if constexpr (PAGED) srow[1] = src_row_of(3);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) accs[1][b] = f32x4{0.f, 0.f, 0.f, 0.f};   // "tile -1": never stored
+  load_bias(bv);
+  lds_barrier();
+
+  // ---- the tile pipeline.  Phase i works on five tiles at once, spread
+  // over the product steps of tile i so that the matrix pipe, the vector
+  // ALU, LDS and the memory path all stay busy:
+  //   products of tile i (activation buffer i % 2, accumulators i % 2),
+  //   gather of tile i+1 (loaded in phase i-2) into the other buffer and
+  //     the loads of tile i+3 into the register set it frees,
+  //   epilogue of tile i-1 (the other accumulators, target table i-1) into
+  //     output tile (i-1) % 2,
+  //   stores of tile i-2 from output tile i % 2,
+  //   the target table of tile i+1 (tables by tile index mod 3).
+  // One barrier ends the phase.  Unrolled by two so that every buffer and
+  // register set is fixed; past the last tile the work runs on stale
+  // buffers whose results are never stored (so the phase has no branches).
+  constexpr int kTq = 0;                       // step of each piece of work
+  constexpr int kTqPut = S - 1;
+  constexpr int kCv0 = S > 1 ? 1 : 0, kCv1 = S > 3 ? 3 : S - 1;
+  constexpr int kOt = S > 4 ? 4 : S - 1, kSt = S > 6 ? 6 : S - 1;
+  auto epi_step = [](int g, int hh) constexpr { return 2 + 2 * g + hh < S ? 2 + 2 * g + hh : S - 1; };
+  auto put_step = [](int jj) constexpr {
+    // keys: after the row's last un-rotation unit (units go piece by piece)
+    return KEYS ? 3 * NJ + jj : (jj + 1 < S ? jj + 1 : S - 1);
+  };
+  auto phase = [&](int i, auto par) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;   // i % 2
+    constexpr int RA = 3;                     // fragment ring: reads RA - 1 steps ahead
+    Raw<KSEL>& r = raw[P ^ 1];
+    f32x4* acc = accs[P];
+    const f32x4* pacc = accs[P ^ 1];
+    const __bf16* xb = sm.act[P] + lam * SLOT + ln * C::ROW + 8 * lg;
+    __bf16* ot_prev = sm.ot[P ^ 1][lam];
+    const float2* ct_prev = sm.ct[(i + 2) % 3];   // tile i-1
+    float2* ct_next = sm.ct[(i + 1) % 3];         // tile i+1
+    u32x4 so[2];
+    f32x4 cv[2][2];
+    f32x4 tq[2];
+    uint32_t pk[2][4];
+    f32x4 v = {};
+    const int32_t row3 = PAGED ? srow[P ^ 1] : src_row_of(i + 3);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = bv[b];
+    bf16x8 xf[RA];
+#pragma unroll
+    for (int s = 0; s < RA - 1; ++s) xf[s] = *(const bf16x8*)(xb + kswz(s));
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + RA - 1 < S) xf[(s + RA - 1) % RA] = *(const bf16x8*)(xb + kswz(s + RA - 1));
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s][b], xf[s % RA], acc[b], 0, 0, 0);
+      if constexpr (KEYS) {
+        // unit s: piece e = s / NJ of row jj = s % NJ
+        const int e = s / NJ, jj = s % NJ;
+        if (jj == 0) v = piece_cs(r, e);
+        turn_unit(r, jj, e, v);
+      }
+      if (s == 0 && PAGED) {
+        srow[P] = src_row_of(i + 4);
+        drow[P] = dst_row_of(i - 1);
+      }
+      if (s == kTq) load_tq(i + 1, tq);
+      if (s == kCv0) epi_tables(ct_prev, 0, cv[0]);
+      if (s == kCv1) epi_tables(ct_prev, 1, cv[1]);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          if (s == epi_step(g, hh)) epi_part(pacc, cv[g], ot_prev, g, hh, pk[g]);
+      if (s == kOt) read_out(sm.ot[P], so);
+      if (s == kSt) write_out(i - 2, PAGED ? drow[P ^ 1] : dst_row_of(i - 2), so);
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj)
+        if (s == put_step(jj)) {
+          put_row(r, jj, P ^ 1);
+          load_row(row3, jj, r);
+          if (jj == NJ - 1) load_cs(i + 3, r);
+        }
+      if (s == kTqPut) {
+        put_tq(tq, ct_next);
+        load_bias(bv);                        // for the next phase's accumulators
+      }
+      // the fragment stays live to the end of the step, so that the vector
+      // work of the step does not reuse its registers and can run beside
+      // the products
+      asm volatile("" ::"v"(xf[s % RA]));
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+  };
+  for (int i = 0; i <= nt + 1; i += 2) {
+    phase(i, std::integral_constant<int, 0>());
+    phase(i + 1, std::integral_constant<int, 1>());
+  }
 }
 
-// Persistent sweep over the keys (KEYS) or the values of every target
-// layer: workgroup b takes items b, b + grid, ...; an item is (token chunk,
-// target layer, head) with the head fastest.
+// Persistent sweep: workgroup b takes items b, b + grid, ...; item =
+// (chunk * n_lpairs + layer pair) * H + head, the head fastest.
 template <int KSEL, bool PAGED, bool KEYS>
 __global__ void __launch_bounds__(kThreads, 1)
-transfer_mfma_kernel(XferArgs a, int32_t n_pairs, int32_t chunk_tokens, int32_t n_items) {
+transfer_mfma_kernel(XferArgs a, int32_t n_lpairs, int32_t chunk_tokens, int32_t n_items) {
   __shared__ __attribute__((aligned(16))) Smem<KSEL> sm;
   for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int32_t pr = item % n_pairs;
-    transfer_item<KSEL, PAGED, KEYS>(a, pr / a.H, pr % a.H, item / n_pairs, chunk_tokens, sm);
+    const int32_t h = item % a.H, rest = item / a.H;
+    const int32_t lp = rest % n_lpairs, chunk = rest / n_lpairs;
+    const int32_t t_begin = chunk * chunk_tokens;
+    const int32_t t_end = (int32_t)min((int64_t)t_begin + chunk_tokens, a.n_tok);
+    transfer_item<KSEL, PAGED, KEYS>(a, lp, lp + n_lpairs, h, t_begin, t_end, sm);
+    lds_barrier();   // the next item's staging overwrites the tiles
   }
 }
 
@@ -597,37 +576,56 @@ int cu_count() {
   return n;
 }
 
+// Token chunks per (layer pair, head): as many as keep every CU busy in as
+// few rounds as possible, counting a few tiles of pipeline fill and map
+// staging per item.
+int64_t pick_chunks(int64_t n_tok, int64_t base_items, int64_t slots) {
+  int64_t best = 1, best_cost = INT64_MAX;
+  for (int64_t c = 1; c <= 64; ++c) {
+    const int64_t items = c * base_items;
+    const int64_t rounds = (items + slots - 1) / slots;
+    const int64_t chunk = ((n_tok + c - 1) / c + kTile - 1) / kTile * kTile;
+    if (c > 1 && (c - 1) * chunk >= n_tok) break;   // chunks would be empty
+    const int64_t cost = rounds * (chunk / kTile + 4);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 bool mfma_supports(const XferArgs& a) {
   // 16-byte vector loads of source rows, W and bias, 16-byte stores of
-  // outputs, and every buffer descriptor's byte range below kMaxRange
+  // outputs, and the buffer descriptors' byte ranges below kMaxRange
   auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
   const int64_t lim = kMaxRange;
-  const bool ranges = (a.n_tok + kTile - 1) / kTile * kCsTileBytes <= lim &&
-                      (a.src_rows - 1) * a.src_tok * 2 + kRowBytes <= lim &&
-                      (a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes <= lim && a.n_tok < 0x7fffffffLL;
+  const bool ranges = (a.n_tok + kTile - 1) / kTile * kTabTile * 8 <= lim &&
+                      (a.dst_rows - 1) * a.dst_tok * 2 + kRowBytes <= lim && a.n_tok < 0x7fffffffLL &&
+                      a.src_tok * 2 <= 0xffffffffLL;
   return ranges && a.D == kD && a.k >= 1 && a.k <= 4 && al(a.src_k, 16) && al(a.src_v, 16) && al(a.W_k, 16) &&
          al(a.W_v, 16) && al(a.out_k, 16) && al(a.out_v, 16) && al(a.rope_src, 16) && al(a.rope_tgt, 16) &&
-         al(a.b_k, 16) && al(a.b_v, 16);
+         al(a.b_k, 16) && al(a.b_v, 16) && (a.src_tok * 2) % 16 == 0 && (a.src_head * 2) % 16 == 0 &&
+         (a.src_layer * 2) % 16 == 0 && (a.dst_tok * 2) % 16 == 0 && (a.dst_head * 2) % 16 == 0 &&
+         (a.dst_layer * 2) % 16 == 0;
 }
 
 hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream) {
   if (!mfma_supports(a)) return hipErrorNotSupported;
   if (a.n_tok <= 0) return hipSuccess;
-  const int64_t n_pairs = (int64_t)a.L_t * a.H;   // per launch: the keys, then the values
-  const int64_t slots = cu_count();   // one 8-wave workgroup per CU
-  // Split tokens into chunks only when there are fewer pairs than CUs.
-  int64_t n_chunks = 1;
-  if (n_pairs < slots) n_chunks = (slots + n_pairs - 1) / n_pairs;
-  int64_t chunk_tokens = (a.n_tok + n_chunks - 1) / n_chunks;
-  chunk_tokens = (chunk_tokens + kTile - 1) / kTile * kTile;
-  n_chunks = (a.n_tok + chunk_tokens - 1) / chunk_tokens;
-  const int64_t n_items = n_pairs * n_chunks;
+  const int64_t n_lpairs = (a.L_t + 1) / 2;
+  const int64_t base = n_lpairs * a.H;
+  const int64_t slots = cu_count();   // one 4-wave workgroup per CU
+  const int64_t n_chunks = pick_chunks(a.n_tok, base, slots);
+  const int64_t chunk_tokens = ((a.n_tok + n_chunks - 1) / n_chunks + kTile - 1) / kTile * kTile;
+  const int64_t chunks = (a.n_tok + chunk_tokens - 1) / chunk_tokens;
+  const int64_t n_items = base * chunks;
   if (n_items > 0x7fffffffLL) return hipErrorInvalidValue;
   const int64_t grid = n_items < slots ? n_items : slots;
   const dim3 g((unsigned)grid), b(kThreads);
-  const int32_t np = (int32_t)n_pairs, ct = (int32_t)chunk_tokens, ni = (int32_t)n_items;
+  const int32_t np = (int32_t)n_lpairs, ct = (int32_t)chunk_tokens, ni = (int32_t)n_items;
   const bool paged = a.src_row != nullptr;
   if (paged != (a.dst_row != nullptr)) return hipErrorInvalidValue;
 #define HELM_LAUNCH(K)                                                                          \

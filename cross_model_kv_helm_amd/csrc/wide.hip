@@ -103,7 +103,7 @@ struct WideArgs {
   const uint16_t* WT_v;
   const float* b_k;           // [L_t, H, D]
   const float* b_v;
-  const float2* rope_tgt;     // (cos, sin) at tgt_pos (rope_index layout)
+  const float2* rope_tgt;     // (cos, sin) at tgt_pos (rope_tgt_index layout)
   const int32_t* layer_sel;   // [L_t, k]
   uint16_t* out_k;            // [L_t, H, T, D] bf16
   uint16_t* out_v;
@@ -316,7 +316,7 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
         if (t >= T) continue;
         float ylo = acc[mb][nb][r] + blo, yhi = acc[mb][nb + kNB / 2][r] + bhi;
         if (kind == 0) {
-          const float2 cs = a.rope_tgt[rope_index(t, dlo, kHalf)];
+          const float2 cs = a.rope_tgt[rope_tgt_index(t, dlo, kHalf)];
           const float olo = fmaf(ylo, cs.x, -(yhi * cs.y));
           const float ohi = fmaf(yhi, cs.x, ylo * cs.y);
           ylo = olo;
@@ -354,8 +354,8 @@ unrotate_keys_kernel(const uint16_t* __restrict__ src_k, const float2* __restric
     u32x4 olo, ohi;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float2 c0 = rope_src[rope_index(t, 8 * pc + 2 * q, kHalf)];
-      const float2 c1 = rope_src[rope_index(t, 8 * pc + 2 * q + 1, kHalf)];
+      const float2 c0 = rope_src[rope_src_index(t, 8 * pc + 2 * q, kHalf)];
+      const float2 c1 = rope_src[rope_src_index(t, 8 * pc + 2 * q + 1, kHalf)];
       const float l0 = __uint_as_float(lo[q] << 16), l1 = __uint_as_float(lo[q] & 0xffff0000u);
       const float h0 = __uint_as_float(hi[q] << 16), h1 = __uint_as_float(hi[q] & 0xffff0000u);
       // R(-p): (lo, hi) -> (lo c + hi s, hi c - lo s)

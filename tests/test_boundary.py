@@ -180,7 +180,7 @@ def test_paged_check():
 def test_paged_workspace_bytes():
     s = paged_shape()
     n = hk.helm_kv_paged_workspace_bytes(s)
-    assert n == 2 * (64 * 64 * 8) + 2 * 256          # tables padded to whole 32-token blocks
+    assert n == 2 * (48 * 64 * 8) + 2 * 256          # 40 tokens: tables padded to whole 16-token blocks
 
 
 def test_paged_invalid_refused():
