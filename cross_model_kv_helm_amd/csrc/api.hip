@@ -159,7 +159,7 @@ int run_transfer(helm::XferArgs& a, int32_t dtype, const int32_t* src_pos, const
 
 // ---- ridge fit ---------------------------------------------------------
 struct RidgeWorkspace {
-  size_t gram, cross, sums, M, total;   // byte offsets of each part, total size
+  size_t gram, cross, sums, M, total;   // byte offsets of each part (sums: the sums, then the shifts), total size
 };
 
 int check_ridge_shape(const helm_ridge_shape_t* s) {
@@ -187,7 +187,7 @@ int check_ridge_shape(const helm_ridge_shape_t* s) {
 bool ridge_workspace_layout(const helm_ridge_shape_t* s, RidgeWorkspace& w) {
   const int64_t G = s->n_groups, IN = s->in_features, D = s->out_features;
   int64_t g = G, c = G, u = G, m = G;
-  if (!mul_ok(g, IN * IN * 4) || !mul_ok(c, IN * D * 4) || !mul_ok(u, (IN + D) * 4) || !mul_ok(m, IN * (IN + D) * 8))
+  if (!mul_ok(g, IN * IN * 4) || !mul_ok(c, IN * D * 4) || !mul_ok(u, (IN + D) * 8) || !mul_ok(m, IN * (IN + D) * 8))
     return false;
   w.gram = 0;
   w.cross = align_up((size_t)g);
@@ -772,6 +772,7 @@ int helm_ridge_fit_stage(int stages, const void* X, const void* Y, float* W, flo
   f.gram = (float*)(ws + w.gram);
   f.cross = (float*)(ws + w.cross);
   f.sums = (float*)(ws + w.sums);
+  f.shift = f.sums + s->n_groups * (int64_t)(s->in_features + s->out_features);
   f.M = (double*)(ws + w.M);
   f.W = W;
   f.b = b;

@@ -113,7 +113,7 @@ bool wide_supports(const WideXfer& x);
 hipError_t launch_wide(const WideXfer& x, bool prep, bool product, hipStream_t stream);
 
 // Ridge fit of G maps (bf16 observations, D = 128 targets, IN a multiple of
-// 128 up to 1024): gram/cross/sums/M are workspace, W [G, IN, D] and
+// 128 up to 1024): gram/cross/sums/shift/M are workspace, W [G, IN, D] and
 // b [G, D] the fp32 results.
 struct RidgeFit {
   const void* X;     // [G, N, IN] bf16
@@ -121,6 +121,7 @@ struct RidgeFit {
   float* gram;       // [G, IN, IN]
   float* cross;      // [G, IN, D]
   float* sums;       // [G, IN + D]
+  float* shift;      // [G, IN + D]
   double* M;         // [G, IN, IN + D]
   float* W;
   float* b;

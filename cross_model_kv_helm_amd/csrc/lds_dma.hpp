@@ -16,10 +16,14 @@ typedef __attribute__((address_space(3))) void* lds_void_t;
 constexpr uint32_t kSkip = 0xffffff00u;
 
 // Raw buffer descriptor words: base, `bytes` in range (offsets at or past it
-// read zeros), raw (unswizzled) dword format.
+// read zeros), raw (unswizzled) dword format.  The arguments are wave-uniform;
+// readfirstlane tells the compiler so, keeping the words in scalar registers
+// (the copy's descriptor operand must be one).
 __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t p = (uint64_t)(uintptr_t)base;
-  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu),
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
 }
 
 // Buffer -> LDS copy of 16 bytes per lane: lane i reads the 16 bytes at

@@ -7,8 +7,20 @@
 // X [N, IN] and targets Y [N, D]:
 //   W = (Xc^T Xc + lambda I)^-1 Xc^T Yc,   b = mean(Y) - mean(X) W
 // (Xc, Yc the centred data).  The centred products follow from one pass
-// over the raw data: Xc^T Xc = X^T X - sx sx^T / N and Xc^T Yc = X^T Y -
-// sx sy^T / N with the column sums sx, sy.
+// over shifted data D = X - 1 s^T, E = Y - 1 t^T (per-feature shifts s,
+// t): Xc^T Xc = D^T D - sd sd^T / N and Xc^T Yc = D^T E - sd se^T / N with
+// the column sums sd, se of the shifted data, and mean(X) = s + sd / N.
+// Centring is what keeps the fp32 sums accurate: with a feature mean m
+// large against its spread sigma, the raw products' partial sums grow like
+// n m^2 and their rounding, left in the centred result, like u n m^2 —
+// a relative error of order u (m / sigma)^2.  The shifts bring the fed
+// values to the order of sigma before any product.  They are taken from the
+// group's first observations (ridge_shift_kernel): a feature whose first
+// min(N, 64) values share one sign and lie within a factor 1.5 of each
+// other is shifted by its first value, any other by 0.  For a shifted
+// feature every value within a factor 2 of the shift differs from it by a
+// bf16 number exactly (the products stay exact); a rarer value is rounded
+// to bf16 once, an error far below the fp32 accumulation's.
 //
 // Design for MI355X:
 //   * Gram kernel (matrix cores, the hot loop: 2 N IN (IN + D) flop per
@@ -51,6 +63,8 @@
 #include "internal.hpp"
 #include "lds_dma.hpp"
 
+#include <type_traits>
+
 namespace helm {
 namespace {
 
@@ -80,9 +94,10 @@ constexpr int kYTile = -2;         // a B tile that holds Y (pieces 0-15) instea
 struct GramArgs {
   const uint16_t* X;     // [G, N, IN] bf16
   const uint16_t* Y;     // [G, N, D] bf16
+  float* shift;          // [G, IN + D] fp32: the shifts of X's features, then of Y's columns
   float* gram;           // [G, IN, IN] fp32 (the 128-blocks on and above the diagonal written)
   float* cross;          // [G, IN, D] fp32
-  float* sums;           // [G, IN + D] fp32: column sums of X, then of Y
+  float* sums;           // [G, IN + D] fp32: column sums of the shifted X, then of the shifted Y
   int64_t N;
   int32_t G, IN, nF;     // nF = IN / 128 feature groups
   int32_t tiles;         // workgroups per group (ridge_tiles_per_group)
@@ -177,15 +192,43 @@ __device__ __forceinline__ float frag_sum(const bf16x8& v, float s) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, s, false);
 }
 
+// x - s for the 8 values of a fragment (ns = -s): each difference formed
+// exactly in fp32 (v_dot2_f32_bf16 against the selectors e0 = (1, 0) and
+// e1 = (0, 1), accumulator -s), then rounded to bf16.  Fragment value j is
+// observation 8 kg + j of its 16-observation slice; with `n_valid` < 16
+// (the group's last slice) the values of later observations (padding read
+// as zeros) become 0.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 shift_frag(const bf16x8& v, float ns, int first, int n_valid, bf16x2 e0,
+                                             bf16x2 e1) {
+  bf16x8 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2 pr = {v[2 * k], v[2 * k + 1]};
+    float d0 = __builtin_amdgcn_fdot2_f32_bf16(pr, e0, ns, false);
+    float d1 = __builtin_amdgcn_fdot2_f32_bf16(pr, e1, ns, false);
+    if (n_valid < 16) {
+      d0 = first + 2 * k < n_valid ? d0 : 0.f;
+      d1 = first + 2 * k + 1 < n_valid ? d1 : 0.f;
+    }
+    o[2 * k] = (__bf16)d0;
+    o[2 * k + 1] = (__bf16)d1;
+  }
+  return o;
+}
+
 struct GramSmem {
   char A[2][kKB * kRowBytes] __attribute__((aligned(16)));
   char B[2][kKB * kRowBytes] __attribute__((aligned(16)));
 };
 
-template <int MODE>
+// SHIFT: the wave's fragments are shifted (ns_a, ns_b: minus the shifts of
+// its A rows' and B columns' features, per 32-block); otherwise every shift
+// of the wave is 0 and the fragments are fed as stored.
+template <int MODE, bool SHIFT>
 __device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int64_t g, const TileJob& tj,
                                            const WaveJob& wj, int w, int lane, f32x16 (&acc)[4][4],
-                                           float (&tot)[4]) {
+                                           float (&tot)[4], const float (&ns_a)[4], const float (&ns_b)[4]) {
   constexpr int NB = MODE == kHalfY ? 2 : 4;            // B 32-column blocks of the wave
   constexpr bool kSame = MODE == kFullSumA;             // B fragments = A fragments
   const int64_t N = a.N;
@@ -255,9 +298,19 @@ __device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int6
   wait_vmcnt<0>();
   lds_barrier();
   constexpr int kStride = NB / 2;   // products per copy in the first half of a step
-  for (int s = 0; s < n_steps; ++s) {
+  // the shift's selectors, held in registers: the compiler would encode
+  // (1, 0) as the inline constant 1.0, which the instruction reads as the
+  // fp32 bit pattern, i.e. (0, 1)
+  uint32_t sel0 = 0x00003f80u, sel1 = 0x3f800000u;
+  asm("" : "+v"(sel0), "+v"(sel1));
+  const bf16x2 e0 = __builtin_bit_cast(bf16x2, sel0), e1 = __builtin_bit_cast(bf16x2, sel1);
+  // one step; MASK: the group's last step, whose observations may end
+  // inside it (only shifted fragments need their padding zeroed)
+  auto step = [&](int s, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int p = s & 1;
     const bool more = s + 1 < n_steps;
+    const int nv = MASK ? (int)(N - (int64_t)s * kKB) : kKB;   // observations of this step
     const u32x4 ra = a_rsrc(more ? s + 1 : s), rb = b_rsrc(more ? s + 1 : s);
     const char* At = sm.A[p];
     const char* Bt = wj.b_in_a ? sm.A[p] : sm.B[p];
@@ -268,10 +321,21 @@ __device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int6
     bf16x8 afs[2][4], bfs[2][NB];
     auto read_ks = [&](int ks, bf16x8* af, bf16x8* bfr) __attribute__((always_inline)) {
       if constexpr (MODE != kIdle) {
+        const int nvs = MASK ? nv - 16 * ks : 16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = read_frag(At, a_off[i], ks);
+        for (int i = 0; i < 4; ++i) {
+          af[i] = read_frag(At, a_off[i], ks);
+          if constexpr (SHIFT) af[i] = shift_frag(af[i], ns_a[i], 8 * kg, nvs, e0, e1);
+        }
 #pragma unroll
-        for (int i = 0; i < NB; ++i) bfr[i] = kSame ? af[i] : read_frag(Bt, b_off[i], ks);
+        for (int i = 0; i < NB; ++i) {
+          if constexpr (kSame) {
+            bfr[i] = af[i];
+          } else {
+            bfr[i] = read_frag(Bt, b_off[i], ks);
+            if constexpr (SHIFT) bfr[i] = shift_frag(bfr[i], ns_b[i], 8 * kg, nvs, e0, e1);
+          }
+        }
       }
     };
     read_ks(0, afs[0], bfs[0]);
@@ -300,7 +364,37 @@ __device__ __forceinline__ void gram_steps(const GramArgs& a, GramSmem& sm, int6
     }
     wait_vmcnt<0>();
     lds_barrier();   // step s+1 landed everywhere; everyone is done with buffer p
+  };
+  if constexpr (SHIFT) {
+    for (int s = 0; s + 1 < n_steps; ++s) step(s, std::false_type());
+    step(n_steps - 1, std::true_type());
+  } else {
+    for (int s = 0; s < n_steps; ++s) step(s, std::false_type());
   }
+}
+
+// The per-feature shifts of every group (one thread per X feature or Y
+// column): the first observation's value when the first min(N, 64)
+// observations share its sign and lie within a factor 1.5 of each other,
+// else 0.  Block b covers group b / nb, columns 256 (b % nb) ...
+__global__ void __launch_bounds__(kThreads) ridge_shift_kernel(GramArgs a, int32_t nb) {
+  const int64_t g = blockIdx.x / nb;
+  const int c = (int)(blockIdx.x % nb) * kThreads + threadIdx.x;
+  const int IN = a.IN;
+  if (c >= IN + kD) return;
+  const bool is_x = c < IN;
+  const uint16_t* p = is_x ? a.X + g * a.N * IN + c : a.Y + g * a.N * kD + (c - IN);
+  const int64_t ld = is_x ? IN : kD;
+  const int rows = (int)(a.N < kKB ? a.N : kKB);
+  const float first = __uint_as_float((uint32_t)p[0] << 16);
+  float lo = first, hi = first;
+  for (int r = 1; r < rows; ++r) {
+    const float v = __uint_as_float((uint32_t)p[r * ld] << 16);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  const bool tight = (lo > 0.f && hi <= 1.5f * lo) || (hi < 0.f && lo >= 1.5f * hi);
+  a.shift[g * (IN + kD) + c] = tight ? first : 0.f;
 }
 
 __global__ void __launch_bounds__(kThreads, 1) ridge_gram_kernel(GramArgs a) {
@@ -331,13 +425,33 @@ __global__ void __launch_bounds__(kThreads, 1) ridge_gram_kernel(GramArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   float tot[4] = {0.f, 0.f, 0.f, 0.f};
-  switch (wj.mode) {
-    case kFull: gram_steps<kFull>(a, sm, g, tj, wj, w, lane, acc, tot); break;
-    case kFullSumA: gram_steps<kFullSumA>(a, sm, g, tj, wj, w, lane, acc, tot); break;
-    case kFullSumB: gram_steps<kFullSumB>(a, sm, g, tj, wj, w, lane, acc, tot); break;
-    case kHalfY: gram_steps<kHalfY>(a, sm, g, tj, wj, w, lane, acc, tot); break;
-    default: gram_steps<kIdle>(a, sm, g, tj, wj, w, lane, acc, tot); break;
+  // minus the shifts of the wave's fragment features: A row 32i + lane%32
+  // of its block, B column 32i + lane%32 (a Y column for X^T Y blocks)
+  float ns_a[4] = {0.f, 0.f, 0.f, 0.f}, ns_b[4] = {0.f, 0.f, 0.f, 0.f};
+  if (wj.mode != kIdle) {
+    const float* sh = a.shift + g * (int64_t)(IN + kD);
+    const int l32 = lane & 31, nbs = wj.mode == kHalfY ? 2 : 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ns_a[i] = -sh[wj.row0 + 32 * i + l32];
+      if (i < nbs) ns_b[i] = -sh[(wj.cross ? IN : 0) + wj.col0 + 32 * i + l32];
+    }
   }
+  bool nz = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nz = nz || ns_a[i] != 0.f || ns_b[i] != 0.f;
+  const bool shifted = __builtin_amdgcn_ballot_w64(nz) != 0;   // wave-uniform
+#define HELM_GRAM(M)                                                                   \
+  (shifted ? gram_steps<M, true>(a, sm, g, tj, wj, w, lane, acc, tot, ns_a, ns_b)       \
+           : gram_steps<M, false>(a, sm, g, tj, wj, w, lane, acc, tot, ns_a, ns_b))
+  switch (wj.mode) {
+    case kFull: HELM_GRAM(kFull); break;
+    case kFullSumA: HELM_GRAM(kFullSumA); break;
+    case kFullSumB: HELM_GRAM(kFullSumB); break;
+    case kHalfY: HELM_GRAM(kHalfY); break;
+    default: gram_steps<kIdle, false>(a, sm, g, tj, wj, w, lane, acc, tot, ns_a, ns_b); break;
+  }
+#undef HELM_GRAM
 
   // ---- epilogue: accumulator register r of a 32 x 32 block holds row
   // 8(r/4) + 4(lane/32) + r%4, column lane%32
@@ -377,6 +491,7 @@ struct SolveArgs {
   const float* gram;     // [G, IN, IN] (upper tiles)
   const float* cross;    // [G, IN, D]
   const float* sums;     // [G, IN + D]
+  const float* shift;    // [G, IN + D]
   double* M;             // [G, IN, IN + D] fp64 workspace: upper A | right-hand sides
   float* W;              // [G, IN, D]
   float* b;              // [G, D]
@@ -410,6 +525,7 @@ __global__ void __launch_bounds__(kThreads, MIN_WAVES) ridge_solve_kernel(SolveA
   const float* __restrict__ C = a.cross + g * (int64_t)n * kD;
   const float* __restrict__ sx = a.sums + g * (int64_t)(n + kD);
   const float* __restrict__ sy = sx + n;
+  const float* __restrict__ sh = a.shift + g * (int64_t)(n + kD);   // the shifts: mean = shift + sums / N
   double* __restrict__ M = a.M + g * (int64_t)n * ld;
   const int pld = n + kD - kP;   // row length of the panel rows in LDS
   auto Pn = [&](int r, int c) __attribute__((always_inline)) -> double& { return pn_lds[r * pld + c]; };
@@ -590,20 +706,21 @@ __global__ void __launch_bounds__(kThreads, MIN_WAVES) ridge_solve_kernel(SolveA
     __syncthreads();
   }
 
-  // ---- outputs: W in fp32; b = mean(Y) - mean(X) W in fp64
+  // ---- outputs: W in fp32; b = mean(Y) - mean(X) W in fp64, the means
+  // being the shifts plus the shifted data's sums / N
   float* Wg = a.W + g * (int64_t)n * kD;
   for (int e = tid; e < n * kD; e += kThreads) {
     const int i = e / kD, d = e % kD;
     Wg[e] = (float)M[(int64_t)i * ld + n + d];
   }
   if (tid < kD) {
-    double v = (double)sy[tid] * invN;
+    double v = (double)sh[n + tid] + (double)sy[tid] * invN;
     for (int i0 = 0; i0 < n; i0 += kRB) {   // (n is a multiple of kRB)
       double mv[kRB];
 #pragma unroll
       for (int u = 0; u < kRB; ++u) mv[u] = M[(int64_t)(i0 + u) * ld + n + tid];
 #pragma unroll
-      for (int u = 0; u < kRB; ++u) v -= (double)sx[i0 + u] * invN * mv[u];
+      for (int u = 0; u < kRB; ++u) v -= ((double)sh[i0 + u] + (double)sx[i0 + u] * invN) * mv[u];
     }
     a.b[g * kD + tid] = (float)v;
   }
@@ -629,6 +746,7 @@ hipError_t launch_ridge(const RidgeFit& f, bool gram, bool solve, hipStream_t st
     GramArgs a{};
     a.X = (const uint16_t*)f.X;
     a.Y = (const uint16_t*)f.Y;
+    a.shift = f.shift;
     a.gram = f.gram;
     a.cross = f.cross;
     a.sums = f.sums;
@@ -637,6 +755,8 @@ hipError_t launch_ridge(const RidgeFit& f, bool gram, bool solve, hipStream_t st
     a.IN = f.IN;
     a.nF = f.IN / kGroupW;
     a.tiles = (int32_t)ridge_tiles_per_group(f.IN);
+    const int32_t nb = (f.IN + kD + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(ridge_shift_kernel, dim3((unsigned)(f.G * nb)), dim3(kThreads), 0, stream, a, nb);
     hipLaunchKernelGGL(ridge_gram_kernel, dim3((unsigned)(f.G * a.tiles)), dim3(kThreads), 0, stream, a);
   }
   if (solve) {
@@ -644,6 +764,7 @@ hipError_t launch_ridge(const RidgeFit& f, bool gram, bool solve, hipStream_t st
     s.gram = f.gram;
     s.cross = f.cross;
     s.sums = f.sums;
+    s.shift = f.shift;
     s.M = f.M;
     s.W = f.W;
     s.b = f.b;

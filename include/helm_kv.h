@@ -302,10 +302,17 @@ int helm_kv_cosine(const void* k_mapped, const void* v_mapped,
  * independent groups g (one (target layer, head, K|V) map each), with
  * observations X[g] [N, IN] and targets Y[g] [N, D]:
  *   W[g] = (Xc^T Xc + lambda I)^-1 Xc^T Yc,   b[g] = mean(Y[g]) - mean(X[g]) W[g]
- * (Xc, Yc = the data minus its column means).  X^T X and X^T Y are
- * accumulated in fp32 on the matrix cores (bf16 products are exact), the
+ * (Xc, Yc = the data minus its column means).  Each feature is first
+ * shifted by a value taken from the group's first observations: its first
+ * value when its first min(N, 64) values share one sign and lie within a
+ * factor 1.5 of each other, else 0 (a mean large against the spread would
+ * otherwise cost about (mean / spread)^2 * 2^-24 of relative accuracy in
+ * the centring of fp32 sums).  The products of the shifted data (each
+ * difference exact in bf16 when within a factor 2 of its shift, else
+ * rounded to bf16 once) are accumulated in fp32 on the matrix cores, the
  * column sums in fp32 on the vector ALU; the centring, lambda, the Cholesky
- * solve and b are fp64; W and b are stored as fp32.
+ * solve and b (with the means = shifts + sums / N) are fp64; W and b are
+ * stored as fp32.
  *   X : [n_groups, n_obs, in_features] bf16, device, 16-byte aligned
  *   Y : [n_groups, n_obs, out_features] bf16, device, 16-byte aligned
  *   W : [n_groups, in_features, out_features] fp32 (in-major, the layout of
@@ -330,8 +337,8 @@ typedef struct {
   size_t workspace_bytes;
 } helm_ridge_shape_t;
 /* Workspace bytes of a fit (0 on an invalid shape): the fp32 products
- * [G, IN, IN] and [G, IN, D], the sums [G, IN + D] and the fp64 solve
- * matrix [G, IN, IN + D] (1,024 groups of IN = 512: 4.2 GB). */
+ * [G, IN, IN] and [G, IN, D], the sums and the shifts [G, IN + D] each and
+ * the fp64 solve matrix [G, IN, IN + D] (1,024 groups of IN = 512: 4.2 GB). */
 size_t helm_ridge_workspace_bytes(const helm_ridge_shape_t* shape);
 int helm_ridge_fit(const void* X, const void* Y, float* W, float* b, const helm_ridge_shape_t* shape);
 /* The fit in two separately enqueued stages: HELM_STAGE_TABLES (1) the

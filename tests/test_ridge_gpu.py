@@ -76,8 +76,17 @@ def check(X, Y, W, b, lam, label, groups=None, oracle_groups=None):
 
 def hk_shift(x, y):
     """The per-feature shifts the library subtracts before its fp32 products
-    (include/helm_kv.h, helm_ridge_fit): none."""
-    return dict(shift_x=None, shift_y=None)
+    (include/helm_kv.h, helm_ridge_fit): a feature's first value when its
+    first min(N, 64) values share one sign and lie within a factor 1.5 of
+    each other, else 0 (the comparisons in fp32, as the library makes them;
+    every value here is a bf16 number, so they are exact)."""
+    def rule(a):
+        head = a[:64].astype(np.float32)
+        lo, hi, first = head.min(axis=0), head.max(axis=0), head[0]
+        k = np.float32(1.5)
+        tight = ((lo > 0) & (hi <= k * lo)) | ((hi < 0) & (lo >= k * hi))
+        return np.where(tight, first, np.float32(0)).astype(np.float64)
+    return dict(shift_x=rule(x), shift_y=rule(y))
 
 
 def fit(X, Y, lam):
@@ -167,3 +176,33 @@ def test_ridge_one_row_in_the_last_step():
     read zeros)."""
     X, Y = draw(3, 65, 256, 9)
     check(X, Y, *fit(X, Y, 0.01), 0.01, "ridge G3 N65 IN256")
+
+
+def test_ridge_large_means():
+    """Features and targets whose means are 30 to 100 times their spread.
+    Sums of raw products lose about (mean / std)^2 * 2^-24 of relative
+    accuracy to cancellation in the centring (up to 6e-4 here); the library
+    shifts such features by their first observation before the products, so
+    the fit must meet the bound of the shifted data.  The bound a library
+    without the shift would need is logged beside it."""
+    G, N, IN = 2, 20000, 256
+    g = torch.Generator(device="cuda").manual_seed(11)
+    sd = 0.5
+    ratio = 30.0 + 70.0 * torch.rand((G, 1, IN), generator=g, device="cuda")
+    sign = torch.where(torch.rand((G, 1, IN), generator=g, device="cuda") < 0.5, -1.0, 1.0)
+    X = (sd * torch.randn((G, N, IN), generator=g, device="cuda") + sign * ratio * sd).to(torch.bfloat16)
+    Wt = torch.randn((G, IN, 128), generator=g, device="cuda") / IN ** 0.5
+    bt = 40.0 + torch.randn((G, 1, 128), generator=g, device="cuda")
+    Y = (torch.bmm(X.float(), Wt) + bt + 0.05 * torch.randn((G, N, 128), generator=g, device="cuda"))
+    Y = Y.to(torch.bfloat16)
+    W, b = fit(X, Y, 0.01)
+    xs, ys = parity.to_np_storage(X), parity.to_np_storage(Y)
+    shifted = 0
+    for gi in range(G):
+        x, y = parity.storage_to_f64(xs[gi]), parity.storage_to_f64(ys[gi])
+        sh = hk_shift(x, y)
+        shifted += int((sh["shift_x"] != 0).sum())
+        plain = ridge_check.check_fit(x, y, W[gi].double().cpu().numpy(), b[gi].double().cpu().numpy(), 0.01)
+        log(f"ridge large means group {gi}: bound without shifts tol_rel {plain['tol_rel']:.3g}")
+    assert shifted >= G * IN * 0.95, f"only {shifted} of {G * IN} features shifted"
+    check(X, Y, W, b, 0.01, "ridge G2 N20000 IN256 mean/std 30-100")
