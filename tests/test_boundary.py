@@ -257,7 +257,7 @@ def test_ridge_workspace_and_refusals():
     L = hk.lib()
     s = hk.ridge_shape(1024, 131072, 512)
     n = hk.helm_ridge_workspace_bytes(s)
-    assert n == 1024 * (512 * 512 * 4 + 512 * 128 * 4 + 640 * 4 + 512 * 640 * 8)
+    assert n == 1024 * (512 * 512 * 4 + 512 * 128 * 4 + 640 * 8 + 512 * 640 * 8)   # sums and shifts: 640 * 4 each
     fake = [ctypes.c_void_p((1 << 40) * (i + 1)) for i in range(4)]     # far apart: no overlaps
     assert L.helm_ridge_fit(*fake, ctypes.byref(hk.ridge_shape(2, 100, 256, dtype=hk.HELM_F32))) == 5
     assert "bf16" in hk.helm_last_error()
