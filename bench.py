@@ -352,7 +352,7 @@ def ridge_leg(hk, synth, w, groups, steps, stream):
     import torch
     dev = torch.device("cuda:0")
     N, IN, D = 131072, w.k * w.head_dim, w.head_dim
-    per_group = N * (IN + D) * 2 + IN * IN * 4 + IN * D * 4 + (IN + D) * 4 + IN * (IN + D) * 8 + IN * D * 4 + D * 4
+    per_group = N * (IN + D) * 2 + IN * IN * 4 + IN * D * 4 + (IN + D) * 8 + IN * (IN + D) * 8 + IN * D * 4 + D * 4
     free, total = torch.cuda.mem_get_info(dev)
     # headroom beyond the leg's own tensors: the input draws' 6 GiB of
     # temporaries, and device memory that tools attached to the process

@@ -58,8 +58,11 @@
 //     phase issues the same operations, and the waits the compiler derives
 //     are exactly for data that has had its pipeline depth to arrive.
 //   * Bias as the products' initial accumulator (exact fp32, no extra work).
-//   * W is staged through LDS as stored and turned into A fragments with the
-//     transposing ds_read_b64_tr_b16.
+//   * W is staged through LDS as stored (32 rows a step, two buffers, the
+//     global loads three steps ahead, so that an item pays about one memory
+//     latency for its 256 KB of maps: at 512 tokens the staging is most of
+//     an item) and turned into A fragments with the transposing
+//     ds_read_b64_tr_b16.
 #include "internal.hpp"
 #include "lds_dma.hpp"
 
@@ -86,6 +89,7 @@ constexpr int kRowBytes = kD * 2;
 constexpr int kOtRow = kD + 8;   // LDS output row (bf16), 16-byte pad
 constexpr int kTabTile = kTile * kHalf;   // float2 entries of one tile's table
 constexpr int kStageRows = 32;   // W rows staged per pass (one product step)
+constexpr int kStageRow = kD + 8;  // a staged W row (bf16), 16-byte pad
 // Byte offset past every descriptor's range: loads there return zero and
 // stores are dropped (descriptor ranges stay below it; adding < 256 cannot wrap).
 constexpr uint32_t kMaxRange = 0xffffff00u;
@@ -158,7 +162,7 @@ struct Smem {
   static constexpr int SLOT = kTile * Cfg<KSEL>::ROW + 64;   // a slot's tile + 128-byte offset
   union {
     __bf16 act[2][2 * SLOT];                    // [tile parity][slot, token, feature]
-    __bf16 stage[2][kStageRows * kD];           // W staging: [slot][row][column]
+    __bf16 stage[2][2][kStageRows * kStageRow]; // W staging: [buffer][slot][row][column]
   };
   __bf16 ot[2][2][kTile * kOtRow];              // [tile parity][slot][token][column]
   float2 ct[3][kTabTile];                       // target (cos, sin) of a tile, by tile index mod 3
@@ -286,10 +290,10 @@ __device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l0, int
   {
     const int64_t grp[2] = {(int64_t)(act_slot[0] ? lay[0] : 0) * a.H + h,
                             (int64_t)(act_slot[1] ? lay[1] : 0) * a.H + h};
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      // rows 32 s .. 32 s + 31 of both slots' W: 1,024 pieces of 16 bytes
-      u32x4 v[4];
+    // rows 32 s .. 32 s + 31 of both slots' W: 1,024 pieces of 16 bytes,
+    // four a thread; loaded three steps ahead, so that the item pays one
+    // memory latency instead of one a step
+    auto load_step = [&](int s, u32x4* v) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int c = tid + kThreads * u;
@@ -297,13 +301,23 @@ __device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l0, int
         const u32x4* g = (const u32x4*)(Wt + (grp[sl] * C::KD + kStageRows * s + row) * kD + 8 * c16);
         v[u] = act_slot[sl] ? *g : u32x4{0u, 0u, 0u, 0u};
       }
-      lds_barrier();                                 // the staging area is free
+    };
+    constexpr int PD = 3;
+    u32x4 v[PD][4];
+#pragma unroll
+    for (int d = 0; d < PD; ++d)
+      if (d < S) load_step(d, v[d]);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      // staging buffer s % 2 was last read at step s - 2, before the
+      // barrier of step s - 1
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int c = tid + kThreads * u;
         const int sl = c >> 9, row = (c >> 4) & 31, c16 = c & 15;
-        *(u32x4*)&sm.stage[sl][row * kD + 8 * c16] = v[u];
+        *(u32x4*)&sm.stage[s & 1][sl][row * kStageRow + 8 * c16] = v[s % PD][u];
       }
+      if (s + PD < S) load_step(s + PD, v[s % PD]);
       lds_barrier();
       // A fragment of block b: lane l gets W[32 s + 8 lg + 0..7][col + ln];
       // within a 16-lane group lane 4e + qq names row (.. + e) and columns
@@ -312,9 +326,9 @@ __device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l0, int
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int row = 8 * lg + e, col = 32 * hc + 16 * (b & 1) + 64 * (b >> 1) + 4 * qq;
-        const __bf16* p = &sm.stage[lam][row * kD + col];
+        const __bf16* p = &sm.stage[s & 1][lam][row * kStageRow + col];
         const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * kD));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * kStageRow));
         wf[s][b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
