@@ -89,7 +89,10 @@ struct Workspace {
 };
 
 bool workspace_layout(int64_t n_tok, int32_t D, bool paged, Workspace& w) {
-  if (n_tok > INT64_MAX / 2) return false;
+  // the tables' entries, (n_tok rounded up to a block) * D/2, must not
+  // overflow before their byte count is checked
+  const int64_t per_block = (int64_t)helm::kRopeBlock * (D / 2) * (int64_t)sizeof(float2);
+  if (n_tok < 0 || n_tok / helm::kRopeBlock + 1 > INT64_MAX / per_block) return false;
   int64_t rb = helm::rope_table_entries(n_tok, D / 2);
   if (!mul_ok(rb, (int64_t)sizeof(float2))) return false;
   w.rope_bytes = align_up((size_t)rb);
