@@ -28,13 +28,22 @@ rope_tables_kernel(const int32_t* __restrict__ src_pos, const int32_t* __restric
                    float2* __restrict__ rope_src, float2* __restrict__ rope_tgt) {
   const int64_t total = n_tok * half;
   const double inv_d = -1.0 / (double)half;   // -2i/D = -i/half
-  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * kThreads) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  // A thread's pair index stays fixed across its grid-stride steps when the
+  // stride is a multiple of half (D = 64, 128, ...): its two frequencies
+  // are then evaluated once; otherwise again for every element.
+  const bool fixed_i = half > 0 && stride % half == 0;
+  int32_t i_w = -1;
+  double w_s = 0.0, w_t = 0.0;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
     const int64_t t = e / half;
     const int32_t i = (int32_t)(e - t * half);
-    const double ex = inv_d * (double)i;
-    const double w_s = pow(theta_src, ex);
-    const double w_t = pow(theta_tgt, ex);
+    if (!fixed_i || i != i_w) {
+      const double ex = inv_d * (double)i;
+      w_s = pow(theta_src, ex);
+      w_t = pow(theta_tgt, ex);
+      i_w = i;
+    }
     double s, c;
     sincos((double)src_pos[t] * w_s, &s, &c);
     rope_src[rope_src_index(t, i, half)] = make_float2((float)c, (float)s);
@@ -88,7 +97,10 @@ hipError_t launch_rope_tables(const int32_t* src_pos, const int32_t* tgt_pos, in
                               float2* rope_src, float2* rope_tgt, hipStream_t stream) {
   if (n_tok <= 0) return hipSuccess;
   const int32_t half = D / 2;
-  hipLaunchKernelGGL(rope_tables_kernel, dim3(grid_for(n_tok * half)), dim3(kThreads), 0, stream,
+  // at most 2,048 workgroups (8 per CU): each thread then takes several
+  // tokens of one pair and evaluates that pair's frequencies once
+  const int grid = grid_for(n_tok * half) < 2048 ? grid_for(n_tok * half) : 2048;
+  hipLaunchKernelGGL(rope_tables_kernel, dim3(grid), dim3(kThreads), 0, stream,
                      src_pos, tgt_pos, n_tok, half, theta_src, theta_tgt, rope_src, rope_tgt);
   return hipGetLastError();
 }
