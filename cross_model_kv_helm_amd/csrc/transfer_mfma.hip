@@ -576,6 +576,29 @@ transfer_mfma_kernel(XferArgs a, int32_t n_lpairs, int32_t chunk_tokens, int32_t
   }
 }
 
+// Keys and values in one launch, for shapes too small to fill the chip with
+// either half: items [0, n_items) map keys, [n_items, 2 n_items) values, each
+// decoded as in transfer_mfma_kernel.  Which half a workgroup maps is uniform
+// over the workgroup.
+template <int KSEL, bool PAGED>
+__global__ void __launch_bounds__(kThreads, 1)
+transfer_mfma_kv_kernel(XferArgs a, int32_t n_lpairs, int32_t chunk_tokens, int32_t n_items) {
+  __shared__ __attribute__((aligned(16))) Smem<KSEL> sm;
+  for (int32_t it = blockIdx.x; it < 2 * n_items; it += gridDim.x) {
+    const bool keys = it < n_items;
+    const int32_t item = keys ? it : it - n_items;
+    const int32_t h = item % a.H, rest = item / a.H;
+    const int32_t lp = rest % n_lpairs, chunk = rest / n_lpairs;
+    const int32_t t_begin = chunk * chunk_tokens;
+    const int32_t t_end = (int32_t)min((int64_t)t_begin + chunk_tokens, a.n_tok);
+    if (keys)
+      transfer_item<KSEL, PAGED, true>(a, lp, lp + n_lpairs, h, t_begin, t_end, sm);
+    else
+      transfer_item<KSEL, PAGED, false>(a, lp, lp + n_lpairs, h, t_begin, t_end, sm);
+    lds_barrier();   // the next item's staging overwrites the tiles
+  }
+}
+
 // CUs of the current device, looked up once per device (safe from any thread)
 int cu_count() {
   constexpr int kDevices = 64;
@@ -607,6 +630,20 @@ int64_t pick_chunks(int64_t n_tok, int64_t base_items, int64_t slots) {
     }
   }
   return best;
+}
+
+// Whether one launch of both halves (c1 token chunks each, every item on a
+// CU of its own) is expected to finish before the two launches with c2
+// chunks.  Cost in sixteen-token tiles of the values launch: a keys tile
+// takes about 1.5 of them, and an item about 18 more for its map staging,
+// pipeline fill and drain (measured on the 28 -> 28-layer pair at 512 and
+// 2,048 tokens).
+bool fused_is_cheaper(int64_t n_tok, int64_t base, int64_t slots, int64_t c2, int64_t c1) {
+  auto tiles = [&](int64_t c) { return ((n_tok + c - 1) / c + kTile - 1) / kTile; };
+  const int64_t rounds2 = (c2 * base + slots - 1) / slots;
+  const int64_t two = rounds2 * (3 * tiles(c2) + 36) + rounds2 * (2 * tiles(c2) + 36);   // doubled units
+  const int64_t one = 3 * tiles(c1) + 36;
+  return one < two;
 }
 
 }  // namespace
@@ -642,6 +679,29 @@ hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream) {
   const int32_t np = (int32_t)n_lpairs, ct = (int32_t)chunk_tokens, ni = (int32_t)n_items;
   const bool paged = a.src_row != nullptr;
   if (paged != (a.dst_row != nullptr)) return hipErrorInvalidValue;
+  // both halves in one launch when neither fills the chip and that is cheaper
+  const int64_t c1 = slots / (2 * base);
+  if (c1 >= 1 && fused_is_cheaper(a.n_tok, base, slots, n_chunks, c1)) {
+    const int64_t ct1 = ((a.n_tok + c1 - 1) / c1 + kTile - 1) / kTile * kTile;
+    const int64_t items1 = base * ((a.n_tok + ct1 - 1) / ct1);   // <= slots / 2
+    const dim3 g1((unsigned)(2 * items1)), b1(kThreads);
+    const int32_t ct1i = (int32_t)ct1, ni1 = (int32_t)items1;
+#define HELM_LAUNCH_KV(K)                                                                         \
+  do {                                                                                            \
+    if (paged)                                                                                    \
+      hipLaunchKernelGGL((transfer_mfma_kv_kernel<K, true>), g1, b1, 0, stream, a, np, ct1i, ni1);  \
+    else                                                                                          \
+      hipLaunchKernelGGL((transfer_mfma_kv_kernel<K, false>), g1, b1, 0, stream, a, np, ct1i, ni1); \
+  } while (0)
+    switch (a.k) {
+      case 1: HELM_LAUNCH_KV(1); break;
+      case 2: HELM_LAUNCH_KV(2); break;
+      case 3: HELM_LAUNCH_KV(3); break;
+      default: HELM_LAUNCH_KV(4); break;
+    }
+#undef HELM_LAUNCH_KV
+    return hipGetLastError();
+  }
 #define HELM_LAUNCH(K)                                                                          \
   do {                                                                                          \
     if (paged) {                                                                                \
