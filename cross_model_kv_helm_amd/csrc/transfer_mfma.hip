@@ -242,7 +242,9 @@ __device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l0, int
   }
   // Row of the gathering lane's token of tile `tile` (clamped into the item:
   // rows outside it are read but never stored).  Paged caches read the slot
-  // map a phase before the rows, so the load never waits on its own index.
+  // maps two phases before their use, ahead of the phase's stores: vector
+  // memory operations complete in issue order, so waiting for a map read
+  // also waits for every older store, and those are then two phases old.
   auto src_row_of = [&](int tile) __attribute__((always_inline)) -> int32_t {
     const int32_t n = min(t_begin + tile * kTile + gt, t_end - 1);
     if constexpr (PAGED) {
@@ -424,7 +426,7 @@ __device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l0, int
 
   // ---- prologue: tile 0 gathered, tile 1 loaded, tile 2 loading, the
   // target table of tile 0 in LDS, the bias of tile 0's accumulators read
-  // (paged: the slots of tile 3's rows loading)
+  // (paged: the slots of tiles 3 and 4's rows loading)
   lds_barrier();                                     // staging reads done: the tiles may be written
   Raw<KSEL> raw[2];
   f32x4 accs[2][4];
@@ -454,7 +456,10 @@ __device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l0, int
     for (int jj = 0; jj < NJ; ++jj) load_row(r2, jj, raw[0]);
     load_cs(2, raw[0]);
   }
-  if constexpr (PAGED) srow[1] = src_row_of(3);
+  if constexpr (PAGED) {
+    srow[0] = src_row_of(3);
+    srow[1] = src_row_of(4);
+  }
 #pragma unroll
   for (int b = 0; b < 4; ++b) accs[1][b] = f32x4{0.f, 0.f, 0.f, 0.f};   // "tile -1": never stored
   load_bias(bv);
@@ -497,7 +502,7 @@ __device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l0, int
     f32x4 tq[2];
     uint32_t pk[2][4];
     f32x4 v = {};
-    const int32_t row3 = PAGED ? srow[P ^ 1] : src_row_of(i + 3);
+    const int32_t row3 = PAGED ? srow[P] : src_row_of(i + 3);
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = bv[b];
     bf16x8 xf[RA];
@@ -516,8 +521,7 @@ __device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l0, int
         turn_unit(r, jj, e, v);
       }
       if (s == 0 && PAGED) {
-        srow[P] = src_row_of(i + 4);
-        drow[P] = dst_row_of(i - 1);
+        srow[P] = src_row_of(i + 5);
       }
       if (s == kTq) load_tq(i + 1, tq);
       if (s == kCv0) epi_tables(ct_prev, 0, cv[0]);
@@ -528,7 +532,8 @@ __device__ __forceinline__ void transfer_item(const XferArgs& a, int32_t l0, int
         for (int hh = 0; hh < 2; ++hh)
           if (s == epi_step(g, hh)) epi_part(pacc, cv[g], ot_prev, g, hh, pk[g]);
       if (s == kOt) read_out(sm.ot[P], so);
-      if (s == kSt) write_out(i - 2, PAGED ? drow[P ^ 1] : dst_row_of(i - 2), so);
+      if (s == kSt) write_out(i - 2, PAGED ? drow[P] : dst_row_of(i - 2), so);
+      if (s == kSt && PAGED) drow[P] = dst_row_of(i);   // for phase i + 2's stores
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj)
         if (s == put_step(jj)) {
