@@ -46,8 +46,10 @@
 //     neither deeper rings, L2 warm-up loads nor loads staged through
 //     registers two steps ahead shortened the wait (vector memory returns in
 //     issue order).
-//   * Epilogue from registers: bias, the forward rotation at tgt_pos (keys;
-//     fp32 tables from the RoPE table kernel), round to bf16, store.
+//   * Epilogue: bias, the forward rotation at tgt_pos (keys; fp32 tables
+//     from the RoPE table kernel) and the rounding to bf16 in registers; the
+//     output tile then goes through LDS (the free operand ring), so the
+//     stores are whole 256-byte rows, 16 bytes a lane.
 #include "internal.hpp"
 #include "lds_dma.hpp"
 
@@ -295,14 +297,25 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
     lds_barrier();
   }
 
-  // ---- epilogue: this wave's map, bias, forward rotation (keys), store.
+  // ---- epilogue: bias, the forward rotation at tgt_pos (keys), bf16.  The
+  // output tile goes through LDS (the operand ring is free once the last
+  // step's barrier has passed) so that the stores are whole 256-byte rows,
+  // 16 bytes a lane.  LDS tile [map q][token row][16 pieces of 16 bytes],
+  // piece j of row r at slot j ^ (r & 15): the two halves of a wave write
+  // rows 4 apart, and one row's 16 pieces cover all banks once.
   // Accumulator register r of block (mb, nb) holds row 8*(r/4) + 4*(lane/32)
   // + r%4 of the block, column lane%32.
-  const int mi = 2 * ct + (kWaves == 4 ? wn : wn >> 1);
-  const int kind = mi / H, h = mi % H;
-  const int64_t grp = (int64_t)l * H + h;
-  const float* bias = (kind ? a.b_v : a.b_k) + grp * kD;
-  uint16_t* out = (kind ? a.out_v : a.out_k) + grp * T * kD;
+  static_assert(sizeof(GemmSmem::As) + sizeof(GemmSmem::Bs) >= 2 * kTT * kD * 2 &&
+                    offsetof(GemmSmem, Bs) == sizeof(GemmSmem::As),
+                "the output tile fits the operand ring (As then Bs)");
+  uint16_t* ot = &As[0][0];
+  auto ot_at = [](int q, int row, int d) __attribute__((always_inline)) {
+    return (q * kTT + row) * kD + 8 * ((d >> 3) ^ (row & 15)) + (d & 7);
+  };
+  const int q_w = kWaves == 4 ? wn : wn >> 1;             // the wave's map within the tile
+  const int mi_w = 2 * ct + q_w;
+  const int kind_w = mi_w / H;
+  const float* bias = (kind_w ? a.b_v : a.b_k) + ((int64_t)l * H + mi_w % H) * kD;
   const int col = lane & 31;
 #pragma unroll
   for (int nb = 0; nb < kNB / 2; ++nb) {
@@ -312,20 +325,31 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int32_t t = t0 + 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (t >= T) continue;
+        const int row = 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int32_t t = t0 + row;
+        if (t >= T) continue;                             // rows past the last token are never stored
         float ylo = acc[mb][nb][r] + blo, yhi = acc[mb][nb + kNB / 2][r] + bhi;
-        if (kind == 0) {
+        if (kind_w == 0) {
           const float2 cs = a.rope_tgt[rope_tgt_index(t, dlo, kHalf)];
           const float olo = fmaf(ylo, cs.x, -(yhi * cs.y));
           const float ohi = fmaf(yhi, cs.x, ylo * cs.y);
           ylo = olo;
           yhi = ohi;
         }
-        out[(int64_t)t * kD + dlo] = __builtin_bit_cast(uint16_t, (__bf16)ylo);
-        out[(int64_t)t * kD + dhi] = __builtin_bit_cast(uint16_t, (__bf16)yhi);
+        ot[ot_at(q_w, row, dlo)] = __builtin_bit_cast(uint16_t, (__bf16)ylo);
+        ot[ot_at(q_w, row, dhi)] = __builtin_bit_cast(uint16_t, (__bf16)yhi);
       }
     }
+  }
+  lds_barrier();
+  // the stores: piece j of row r of map q per thread, 16 threads per row
+  for (int g = tid; g < 2 * kTT * 16; g += kThreads) {
+    const int q = g / (kTT * 16), row = (g / 16) % kTT, j = g % 16;
+    const int32_t t = t0 + row;
+    if (t >= T) continue;
+    const int mi = 2 * ct + q;
+    uint16_t* out = (mi / H ? a.out_v : a.out_k) + (((int64_t)l * H + mi % H) * T + t) * kD;
+    *(u32x4*)(out + 8 * j) = *(const u32x4*)&ot[(q * kTT + row) * kD + 8 * (j ^ (row & 15))];
   }
 }
 
