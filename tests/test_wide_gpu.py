@@ -125,12 +125,15 @@ def test_wide_xcd_order_full():
 
 def test_wide_qwen3_14b_32b_t32k_sampled():
     """The benchmark's wide workload (40 -> 64 layers, 8 heads, k = 4, IN =
-    8192, 32,768 tokens) on sampled rows of every slab."""
+    8192, 32,768 tokens) on sampled rows of every slab: fixed tokens, a few
+    random ones and one random token in every 256-token tile, so every
+    (token tile, column tile) of the product's XCD-ordered schedule is
+    compared."""
     w = synth.CONFIGS["qwen3_14b_32b_t32k_wide"]
     case = WideCase(w)
     out = case.run_gpu()
     torch.cuda.synchronize()
-    rows = sample_rows(w.n_tgt_layers, w.n_kv_heads, case.T, 4, 2)
+    rows = sample_rows(w.n_tgt_layers, w.n_kv_heads, case.T, 2, 2, tile=256)
     case.check(*out, rows=rows)
 
 
