@@ -23,7 +23,9 @@
 //     RoPE tables of a tile serve both slots.  Work items are (token chunk,
 //     layer pair, head) with the head fastest: workgroups go to the 8 XCDs
 //     round robin, so with 8 heads each XCD maps one head's 64 target layers
-//     and its L2 holds that head's source rows for all of them.
+//     and its L2 holds that head's source rows for all of them.  Keys and
+//     values are two launches; when neither half fills the chip (small
+//     shapes) one launch carries both, each map staged once.
 //   * One wave per SIMD, each holding W for 64 output columns of one slot
 //     (256 registers at k = 4): columns 32c .. 32c+31 and their RoPE
 //     partners 64+32c .. 64+32c+31 (c = the wave's half), as four 16-row
