@@ -314,11 +314,12 @@ def test_paged_small_full():
     pc.check(tk, tv)
 
 
-@pytest.mark.parametrize("k", [1, 3])
-def test_paged_k1_k3_full(k):
-    """The paged instantiations for k = 1 and k = 3 (the other tests take
-    k = 2 and 4): four requests whose lengths cross 32-token tiles and
-    16-token pages unevenly, with per-request target offsets."""
+@pytest.mark.parametrize("k", [1, 3, 4])
+def test_paged_small_k1_k3_k4_full(k):
+    """The paged instantiations for k = 1, 3 and 4 on a shape small enough
+    that keys and values go into one launch (the 32-request test takes k = 4
+    through the two launches): four requests whose lengths cross 16-token
+    tiles and pages unevenly, with per-request target offsets."""
     w = synth.Workload(f"paged_k{k}", 6, 5, 2, 128, 0, k, "bf16", 1e6, "same", 40 + k, paged=True,
                        n_requests=4, max_offset=500)
     pc = PagedCase(w, lens=[33, 70, 5, 129])
