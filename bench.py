@@ -420,7 +420,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the transfer shards by KV head with no exchange, "
-              f"and this build runs on a single MI355X (got --gpus {args.gpus})", file=sys.stderr)
+              f"so one MI355X's throughput is the figure (got --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
