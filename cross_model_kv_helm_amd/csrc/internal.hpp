@@ -106,9 +106,6 @@ struct WideXfer {
   uint16_t* WT_v;
   int32_t L_s, L_t, H, D, k, T;
 };
-// Compute units of the current device (looked up once per device).
-int device_cu_count();
-
 int64_t wide_in_features(int32_t k, int32_t H, int32_t D);
 bool wide_supports(const WideXfer& x);
 // prep: the un-rotated keys and the transposed maps into the workspace

@@ -606,6 +606,19 @@ transfer_mfma_kv_kernel(XferArgs a, int32_t n_lpairs, int32_t chunk_tokens, int3
   }
 }
 
+// CUs of the current device, looked up once per device (safe from any thread)
+int cu_count() {
+  constexpr int kDevices = 64;
+  static std::atomic<int> counts[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
+  int n = counts[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // Token chunks per (layer pair, head): as many as keep every CU busy in as
 // few rounds as possible, counting a few tiles of pipeline fill and map
@@ -642,20 +655,6 @@ bool fused_is_cheaper(int64_t n_tok, int64_t base, int64_t slots, int64_t c2, in
 
 }  // namespace
 
-// CUs of the current device, looked up once per device (safe from any thread)
-int device_cu_count() {
-  constexpr int kDevices = 64;
-  static std::atomic<int> counts[kDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
-  int n = counts[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    counts[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 bool mfma_supports(const XferArgs& a) {
   // 16-byte vector loads of source rows, W and bias, 16-byte stores of
   // outputs, and the buffer descriptors' byte ranges below kMaxRange
@@ -676,7 +675,7 @@ hipError_t launch_transfer_mfma(const XferArgs& a, hipStream_t stream) {
   if (a.n_tok <= 0) return hipSuccess;
   const int64_t n_lpairs = (a.L_t + 1) / 2;
   const int64_t base = n_lpairs * a.H;
-  const int64_t slots = device_cu_count();   // one 4-wave workgroup per CU
+  const int64_t slots = cu_count();   // one 4-wave workgroup per CU
   const int64_t n_chunks = pick_chunks(a.n_tok, base, slots);
   const int64_t chunk_tokens = ((a.n_tok + n_chunks - 1) / n_chunks + kTile - 1) / kTile * kTile;
   const int64_t chunks = (a.n_tok + chunk_tokens - 1) / chunk_tokens;

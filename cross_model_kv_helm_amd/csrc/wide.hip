@@ -473,7 +473,12 @@ hipError_t launch_wide(const WideXfer& x, bool prep, bool product, hipStream_t s
   a.n_ct = (2 * x.H * kD) / kCT;   // = H
   const int64_t n_tiles = (int64_t)x.L_t * a.n_tt * a.n_ct;
   if (n_tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int64_t grid = n_tiles < device_cu_count() ? n_tiles : device_cu_count();
+  // one workgroup per CU (a microsecond query next to a ~60 ms launch)
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t grid = n_tiles < cus ? n_tiles : cus;
   hipLaunchKernelGGL(wide_gemm_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
