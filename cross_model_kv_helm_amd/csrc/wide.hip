@@ -67,6 +67,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef lds::u32x4 u32x4;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kMaxRange = 0xffffff00u;   // largest buffer range used (offsets below it never wrap)
+
+// A buffer descriptor from workgroup-uniform values (kept in scalar registers).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* q = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
 
 constexpr int kD = 128;
 constexpr int kHalf = 64;
@@ -317,23 +329,43 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
   const int mi_w = 2 * ct + q_w;
   const int kind_w = mi_w / H;
   const float* bias = (kind_w ? a.b_v : a.b_k) + ((int64_t)l * H + mi_w % H) * kD;
-  const int col = lane & 31;
+  const int col = lane & 31, hl = lane >> 5;
+  // Key maps: the (cos, sin) of the forward rotation for the lane's 16 rows of
+  // a 32-row block are read from the tile's slice of the target table through
+  // a buffer descriptor and issued together before the block's arithmetic (a
+  // read per element, each waited for before the next, made the epilogue of a
+  // key tile tens of microseconds).  In rope_tgt_index's layout the lane's
+  // pair i = dlo and rows 8(r/4) + 4 hl + r%4 of a block that starts at a
+  // multiple of 32 tokens sit at a per-lane base plus a constant per r.  Rows
+  // past the table read zeros; rows past the last token are computed but
+  // never stored.
+  const int64_t tab_entries = (int64_t)((T + kRopeBlock - 1) / kRopeBlock) * kRopeBlock * kHalf;   // the table's size
+  const int64_t tab_left = (tab_entries - (int64_t)t0 * kHalf) * (int64_t)sizeof(float2);
+  const rsrc_t tab = make_rsrc(a.rope_tgt + (int64_t)t0 * kHalf, (uint32_t)(tab_left < kMaxRange ? tab_left : kMaxRange));
 #pragma unroll
   for (int nb = 0; nb < kNB / 2; ++nb) {
     const int dlo = (kWaves == 4 ? 32 * nb : 32 * (wn & 1)) + col, dhi = dlo + kHalf;
     const float blo = bias[dlo], bhi = bias[dhi];
+    const uint32_t lane_tab =
+        (uint32_t)((dlo >> 2) * 64 + ((dlo & 3) >> 1) * 32 + 8 * hl + (dlo & 1)) * (uint32_t)sizeof(float2);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
+      f32x2 cs[16];
+      if (kind_w == 0) {
+        const uint32_t blk = lane_tab + (uint32_t)((128 * wm + 32 * mb) * kHalf * sizeof(float2));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t e = (uint32_t)((r >> 3) * kRopeBlock * kHalf + 16 * ((r >> 2) & 1) + 2 * (r & 3));
+          cs[r] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(tab, blk + e * (uint32_t)sizeof(float2), 0, 0));
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int32_t t = t0 + row;
-        if (t >= T) continue;                             // rows past the last token are never stored
+        const int row = 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
         float ylo = acc[mb][nb][r] + blo, yhi = acc[mb][nb + kNB / 2][r] + bhi;
         if (kind_w == 0) {
-          const float2 cs = a.rope_tgt[rope_tgt_index(t, dlo, kHalf)];
-          const float olo = fmaf(ylo, cs.x, -(yhi * cs.y));
-          const float ohi = fmaf(yhi, cs.x, ylo * cs.y);
+          const float olo = fmaf(ylo, cs[r].x, -(yhi * cs[r].y));
+          const float ohi = fmaf(yhi, cs[r].x, ylo * cs[r].y);
           ylo = olo;
           yhi = ohi;
         }
