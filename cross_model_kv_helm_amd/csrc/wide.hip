@@ -435,18 +435,42 @@ unrotate_keys_kernel(const uint16_t* __restrict__ src_k, const float2* __restric
 }
 
 // W [G, IN, D] -> WT [G, D, IN] through a 64 x 64 LDS tile per block:
-// grid (IN / 64, D / 64, G).
+// grid (IN / 64, D / 64, G).  VEC (W 16-byte aligned): every global access is
+// 16 bytes (8 threads a 128-byte row segment), the tile's rows padded to 16-
+// byte multiples; otherwise 2-byte accesses.
+template <bool VEC>
 __global__ void __launch_bounds__(256)
 transpose_w_kernel(const uint16_t* __restrict__ W, int32_t IN, uint16_t* __restrict__ WT) {
-  __shared__ uint16_t tile[64][66];
   const int64_t g = blockIdx.z;
   const int m0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
   const uint16_t* src = W + g * (int64_t)IN * kD;
   uint16_t* dst = WT + g * (int64_t)kD * IN;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) tile[r][tx] = src[(int64_t)(m0 + r) * kD + d0 + tx];
-  __syncthreads();
-  for (int r = ty; r < 64; r += 4) dst[(int64_t)(d0 + r) * IN + m0 + tx] = tile[tx][r];
+  if constexpr (VEC) {
+    constexpr int kP = 72;   // padded row (elements)
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kP];
+    const int c = threadIdx.x & 7, r = threadIdx.x >> 3;   // piece c of rows r, r + 32
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int rr = r + 32 * k;
+      *(u32x4*)&tile[rr * kP + 8 * c] = *(const u32x4*)(src + (int64_t)(m0 + rr) * kD + d0 + 8 * c);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int d = r + 32 * k;   // output row d0 + d: inputs m0 + 8c .. m0 + 8c + 7
+      u32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = (uint32_t)tile[(8 * c + 2 * j) * kP + d] | ((uint32_t)tile[(8 * c + 2 * j + 1) * kP + d] << 16);
+      *(u32x4*)(dst + (int64_t)(d0 + d) * IN + m0 + 8 * c) = v;
+    }
+  } else {
+    __shared__ uint16_t tile[64][66];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int r = ty; r < 64; r += 4) tile[r][tx] = src[(int64_t)(m0 + r) * kD + d0 + tx];
+    __syncthreads();
+    for (int r = ty; r < 64; r += 4) dst[(int64_t)(d0 + r) * IN + m0 + tx] = tile[tx][r];
+  }
 }
 
 int grid_for(int64_t work) {
@@ -477,10 +501,15 @@ hipError_t launch_wide(const WideXfer& x, bool prep, bool product, hipStream_t s
     hipLaunchKernelGGL(unrotate_keys_kernel, dim3(grid_for(rows * 8)), dim3(256), 0, stream,
                        (const uint16_t*)x.src_k, x.rope_src, rows, x.T, x.U);
     // pre-pass 2: every map's W transposed to [D, IN]
-    hipLaunchKernelGGL(transpose_w_kernel, dim3(IN / 64, kD / 64, (unsigned)G), dim3(256), 0, stream,
-                       (const uint16_t*)x.W_k, IN, x.WT_k);
-    hipLaunchKernelGGL(transpose_w_kernel, dim3(IN / 64, kD / 64, (unsigned)G), dim3(256), 0, stream,
-                       (const uint16_t*)x.W_v, IN, x.WT_v);
+    const dim3 tg(IN / 64, kD / 64, (unsigned)G);
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* Wm = (const uint16_t*)(kv ? x.W_v : x.W_k);
+      uint16_t* WTm = kv ? x.WT_v : x.WT_k;
+      if ((uintptr_t)Wm % 16 == 0)
+        hipLaunchKernelGGL(transpose_w_kernel<true>, tg, dim3(256), 0, stream, Wm, IN, WTm);
+      else
+        hipLaunchKernelGGL(transpose_w_kernel<false>, tg, dim3(256), 0, stream, Wm, IN, WTm);
+    }
   }
   if (!product) return hipGetLastError();
   // the product with its epilogue

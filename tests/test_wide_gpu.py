@@ -182,3 +182,29 @@ def test_wide_invalid_device_layer_sel_leaves_target_layer_unwritten(bad, value)
                            for l in good for h in range(w.n_kv_heads)])
     case.host["layer_sel"] = np.where((sel < 0) | (sel >= w.n_src_layers), 0, sel).astype(np.int32)
     case.check(*out, rows=rows, label="valid rows of ")
+
+
+def test_wide_maps_not_16_byte_aligned_full():
+    """W_k and W_v in buffers offset by one element (not 16-byte aligned):
+    the preparation transposes them with 2-byte accesses instead of 16-byte
+    ones; the outputs are the same as from aligned maps, bit for bit, and
+    within the tolerance of the oracle."""
+    import cross_model_kv_helm_amd as hk
+    case = WideCase(W("wide_misaligned_w", 5, 3, 2, 128, 300, 2, "bf16", 1e6, "shift4096", 67))
+    d, w = case.dev, case.w
+    aligned = case.run_gpu()
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+    Wk, Wv = shifted(d["W_k"]), shifted(d["W_v"])
+    assert Wk.data_ptr() % 16 != 0 and Wv.data_ptr() % 16 != 0
+    out = (torch.full_like(aligned[0], float("nan")), torch.full_like(aligned[1], float("nan")))
+    s = hk.make_shape(d["src_k"], Wk, d["layer_sel"], w.theta, w.theta)
+    hk.helm_kv_transfer_wide(d["src_k"], d["src_v"], d["src_pos"], d["tgt_pos"], d["layer_sel"], Wk, d["b_k"],
+                             Wv, d["b_v"], out[0], out[1], s)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], aligned[0]) and torch.equal(out[1], aligned[1])
+    case.check(*out)
