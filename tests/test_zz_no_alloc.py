@@ -2,7 +2,8 @@
 its outputs equal helm_kv_transfer's bit for bit on two calls in a row, the
 second with a smaller input (the static scratch keeps the first call's
 tables, which the second must not read), and both match the oracle.  A call
-beyond the scratch's limit is refused before anything is enqueued.
+beyond the scratch's limit is refused before anything is enqueued, and the
+call captured in a HIP graph replays bit for bit.
 """
 import dataclasses
 
@@ -74,3 +75,40 @@ def test_noalloc_limit_refused_before_any_work():
     torch.cuda.synchronize()
     assert bool((out == 5.0).all()) and bool((out2 == 5.0).all())
     del w
+
+
+def test_noalloc_captured_in_a_graph_replays_bit_for_bit():
+    """The call captured in a HIP graph (torch.cuda.CUDAGraph) on torch's
+    capture stream, for callers that record their work as graphs: three
+    replays, with the outputs overwritten in between, reproduce the eager
+    call bit for bit (nothing in the call allocates or clears memory)."""
+    import cross_model_kv_helm_amd as hk
+    w = dataclasses.replace(synth.CONFIGS["qwen3_0.6b_1.7b_t512"], name="graph", n_src_layers=6, n_tgt_layers=5,
+                            positions="shift4096", seed=93)
+    case = Case(w)
+    d = case.dev
+    shape = (w.n_tgt_layers, w.n_kv_heads, case.T, w.head_dim)
+    out = (torch.empty(shape, dtype=torch.bfloat16, device="cuda"),
+           torch.empty(shape, dtype=torch.bfloat16, device="cuda"))
+
+    def call():
+        s = hk.make_shape(d["src_k"], d["W_k"], d["layer_sel"], w.theta, w.theta)   # stream: the current one
+        hk.helm_kv_transfer_noalloc(d["src_k"], d["src_v"], d["src_pos"], d["tgt_pos"], d["layer_sel"], d["W_k"],
+                                    d["b_k"], d["W_v"], d["b_v"], out[0], out[1], s)
+
+    call()                       # eager: the first call looks up the static scratch's device address
+    torch.cuda.synchronize()
+    ref = (out[0].clone(), out[1].clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out[0].fill_(float("nan"))
+        out[1].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out[0].view(torch.int16), ref[0].view(torch.int16)), f"replay {rep}: K"
+        assert torch.equal(out[1].view(torch.int16), ref[1].view(torch.int16)), f"replay {rep}: V"
+    log(f"{w.name}: 3 graph replays bit-identical to the eager call")
