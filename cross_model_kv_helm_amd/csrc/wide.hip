@@ -28,8 +28,9 @@
 //     waves of 128 x 128 run at the same speed with twice the registers.)
 //   * Operand tiles of 64 k-values reach LDS by buffer->LDS DMA (16 bytes
 //     per lane, no registers in between), double-buffered: the copies of
-//     step s+1 are issued between the first 32 products of step s (one
-//     after every other product) and land while the rest run.  (The ring
+//     step s+1 are issued by four of the eight waves (one per SIMD), one
+//     after each of their first 16 products of step s, and land while the
+//     rest run.  (The ring
 //     depth and step size are parameters; deeper rings of 32-value steps
 //     measured slower: one barrier per 32 products instead of 64.)  A lane
 //     chooses which 16-byte piece it copies, so the tiles are stored
@@ -93,7 +94,8 @@ constexpr int kNB = 16 / kWaves;  // 32-column accumulator blocks per wave
 constexpr int kRowPieces = kKB * 2 / 16;   // 16-byte pieces per tile row and step
 constexpr int kSwz = 16 / kRowPieces;      // rows sharing one swizzle pattern
 constexpr int kRowsPerCopy = 64 / kRowPieces;   // tile rows per 1 KB copy instruction
-constexpr int kPer = 4 * kRowPieces / kWaves;   // copy instructions per wave, operand and step (tile / waves / 1 KB)
+constexpr int kCopyWaves = 4;     // waves that issue the operand copies: 0..3, one per SIMD
+constexpr int kPer = 4 * kRowPieces / kCopyWaves;   // copy instructions per copying wave, operand and step (tile / waves / 1 KB)
 constexpr int kMfmaPerStep = (kKB / 16) * 4 * kNB;
 constexpr int kCopyStride = kMfmaPerStep / 2 / (2 * kPer) > 0 ? kMfmaPerStep / 2 / (2 * kPer) : 1;   // copies spread over half a step
 static_assert(kKB % 16 == 0 && 16 % kRowPieces == 0 && kBufs >= 2 && kBufs <= 5 && (kBufs - 2) * 2 * kPer < 64, "pipeline shape");
@@ -178,8 +180,11 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
   const uint32_t map_bytes = (uint32_t)kD * IN * 2;
   const int n_steps = IN / kKB;
 
-  // ---- operand copies: wave w issues the A and B copy instructions i =
-  // w, w+4, w+8, ...; instruction i covers kRowsPerCopy tile rows from
+  // ---- operand copies: wave w < kCopyWaves issues the A and B copy
+  // instructions i = w, w+4, w+8, ... (the other wave of each SIMD issues
+  // none, so one wave per SIMD keeps issuing products while its partner
+  // waits to issue copies: 58.7-59.1 ms against 59.6-60.2 ms with all eight
+  // waves copying; two copying waves ran 65-68 ms); instruction i covers kRowsPerCopy tile rows from
   // kRowsPerCopy*i on, lane q the row kRowsPerCopy*i + q/kRowPieces and slot
   // q % kRowPieces of it (so the piece that swizzles to that slot).  The
   // per-lane byte offsets do not depend on the step; the step's part (which
@@ -189,10 +194,11 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
   // take the same pieces (the swizzle term repeats every 16*kSwz rows), so
   // one per-lane offset per operand serves all: A adds the row step (and
   // skips rows past T), B folds it, modulo one map, into the scalar offset.
-  constexpr int kRowStep = kWaves * kRowsPerCopy;                // rows between a wave's instructions
+  constexpr int kRowStep = kCopyWaves * kRowsPerCopy;            // rows between a wave's instructions
   constexpr int kMapWraps = kD / kRowStep;                       // instructions per map (B)
   static_assert((16 * kSwz) % kRowStep == 0 || kRowStep % (16 * kSwz) == 0, "swizzle period");
-  const int r0 = kRowsPerCopy * w + lane / kRowPieces;
+  const int wc = w % kCopyWaves;                                 // (the copying waves' layout)
+  const int r0 = kRowsPerCopy * wc + lane / kRowPieces;
   const int c0 = (lane % kRowPieces) ^ ((r0 / kSwz) % kRowPieces);
   const uint32_t voff_a0 = (uint32_t)(t0 + r0) * (kD * 2) + 16 * c0;
   const uint32_t a_lim = (uint32_t)T * (kD * 2);                 // first byte past the last token
@@ -214,15 +220,16 @@ __device__ __forceinline__ void gemm_tile(const WideArgs& a, int64_t m, GemmSmem
   // A instruction q, else its B instruction q-kPer (the first half of the B
   // instructions covers map 0, the second map 1)
   auto copy_one = [&](int s, int p, int q, const u32x4& ra) __attribute__((always_inline)) {
+    if (w >= kCopyWaves) return;   // wave-uniform
     if (q < kPer) {
       const uint32_t va = voff_a0 + (uint32_t)(q * kRowStep * kD * 2);
       dma16(ra, va < a_lim ? va : kSkip, (uint32_t)(s % kStepsPerBlock) * (kKB * 2),   // (kSkip + 192 stays past every range)
-            (const char*)As[p] + 1024 * (w + kWaves * q));
+            (const char*)As[p] + 1024 * (wc + kCopyWaves * q));
     } else {
       const int n = q - kPer;
       dma16(rs_b[n >= kPer / 2 ? 1 : 0], voff_b0,
             (uint32_t)s * (kKB * 2) + (uint32_t)((n % kMapWraps) * kRowStep) * (uint32_t)IN * 2,
-            (const char*)Bs[p] + 1024 * (w + kWaves * n));
+            (const char*)Bs[p] + 1024 * (wc + kCopyWaves * n));
     }
   };
 
