@@ -677,6 +677,9 @@ int helm_kv_transfer_wide_stage(int stages, const void* src_k, const void* src_v
   x.WT_v = (uint16_t*)(ws + 2 * w.rope_bytes + w.u_bytes + w.wt_bytes);
   x.L_s = s->n_src_layers; x.L_t = s->n_tgt_layers; x.H = s->n_kv_heads; x.D = s->head_dim; x.k = s->k;
   x.T = (int32_t)s->n_tokens;
+  if ((uintptr_t)out_k % 16 || (uintptr_t)out_v % 16)
+    return fail(HELM_E_INVALID_ARG, "the wide-input map stores 16-byte pieces: out_k %p and out_v %p must be 16-byte aligned",
+                out_k, out_v);
   if (!helm::wide_supports(x))
     return fail(HELM_E_INVALID_ARG, "the wide-input map needs 16-byte aligned caches and a cache slab below 4 GB");
   rc = device_gate(-1);

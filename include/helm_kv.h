@@ -234,8 +234,10 @@ int helm_kv_transfer_paged(const void* src_k_pool, const void* src_v_pool,
  * except:
  *   W_k, W_v : [L_t, H, IN, D] bf16 (in-major)
  *   dtype    : HELM_BF16 only (HELM_E_DTYPE otherwise); head_dim 128 only
- *              (HELM_E_PAIR_SHAPE otherwise); every tensor and the workspace
- *              16-byte aligned (HELM_E_INVALID_ARG otherwise)
+ *              (HELM_E_PAIR_SHAPE otherwise); src_k, src_v, out_k and out_v
+ *              16-byte aligned (HELM_E_INVALID_ARG otherwise); W_k and W_v
+ *              need only their elements' alignment (16-byte aligned maps are
+ *              transposed with 16-byte accesses, others with 2-byte ones)
  *   workspace: helm_kv_wide_workspace_bytes(shape) bytes, 256-byte aligned;
  *              it holds the RoPE tables, the un-rotated source keys
  *              [L_s, H, T, D] and both maps transposed [L_t, H, D, IN]

@@ -247,6 +247,15 @@ def test_wide_map_workspace_and_refusals():
         assert L.helm_kv_transfer_wide_stage(stages, *fake, ctypes.byref(s)) == 7
     for stages in (0, 4, -1):
         assert L.helm_kv_transfer_wide_stage(stages, *fake, ctypes.byref(s)) == 1
+    # outputs not 16-byte aligned: refused (the epilogue stores 16-byte pieces), before any device access
+    ws_s = shape(n_tokens=64)
+    ws_s.workspace = ctypes.c_void_p(1 << 40)
+    ws_s.workspace_bytes = hk.helm_kv_wide_workspace_bytes(ws_s)
+    for bad in (9, 10):                                                       # out_k, out_v
+        args = list(fake)
+        args[bad] = ctypes.c_void_p(args[bad].value + 2)
+        assert L.helm_kv_transfer_wide(*args, ctypes.byref(ws_s)) == 1
+        assert "16-byte aligned" in hk.helm_last_error()
 
 
 def test_ridge_workspace_and_refusals():
