@@ -208,3 +208,25 @@ def test_wide_maps_not_16_byte_aligned_full():
     torch.cuda.synchronize()
     assert torch.equal(out[0], aligned[0]) and torch.equal(out[1], aligned[1])
     case.check(*out)
+
+
+def test_wide_131k_tokens_shifted_sampled():
+    """The 14B -> 32B wide shape at 131,072 tokens with target positions
+    shifted by 4,096 (positions up to 135,167; 512 token tiles a layer on the
+    persistent grid, the epilogue's table slice at token offsets up to
+    130,816): 24 slabs (the first and last target layer's 8 heads and 8 more
+    spread over the rest), one random token in every 256-token tile of each
+    plus fixed tokens, against the oracle."""
+    w = dataclasses.replace(synth.CONFIGS["qwen3_14b_32b_t32k_wide"], name="wide_t128k_shift", n_tokens=131072,
+                            positions="shift4096", seed=312)
+    case = WideCase(w)
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    H, T = w.n_kv_heads, case.T
+    rng = np.random.default_rng(5)
+    slabs = sorted(set(list(range(H)) + list(range((w.n_tgt_layers - 1) * H, w.n_tgt_layers * H)) +
+                       rng.choice(np.arange(H, (w.n_tgt_layers - 1) * H), 8, replace=False).tolist()))
+    starts = np.arange(0, T, 256)
+    toks = np.unique(np.concatenate([starts + rng.integers(0, 256, starts.size), [0, 1, 65535, 65536, T - 1]]))
+    rows = np.concatenate([g * T + toks for g in slabs]).astype(np.int64)
+    case.check(*out, rows=rows)
