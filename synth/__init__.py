@@ -270,13 +270,12 @@ def slot_index(lay: PagedLayout, table: np.ndarray) -> np.ndarray:
 def scatter_to_pool(x: torch.Tensor, lay: PagedLayout, table: np.ndarray, n_blocks: int,
                     fill_bits: int | None = None) -> torch.Tensor:
     """Lays packed rows x [L, H, N, D] into a pool [L, n_blocks, B, H, D].
-    Slots no token uses hold ``fill_bits`` (bf16 bit pattern) or zeros."""
+    Slots no token uses hold the canary ``fill_bits`` (see fill_canary) or zeros."""
     L, H, N, D = x.shape
     B = lay.block_size
     pool = torch.zeros((L, n_blocks * B, H, D), dtype=x.dtype, device=x.device)
     if fill_bits is not None:
-        assert x.dtype == torch.bfloat16
-        pool.view(torch.int16).fill_(np.int16(np.uint16(fill_bits).view(np.int16)))
+        fill_canary(pool, fill_bits)
     idx = torch.from_numpy(slot_index(lay, table)).to(x.device)
     for l in range(L):
         pool[l, idx] = x[l].permute(1, 0, 2)
@@ -287,8 +286,24 @@ def empty_target_pool(w: Workload, lay: PagedLayout, device="cpu") -> torch.Tens
     """Target pool [L_t, n_tgt_blocks, B, H, D] with every slot holding the canary."""
     pool = torch.empty((w.n_tgt_layers, lay.n_tgt_blocks, lay.block_size, w.n_kv_heads, w.head_dim),
                        dtype=torch_dtype(w), device=device)
-    pool.view(torch.int16).fill_(np.int16(np.uint16(CANARY_BITS).view(np.int16)))
+    fill_canary(pool)
     return pool
+
+
+def canary_view(pool: torch.Tensor, bits: int = CANARY_BITS):
+    """(integer view of pool, the canary as an element of that view): bf16
+    elements are 16-bit patterns, fp32 elements hold the pattern in both
+    halves (a NaN as well)."""
+    if pool.dtype == torch.bfloat16:
+        return pool.view(torch.int16), int(np.uint16(bits).view(np.int16))
+    if pool.dtype == torch.float32:
+        return pool.view(torch.int32), int(np.uint32(bits * 0x10001).view(np.int32))
+    raise ValueError(f"no canary for {pool.dtype}")
+
+
+def fill_canary(pool: torch.Tensor, bits: int = CANARY_BITS) -> None:
+    view, value = canary_view(pool, bits)
+    view.fill_(value)
 
 
 def ridge_inputs(n_groups: int, n_obs: int, in_features: int, out_features: int, seed: int, device):

@@ -15,7 +15,7 @@ import torch
 import oracle
 import synth
 from tests import parity
-from tests.parity import Case, check_case, log, sample_rows
+from tests.parity import Case, PagedCase, check_case, log, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -246,65 +246,6 @@ def test_bitwise_deterministic():
 
 
 # ---------------------------------------------------------------- paged
-class PagedCase:
-    def __init__(self, w: synth.Workload, lens=None):
-        self.w = w
-        self.lay = lay = synth.paged_layout(w, lens=lens)
-        c = synth.paged_content(w, lay, device="cuda")
-        dt = parity.oracle_dtype(w)
-        k_enc = oracle.encode_keys(parity.to_np_storage(c.pop("k_content")), lay.src_pos, w.theta, dt)
-        k_dev = parity.from_np_storage(k_enc, "cuda")
-        del k_enc
-        self.dev = dict(c)
-        self.dev["src_k_pool"] = synth.scatter_to_pool(k_dev, lay, lay.src_bt, lay.n_src_blocks, synth.CANARY_BITS)
-        self.dev["src_v_pool"] = synth.scatter_to_pool(c["src_v"], lay, lay.src_bt, lay.n_src_blocks, synth.CANARY_BITS)
-        del k_dev, self.dev["src_v"]
-        for name, arr in (("src_bt", lay.src_bt), ("tgt_bt", lay.tgt_bt), ("cu", lay.cu_seqlens)):
-            self.dev[name] = torch.from_numpy(arr).cuda()
-        self.host = {k: parity.to_np_storage(v) for k, v in self.dev.items()}
-
-    def run_gpu(self):
-        import cross_model_kv_helm_amd as hk
-        d, w, lay = self.dev, self.w, self.lay
-        tk = synth.empty_target_pool(w, lay, "cuda")
-        tv = synth.empty_target_pool(w, lay, "cuda")
-        s = hk.make_paged_shape(d["src_k_pool"], tk, d["W_k"], d["layer_sel"], d["src_bt"], d["tgt_bt"],
-                                lay.n_tokens, w.theta, w.theta)
-        assert hk.helm_paged_check(s, lay.src_bt, lay.tgt_bt, lay.cu_seqlens) == 0, hk.helm_last_error()
-        hk.helm_kv_transfer_paged(d["src_k_pool"], d["src_v_pool"], d["src_bt"], d["tgt_bt"], d["cu"],
-                                  d["src_pos"], d["tgt_pos"], d["layer_sel"], d["W_k"], d["b_k"], d["W_v"],
-                                  d["b_v"], tk, tv, s)
-        return tk, tv
-
-    def check(self, tk, tv, rows=None):
-        w, lay, h = self.w, self.lay, self.host
-        pb = oracle.Problem(w.n_src_layers, w.n_tgt_layers, w.n_kv_heads, w.head_dim, w.k,
-                            n_tokens=lay.n_tokens, theta_src=w.theta, theta_tgt=w.theta,
-                            dtype=parity.oracle_dtype(w))
-        pg = oracle.Paged(lay.block_size, len(lay.lens), lay.max_blocks, lay.max_blocks,
-                          lay.n_src_blocks, lay.n_tgt_blocks)
-        ref_k, ref_v, dst = oracle.transfer_paged_rows(
-            pb, pg, h["src_k_pool"], h["src_v_pool"], h["src_bt"], h["tgt_bt"], h["cu"], h["src_pos"],
-            h["tgt_pos"], h["layer_sel"], h["W_k"], h["b_k"], h["W_v"], h["b_v"], rows=rows)
-        D = w.head_dim
-        idx = torch.from_numpy(dst[:, None] + np.arange(D)[None, :]).cuda()
-        g_k = parity.storage_to_f64(parity.to_np_storage(tk.reshape(-1)[idx]))
-        g_v = parity.storage_to_f64(parity.to_np_storage(tv.reshape(-1)[idx]))
-        n_rows = np.arange(ref_k.shape[0]) if rows is None else rows
-        slab = n_rows // lay.n_tokens
-        parity.compare(g_k, ref_k, slab, w.dtype, f"{w.name} K")
-        parity.compare(g_v, ref_v, slab, w.dtype, f"{w.name} V")
-        # every slot no token owns still holds the canary
-        canary = np.int16(np.uint16(synth.CANARY_BITS).view(np.int16))
-        owned = torch.from_numpy(synth.slot_index(lay, lay.tgt_bt)).cuda()
-        for pool in (tk, tv):
-            flat = pool.view(w.n_tgt_layers, -1, w.n_kv_heads, D).view(torch.int16)
-            mask = torch.ones(flat.shape[1], dtype=torch.bool, device="cuda")
-            mask[owned] = False
-            assert bool((flat[:, mask] == canary).all()), "a slot outside every request was written"
-            assert not bool((flat[:, owned] == canary).any()), "an owned slot was not written"
-
-
 def test_paged_small_full():
     w = synth.Workload("paged_small", 5, 4, 2, 128, 0, 2, "bf16", 1e6, "same", 31, paged=True,
                        n_requests=5, max_offset=300)

@@ -77,3 +77,29 @@ def test_scatter_to_pool_places_rows():
         assert torch.equal(flat[:, slots[n]], x[:, :, n])
     unused = np.setdiff1d(np.arange(lay.n_src_blocks * 16), slots)
     assert (flat[:, unused].view(torch.int16) == np.int16(np.uint16(synth.CANARY_BITS).view(np.int16))).all()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_pool_canary_per_storage_dtype(dtype):
+    """Unused slots hold the canary in either storage type: a NaN that no
+    transfer output equals, compared on the element's whole bit pattern
+    (for fp32 the 16-bit pattern fills both halves)."""
+    w = synth.Workload("t", 2, 2, 2, 8, 0, 1, "bf16" if dtype == torch.bfloat16 else "f32", 1e6, "same", 9,
+                       paged=True, n_requests=2, block_size=5)
+    lay = synth.paged_layout(w, lens=[7, 0])
+    x = torch.randn(2, 2, lay.n_tokens, 8).to(dtype)
+    pool = synth.scatter_to_pool(x, lay, lay.src_bt, lay.n_src_blocks, fill_bits=synth.CANARY_BITS)
+    slots = synth.slot_index(lay, lay.src_bt)
+    flat = pool.view(2, -1, 2, 8)
+    for n in range(lay.n_tokens):
+        assert torch.equal(flat[:, slots[n]], x[:, :, n])
+    unused = np.setdiff1d(np.arange(lay.n_src_blocks * 5), slots)
+    bits, canary = synth.canary_view(flat)
+    assert (bits[:, unused] == canary).all()
+    assert torch.isnan(flat[:, unused]).all()
+    tgt = synth.empty_target_pool(w, lay)
+    assert tgt.dtype == dtype
+    tbits, tcanary = synth.canary_view(tgt)
+    assert (tbits == tcanary).all() and torch.isnan(tgt).all()
+    if dtype == torch.float32:
+        assert tcanary == 0x7FA57FA5
