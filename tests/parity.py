@@ -264,3 +264,46 @@ class PagedCase:
             mask[owned] = False
             assert bool((flat[:, mask] == canary).all()), "a slot outside every request was written"
             assert not bool((flat[:, owned] == canary).any()), "an owned slot was not written"
+
+
+class WideCase:
+    """Device tensors for the library, host copies for the oracle."""
+
+    def __init__(self, w: synth.Workload):
+        self.w = w
+        c = synth.contiguous_inputs(w, device="cuda")
+        c["W_k"], c["b_k"], c["W_v"], c["b_v"] = synth.wide_maps(w, "cuda")
+        self.T = c["k_content"].shape[2]
+        self.host = {k: to_np_storage(v) for k, v in c.items() if k != "k_content"}
+        self.host["src_k"] = oracle.encode_keys(to_np_storage(c.pop("k_content")), self.host["src_pos"],
+                                                w.theta, oracle.BF16)
+        c["src_k"] = from_np_storage(self.host["src_k"], "cuda")
+        self.dev = c
+
+    def run_gpu(self):
+        import cross_model_kv_helm_amd as hk
+        d, w = self.dev, self.w
+        shape = (w.n_tgt_layers, w.n_kv_heads, self.T, w.head_dim)
+        out = (torch.empty(shape, dtype=torch.bfloat16, device="cuda"),
+               torch.empty(shape, dtype=torch.bfloat16, device="cuda"))
+        s = hk.make_shape(d["src_k"], d["W_k"], d["layer_sel"], w.theta, w.theta)
+        hk.helm_kv_transfer_wide(d["src_k"], d["src_v"], d["src_pos"], d["tgt_pos"], d["layer_sel"], d["W_k"],
+                                 d["b_k"], d["W_v"], d["b_v"], out[0], out[1], s)
+        return out
+
+    def check(self, out_k, out_v, rows=None, label=""):
+        w, h, D = self.w, self.host, self.w.head_dim
+        pb = oracle.Problem(w.n_src_layers, w.n_tgt_layers, w.n_kv_heads, D, w.k, n_tokens=self.T,
+                            theta_src=w.theta, theta_tgt=w.theta, dtype=oracle.BF16, quantize_content=True)
+        ref_k, ref_v = oracle.transfer_wide_rows(pb, h["src_k"], h["src_v"], h["src_pos"], h["tgt_pos"],
+                                                 h["layer_sel"], h["W_k"], h["b_k"], h["W_v"], h["b_v"], rows=rows)
+        gk = storage_to_f64(to_np_storage(out_k)).reshape(-1, D)
+        gv = storage_to_f64(to_np_storage(out_v)).reshape(-1, D)
+        if rows is None:
+            rows = np.arange(gk.shape[0])
+        else:
+            gk, gv = gk[rows], gv[rows]
+        slab = rows // self.T
+        sk = compare(gk, ref_k.reshape(-1, D), slab, "bf16", f"{label}{w.name} K")
+        sv = compare(gv, ref_v.reshape(-1, D), slab, "bf16", f"{label}{w.name} V")
+        log(f"{label}{w.name}: {len(rows)} rows; K {sk}; V {sv}")

@@ -1,6 +1,6 @@
 """GPU parity over seeded random shapes: the contiguous and the paged
-transfer through the C ABI against the fp64 oracle, every output element
-compared (tolerances: tests/parity.py).
+transfer and the wide-input map through the C ABI against the fp64 oracle,
+every output element compared (tolerances: tests/parity.py).
 
 The fixed cases elsewhere pin chosen corners; these draw the shape itself —
 source and target layer counts, heads, head_dim 64 or 128, k (up to 5, past
@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import synth
-from tests.parity import Case, PagedCase, check_case, log
+from tests.parity import Case, PagedCase, WideCase, check_case, log
 
 pytestmark = pytest.mark.gpu
 
@@ -102,3 +102,32 @@ def test_random_shape_paged_full(i):
     tk, tv = pc.run_gpu()
     torch.cuda.synchronize()
     pc.check(tk, tv)
+
+
+N_WIDE = 8
+
+
+def _wide_workload(i: int) -> synth.Workload:
+    rng = np.random.default_rng(9000 + i)
+    L_s = int(rng.integers(1, 10))
+    L_t = int(rng.integers(1, 5))
+    H = int(rng.integers(1, 5))
+    k = int(rng.integers(1, min(4, L_s) + 1))
+    T = int(rng.integers(1, 600))
+    positions = str(rng.choice(["same", "shift4096", "gap1000"]))
+    theta = float(rng.choice([1e4, 1e6]))
+    return synth.Workload(f"wsweep{i}", L_s, L_t, H, 128, T, k, "bf16", theta, positions, 9000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_WIDE))
+def test_random_shape_wide_full(i):
+    """The wide-input map (helm_kv_transfer_wide) over seeded random shapes:
+    input widths IN = k*2*H*128 from 256 to 4,096 and token counts that end
+    anywhere inside a 256-token tile."""
+    w = _wide_workload(i)
+    log(f"wide sweep {i}: L_s={w.n_src_layers} L_t={w.n_tgt_layers} H={w.n_kv_heads} k={w.k} "
+        f"T={w.n_tokens} {w.positions} theta={w.theta:g}")
+    case = WideCase(w)
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    case.check(*out)
