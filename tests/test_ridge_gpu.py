@@ -206,3 +206,23 @@ def test_ridge_large_means():
         log(f"ridge large means group {gi}: bound without shifts tol_rel {plain['tol_rel']:.3g}")
     assert shifted >= G * IN * 0.95, f"only {shifted} of {G * IN} features shifted"
     check(X, Y, W, b, 0.01, "ridge G2 N20000 IN256 mean/std 30-100")
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_ridge_random_shapes(i):
+    """Seeded random fits: 1-3 groups, 1-2,499 observations (so the last
+    64-observation step ends anywhere, and N <= IN happens), IN any multiple
+    of 128 up to 1,024, lambda 0.01 or 1, feature means 0, 2 or 30 sigma (the
+    last ones shifted before the products); every group checked against the
+    definition and the oracle."""
+    rng = np.random.default_rng(9500 + i)
+    IN = 128 * int(rng.integers(1, 9))
+    G = int(rng.integers(1, 4))
+    N = int(rng.integers(1, 2500))
+    lam = float(rng.choice([0.01, 1.0]))
+    mean = float(rng.choice([0.0, 2.0, 30.0]))
+    label = f"ridge sweep {i}: G={G} N={N} IN={IN} lambda={lam} mean={mean}"
+    log(label)
+    X, Y = draw(G, N, IN, 9500 + i, mean=mean)
+    W, b = fit(X, Y, lam)
+    check(X, Y, W, b, lam, label)
