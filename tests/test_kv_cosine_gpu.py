@@ -154,3 +154,28 @@ def test_qwen3_14b_32b_t32k_sampled_slabs():
             worst = max(worst, abs(got_h[kv, l, h] - want))
     log(f"t32k sampled: max |gpu - oracle| {worst:.2e} over {2 * len(picks)} slabs")
     assert worst <= ATOL
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_shapes(i):
+    """Seeded random shapes: 1-9 layers, 1-8 heads, 1-2,999 tokens, head_dim
+    64 or 128, bf16 or fp32, pairs of any correlation (from unrelated to
+    nearly equal), every cosine against the oracle."""
+    import cross_model_kv_helm_amd as hk
+    rng = np.random.default_rng(9700 + i)
+    L_t, H = int(rng.integers(1, 10)), int(rng.integers(1, 9))
+    T, D = int(rng.integers(1, 3000)), int(rng.choice([64, 128]))
+    dt = BF16 if i % 2 == 0 else F32
+    rho = float(rng.choice([0.0, 0.5, 0.99, 0.999999]))
+    label = f"cosine sweep {i}: L_t={L_t} H={H} T={T} D={D} {'bf16' if dt == BF16 else 'fp32'} rho={rho}"
+    log(label)
+    g = torch.Generator(device="cuda").manual_seed(9700 + i)
+    tdt = torch.bfloat16 if dt == BF16 else torch.float32
+    a = [torch.randn((L_t, H, T, D), generator=g, device="cuda") for _ in range(2)]
+    b = [rho * x + (1 - rho * rho) ** 0.5 * torch.randn(x.shape, generator=g, device="cuda") for x in a]
+    a = [x.to(tdt) for x in a]
+    b = [x.to(tdt) for x in b]
+    got = hk.helm_kv_cosine(a[0], a[1], b[0], b[1], cos_shape(L_t, H, T, D, dt))
+    torch.cuda.synchronize()
+    want = np.stack([oracle.kv_cosine(storage(a[j]), storage(b[j]), dt) for j in range(2)])
+    compare(got, want, label)
